@@ -1,0 +1,306 @@
+"""Pins of the oracle's pool-16 path (kpool_compress page,
+``_kpool_softmax_rotate_write_cache_kernel`` and
+``_kpool_decode_update_batched_kernel``).
+
+The softmax-weighted mean is checked against a 40-digit decimal brute force
+and against closed forms; the whole epilogue against hand-derived golden
+cases and against a recomposition from library routines (torch casts, scipy
+Hadamard); the ring decode against the single-pool function it must reduce to.
+"""
+import json
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle
+from kv_cache_compression_pool_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pool16_closed_forms.json")
+H128 = scipy.linalg.hadamard(128).astype(np.float64)
+
+
+def f32_bits_to_bf16(x):
+    return synth.to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _exact_softmax_mean(keys_f32, s_f32):
+    """40-digit decimal value of sum e^{s_i} k_i / sum e^{s_i} per channel."""
+    getcontext().prec = 40
+    P = keys_f32.shape[0]
+    out = []
+    for d in range(128):
+        e = [Decimal(float(s_f32[i, d])).exp() for i in range(P)]
+        num = sum(e[i] * Decimal(float(keys_f32[i, d])) for i in range(P))
+        out.append(num / sum(e))
+    return out
+
+
+def _ulp32(v):
+    v = np.float32(abs(v))
+    return float(np.nextafter(v, np.float32(np.inf)) - v) if v > 0 else float(np.float32(1e-45))
+
+
+@pytest.mark.parametrize("P,spread", [(1, 1.0), (2, 1.0), (16, 1.0), (16, 30.0), (5, 8.0)])
+def test_softmax_mean_matches_decimal_bruteforce(P, spread):
+    g = np.random.default_rng(100 + P)
+    keys = f32_bits_to_bf16(g.standard_normal((P, 128)) * 2)
+    scores = f32_bits_to_bf16(g.standard_normal((P, 128)) * spread)
+    ape = synth.bf16_bits_to_f32(f32_bits_to_bf16(g.standard_normal((P, 128)) * 0.1))
+    x = oracle.softmax_mean(keys, scores, ape)
+    s32 = synth.bf16_bits_to_f32(scores) + ape      # fp32 sum, as on the page
+    ex = _exact_softmax_mean(synth.bf16_bits_to_f32(keys), s32)
+    for d in range(128):
+        err = abs(Decimal(float(x[d])) - ex[d])
+        assert err <= Decimal(0.5 * _ulp32(float(ex[d]))) * Decimal("1.000001") + Decimal(1e-40)
+
+
+def test_softmax_mean_special_cases():
+    g = np.random.default_rng(7)
+    zeros = np.zeros((16, 128), np.float32)
+    keys = f32_bits_to_bf16(g.standard_normal((16, 128)))
+    kf = synth.bf16_bits_to_f32(keys).astype(np.float64)
+    # equal gated scores -> plain mean of the keys
+    eq = f32_bits_to_bf16(np.full((16, 128), 0.75))
+    x = oracle.softmax_mean(keys, eq, zeros)
+    assert np.array_equal(x, kf.mean(axis=0).astype(np.float32))
+    # one slot dominates by a margin far beyond fp32 resolution -> that key
+    sc = np.full((16, 128), -100.0, np.float32)
+    sc[9] = 100.0
+    x = oracle.softmax_mean(keys, f32_bits_to_bf16(sc), zeros)
+    assert np.array_equal(x, kf[9].astype(np.float32))
+    # P = 1 -> the key itself
+    x = oracle.softmax_mean(keys[:1], eq[:1], zeros[:1])
+    assert np.array_equal(x, kf[0].astype(np.float32))
+    # shift invariance: adding the same constant to every gated score of a
+    # channel (exactly, via ape) leaves the result bit-identical
+    sc = f32_bits_to_bf16(np.round(g.standard_normal((16, 128)) * 4) / 4)
+    x0 = oracle.softmax_mean(keys, sc, zeros)
+    x1 = oracle.softmax_mean(keys, sc, np.full((16, 128), 3.0, np.float32))
+    assert np.array_equal(x0, x1)
+    # convexity: the mean lies between the smallest and largest key
+    sc = f32_bits_to_bf16(g.standard_normal((16, 128)) * 3)
+    x = oracle.softmax_mean(keys, sc, zeros)
+    assert np.all(x >= kf.min(axis=0).astype(np.float32)) and np.all(x <= kf.max(axis=0).astype(np.float32))
+
+
+def _golden_inputs(case):
+    P = 16
+    keys = np.zeros((P, 128), np.float32)
+    scores = np.zeros((P, 128), np.float32)
+    row37 = H128[37].astype(np.float32)
+    kspec, sspec = case["keys"], case["scores"]
+    if kspec == "all 1.0":
+        keys[:] = 1.0
+    elif kspec == "all -1.0":
+        keys[:] = -1.0
+    elif kspec.startswith("every slot: k_d = (-1)^popcount(37 & d)"):
+        keys[:] = row37
+    elif kspec.startswith("every slot: k_0 = 1.0"):
+        keys[:, 0] = 1.0
+    elif kspec.startswith("slot 5: k_d = 2*"):
+        keys[:] = -7.0
+        keys[5] = 2 * row37
+    elif kspec == "all 0.0":
+        pass
+    else:
+        raise AssertionError(kspec)
+    if sspec.startswith("slot 5: 120.0"):
+        scores[:] = -120.0
+        scores[5] = 120.0
+    else:
+        assert sspec == "all 0.0"
+    assert case["ape"] == "all 0.0"
+    return f32_bits_to_bf16(keys), f32_bits_to_bf16(scores), np.zeros((P, 128), np.float32)
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+@pytest.mark.parametrize("mode", ["round_off", "round_on"])
+def test_pool_compress_closed_form_golden(case, mode):
+    keys, scores, ape = _golden_inputs(case)
+    code, scale, _, _ = oracle.pool_compress(keys, scores, ape, round_scale=(mode == "round_on"))
+    spec = case[mode]
+    expect = np.zeros(128, np.uint8)
+    if "all" in spec:
+        expect[:] = spec["all"]
+    for k, v in spec.get("nonzero", {}).items():
+        expect[int(k)] = v
+    assert np.array_equal(code, expect)
+    if "scale" in spec:
+        assert scale == np.float32(spec["scale"])
+    else:
+        ref = spec["scale_approx"]
+        assert abs(scale - ref) <= 2 * _ulp32(ref)
+
+
+def _recompose(x32, round_scale):
+    """The epilogue re-expressed with library routines (torch casts, scipy H)."""
+    xb = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
+    h = (H128 @ xb.astype(np.float64) / np.sqrt(128.0)).astype(np.float32)
+    y = torch.from_numpy(h).to(torch.bfloat16).to(torch.float32).numpy()
+    a = np.maximum(np.abs(y).max(), np.float32(1e-4))
+    t = np.float32(a) * np.float32(1.0 / 448.0)
+    scale = np.float32(np.exp2(np.ceil(np.log2(np.float64(t))))) if round_scale else t
+    q = np.clip(y / scale, np.float32(-448), np.float32(448)).astype(np.float32)
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, np.float32(scale), y
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_pool_compress_epilogue_recomposed_from_libraries(round_scale):
+    d = synth.pool16_single(seed=3)
+    for p in range(16):
+        k = d["keys"][16 * p:16 * p + 16]
+        s = d["scores"][16 * p:16 * p + 16]
+        code, scale, x, y = oracle.pool_compress(k, s, d["ape"], round_scale)
+        rc, rs, ry = _recompose(x, round_scale)
+        assert np.array_equal(y, ry)
+        assert scale == rs
+        assert np.array_equal(code, rc)
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_pool_compress_scale_invariants(round_scale):
+    d = synth.pool16_ragged(seed=5, num_seqs=4, max_len=600)
+    rows = oracle.pool_plan(d["seq_lens"])
+    codes, scales, _ = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
+    mags = oracle.e4m3_decode(codes.ravel()).reshape(codes.shape)
+    amax = np.abs(mags).max(axis=1)
+    if round_scale:
+        m, e = np.frexp(scales.astype(np.float64))
+        assert np.all(m == 0.5)                              # powers of two
+        assert np.all(amax >= 224) and np.all(amax <= 448)   # largest |q| in (224, 448] before rounding
+    else:
+        assert np.all(amax == 448)                           # absmax element hits the max code
+    # dequantised vector approximates the bf16 rotated vector within e4m3 resolution
+    _, _, x = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
+    for p in range(0, len(rows), 7):
+        _, _, y = _recompose(x[p], round_scale)
+        deq = mags[p] * scales[p]
+        assert np.all(np.abs(deq - y) <= np.abs(y) / 16 + scales[p] * 2.0**-9 + 1e-30)
+
+
+def test_compress_prefill_pool_plan_and_null_rows():
+    lens = np.array([15, 16, 17, 0, 47, 1], np.int64)
+    rows = oracle.pool_plan(lens)
+    assert list(rows) == [15, 31, 48, 64]
+    d = synth.pool16_single(seed=1)
+    a = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], None, False)
+    b = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], np.arange(16, dtype=np.int32) * 16, False)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------------ ring decode
+def _ring_inputs(g, R=1, N=1, nb=None):
+    nb = nb or R
+    ring = synth.bf16_normal(g, (nb, 2, 16, 128))
+    key = synth.bf16_normal(g, (R, N, 128))
+    score = synth.bf16_normal(g, (R, N, 128))
+    return ring, key, score
+
+
+def test_ring_decode_token_by_token_equals_single_pool():
+    g = np.random.default_rng(21)
+    ape = synth.ape_pool16(g)
+    toks_k = synth.bf16_normal(g, (40, 128))
+    toks_s = synth.bf16_normal(g, (40, 128))
+    ring = synth.bf16_normal(g, (3, 2, 16, 128))
+    blk = 2
+    out_c = np.zeros((4, 128), np.uint8)
+    out_s = np.zeros(4, np.float32)
+    for pos in range(40):
+        loc = pos // 16 if pos % 16 == 15 else -1
+        oracle.ring_decode(ring, np.array([[blk * 16 + pos % 16]], np.int32),
+                           toks_k[pos][None, None], toks_s[pos][None, None], ape,
+                           np.array([[loc]], np.int32), np.array([[pos]], np.int32),
+                           num_out=4, round_scale=True, out_code=out_c, out_scale=out_s)
+    for p in range(2):
+        c, s, _, _ = oracle.pool_compress(toks_k[16 * p:16 * p + 16], toks_s[16 * p:16 * p + 16], ape, True)
+        assert np.array_equal(out_c[p], c) and out_s[p] == s
+    # the ring now holds tokens 32..39 in slots 0..7 and tokens 16+8..31 in 8..15
+    assert np.array_equal(ring[blk, 0, :8], toks_k[32:40])
+    assert np.array_equal(ring[blk, 0, 8:], toks_k[24:32])
+    assert np.array_equal(ring[blk, 1, :8], toks_s[32:40])
+
+
+def test_ring_decode_verify_batch_straddling_a_pool_boundary_is_ordered():
+    g = np.random.default_rng(22)
+    ape = synth.ape_pool16(g)
+    R, N = 3, 5
+    ring0 = synth.bf16_normal(g, (R, 2, 16, 128))
+    key = synth.bf16_normal(g, (R, N, 128))
+    score = synth.bf16_normal(g, (R, N, 128))
+    base = np.array([12, 27, 100])          # pools close at t=3, t=4 and never
+    pos = (base[:, None] + np.arange(N)).astype(np.int32)
+    ts = (np.arange(R)[:, None] * 16 + pos % 16).astype(np.int32)
+    loc = np.where(pos % 16 == 15, np.arange(R)[:, None], -1).astype(np.int32)
+    ring_a = ring0.copy()
+    ca, sa = oracle.ring_decode(ring_a, ts, key, score, ape, loc, pos, R, True)
+    # sequential one-token calls give the same result
+    ring_b = ring0.copy()
+    cb = np.zeros((R, 128), np.uint8)
+    sb = np.zeros(R, np.float32)
+    for t in range(N):
+        oracle.ring_decode(ring_b, ts[:, t:t + 1], key[:, t:t + 1], score[:, t:t + 1], ape,
+                           loc[:, t:t + 1], pos[:, t:t + 1], R, True, out_code=cb, out_scale=sb)
+    assert np.array_equal(ring_a, ring_b) and np.array_equal(ca, cb) and np.array_equal(sa, sb)
+    # request 0: pool closes at t=3 (pos 15): slots 12..14 come from this call
+    pk = ring0[0, 0].copy()
+    ps = ring0[0, 1].copy()
+    pk[12:16] = key[0, :4]
+    ps[12:16] = score[0, :4]
+    c, s, _, _ = oracle.pool_compress(pk, ps, ape, True)
+    assert np.array_equal(ca[0], c) and sa[0] == s
+    assert np.all(ca[2] == 0) and sa[2] == 0          # no completion for request 2
+
+
+def test_ring_decode_padded_entries_are_never_read():
+    g = np.random.default_rng(23)
+    ape = synth.ape_pool16(g)
+    ring0 = synth.bf16_normal(g, (1, 2, 16, 128))
+    key = synth.bf16_normal(g, (1, 3, 128))
+    score = synth.bf16_normal(g, (1, 3, 128))
+    key[0, 1] = synth.BF16_NAN
+    score[0, 1] = synth.BF16_NAN
+    pos = np.array([[14, -1, 15]], np.int32)
+    ts = np.array([[14, -1, 15]], np.int32)
+    loc = np.array([[-1, -1, 0]], np.int32)
+    ring = ring0.copy()
+    c, s = oracle.ring_decode(ring, ts, key, score, ape, loc, pos, 1, True)
+    assert np.isfinite(s[0]) and not np.any(c[0] == 0x7F) and not np.any(c[0] == 0xFF)
+    pk = ring0[0, 0].copy()
+    ps = ring0[0, 1].copy()
+    pk[14], ps[14] = key[0, 0], score[0, 0]
+    pk[15], ps[15] = key[0, 2], score[0, 2]
+    c2, s2, _, _ = oracle.pool_compress(pk, ps, ape, True)
+    assert np.array_equal(c[0], c2) and s[0] == s2
+    assert np.array_equal(ring[0, :, :14], ring0[0, :, :14])
+
+
+def test_ring_decode_negative_tail_slot_reads_block_zero():
+    # A completion whose tail slot is a negative sentinel reads block 0 (the
+    # page clamps the block id instead of forming a negative base) and stashes
+    # nothing.
+    g = np.random.default_rng(24)
+    ape = synth.ape_pool16(g)
+    ring0 = synth.bf16_normal(g, (2, 2, 16, 128))
+    key = synth.bf16_normal(g, (1, 1, 128))
+    score = synth.bf16_normal(g, (1, 1, 128))
+    ring = ring0.copy()
+    c, s = oracle.ring_decode(ring, np.array([[-1]], np.int32), key, score, ape,
+                              np.array([[0]], np.int32), np.array([[31]], np.int32), 1, False)
+    pk = ring0[0, 0].copy()
+    ps = ring0[0, 1].copy()
+    pk[15], ps[15] = key[0, 0], score[0, 0]
+    c2, s2, _, _ = oracle.pool_compress(pk, ps, ape, False)
+    assert np.array_equal(c[0], c2) and s[0] == s2
+    assert np.array_equal(ring, ring0)
