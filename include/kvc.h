@@ -1,0 +1,236 @@
+/*
+ * kvc.h -- C ABI of libkvc, softmax-gated token-pool KV compression on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources: the vLLM API page "kpool_compress" for the pool-16
+ * path and the SGLang page "c128_online.cuh" for the pool-128 online path):
+ *
+ *   pool-16   For every complete pool of 16 consecutive tokens and every
+ *             channel d, take the softmax over the pool of score[i,d]+ape[i,d]
+ *             and sum the keys with those weights.  Round the 128-vector to
+ *             bf16, rotate it with the 128-point Walsh-Hadamard transform
+ *             (Sylvester order, scaled by 1/sqrt(128)), round to bf16 again,
+ *             and quantise to OCP FP8 e4m3 with one scale per vector:
+ *             max(absmax, 1e-4) * fp32(1/448), optionally rounded up to a
+ *             power of two.
+ *   pool-128  A running fp32 (max, sum, kv) state per sequence folds tokens
+ *             into the open 128-token chunk; when a chunk closes, its
+ *             softmax-weighted mean (fp32) is emitted.
+ *
+ * Conventions shared by every entry point
+ *   - head_dim is 128 everywhere; pool_size must be 16 on the pool-16 path.
+ *     Other values return KVC_ERR_UNSUPPORTED.
+ *   - Pointers documented as "device" are HIP device (or managed) memory;
+ *     "host" pointers are ordinary CPU memory.  The caller owns every buffer;
+ *     the library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device entry points only enqueue work; they never synchronise.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     failed check returns a negative status and enqueues nothing;
+ *     kvc_last_error() then describes it (thread-local, valid until the next
+ *     call on the same thread).  A failed launch returns KVC_ERR_HIP.
+ *   - Empty work (zero pools, requests, tokens or plans) returns KVC_OK and
+ *     launches nothing.
+ *   - Indices that live in device memory (source rows, slots, plans) cannot
+ *     be checked on the host; the kernels check them and skip any item that
+ *     would read or write out of bounds, leaving its outputs untouched.
+ *   - bf16 arrays are passed as their raw uint16_t bit patterns.
+ *   - All row starts of bf16 / fp32 vectors must be 16-byte aligned (every
+ *     lane moves 128 bits); fp8 output rows 8-byte aligned.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    KVC_OK = 0,
+    KVC_ERR_NULL = -1,        /* a required pointer is NULL                    */
+    KVC_ERR_SHAPE = -2,       /* a size, stride or alignment is invalid         */
+    KVC_ERR_UNSUPPORTED = -3, /* head_dim / pool_size other than supported      */
+    KVC_ERR_PLAN = -4,        /* planner: bad lengths or capacity exceeded      */
+    KVC_ERR_HIP = -5          /* the HIP runtime reported an error              */
+};
+
+/* Plan entry of the pool-128 online prefill (c128_online.cuh page,
+ * OnlinePrefillPlan): one segment of consecutive extend tokens of one
+ * request lying inside one 128-chunk.  ragged_id / position are the ragged
+ * row and global position of the segment's LAST token; window_len (1..128)
+ * is the number of tokens, so the first token is at position-window_len+1.
+ * An entry whose ragged_id is 0xFFFFFFFF is padding and is skipped. */
+typedef struct kvc_online_plan {
+    uint32_t ragged_id;
+    uint32_t batch_id;
+    uint32_t position;
+    uint32_t window_len;
+} kvc_online_plan;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int kvc_version(void);
+
+/* Description of the last failure on this thread ("" if none). */
+const char* kvc_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Host planners (pure CPU; host memory in and out).
+ * ------------------------------------------------------------------------ */
+
+/* Pool plan for a ragged prefill batch (the packing of the pool-16 prefill
+ * workload): request b owns seq_lens[b] consecutive rows of the packed
+ * key/score matrices, starting after the rows of requests 0..b-1.  Its
+ * complete pools j = 0 .. seq_lens[b]/pool_size - 1 start at row
+ * start_b + j*pool_size; tokens after the last complete pool are not
+ * compressed.  Writes the first row of every pool, in request order, to
+ * pool_src_row[0 .. *n_pools-1].
+ *   seq_lens      host [batch], each >= 0
+ *   pool_src_row  host [cap] int32 (may be NULL when cap == 0)
+ *   n_pools       host, out: number of pools
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE (negative length, rows >= 2^31),
+ *         KVC_ERR_UNSUPPORTED (pool_size != 16), KVC_ERR_PLAN (cap too small;
+ *         *n_pools still receives the required count). */
+int kvc_plan_pool_prefill(const int64_t* seq_lens, int64_t batch, int pool_size,
+                          int32_t* pool_src_row, int64_t cap, int64_t* n_pools);
+
+/* Segment planner of the pool-128 online prefill (c128_online.cuh page,
+ * plan_online_prefill_host).  Request b extends its sequence from
+ * prefix = seq_lens[b] - extend_lens[b] to seq_lens[b]; its extend tokens are
+ * rows counter_b .. counter_b + extend_lens[b] - 1 of the ragged input, with
+ * counter_b the sum of the earlier extends.  Each extend range is cut at
+ * multiples of 128.  A segment that ends on chunk position 127 becomes a
+ * compress plan; the request's trailing segment that ends earlier becomes its
+ * single write plan.  Plans are emitted in request order.
+ *   compress_plan, write_plan  host [num_tokens] (capacity)
+ *   pad_to_capacity  nonzero: fill both lists with padding entries up to
+ *                    num_tokens and report num_tokens for both counts, so a
+ *                    captured launch always sees the same grid.
+ * Errors: KVC_ERR_NULL, KVC_ERR_PLAN (extend not in (0, seq_len], a list
+ *         over capacity, or sum of extends != num_tokens), KVC_ERR_SHAPE
+ *         (lengths >= 2^32). */
+int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, int64_t batch,
+                          int64_t num_tokens, kvc_online_plan* compress_plan,
+                          kvc_online_plan* write_plan, int pad_to_capacity,
+                          uint32_t* n_compress, uint32_t* n_write);
+
+/* ------------------------------------------------------------------------
+ * Device entry points.
+ * ------------------------------------------------------------------------ */
+
+/* Pool-16 prefill compression (kpool_compress page,
+ * _kpool_softmax_rotate_write_cache_kernel, packed-return mode).
+ *   keys, scores    device bf16 [num_rows, *] with row strides in elements
+ *                   (multiples of 8); channels 0..127 of each row are used.
+ *   ape             device fp32 [16, 128], per-slot position bias.
+ *   pool_src_row    device int32 [n_pools]: first row of pool p; NULL means
+ *                   pool p starts at row 16*p.  A pool whose rows fall
+ *                   outside [0, num_rows) is skipped.
+ *   out_fp8         device uint8 [n_pools, 128] e4m3 codes.
+ *   out_scale       device fp32 [n_pools].
+ *   round_scale     nonzero: scale rounded up to a power of two.
+ *   dbg_pooled      device fp32 [n_pools, 128] or NULL: receives the fp32
+ *                   weighted mean before any rounding (for parity checks).
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE (strides, alignment, sizes),
+ *         KVC_ERR_UNSUPPORTED (pool_size != 16), KVC_ERR_HIP. */
+int kvc_compress_prefill(const uint16_t* keys, int64_t key_row_stride,
+                         const uint16_t* scores, int64_t score_row_stride, int64_t num_rows,
+                         const float* ape, int pool_size,
+                         const int32_t* pool_src_row, int64_t n_pools,
+                         uint8_t* out_fp8, float* out_scale, int round_scale,
+                         float* dbg_pooled, void* stream);
+
+/* Pool-16 decode with a tail ring and ordered verify tokens (kpool_compress
+ * page, _kpool_decode_update_batched_kernel).  Request r processes its tokens
+ * t = 0..next_n-1 strictly in order; for entry e = r*next_n + t:
+ *   blk = max(tail_slot_mapping[e], 0) / 16          (entries with
+ *         blk >= num_ring_blocks are skipped entirely)
+ *   if slot_mapping[e] >= 0 and positions[e] >= 0 and positions[e] % 16 == 15:
+ *       the pool is ring slots 0..14 of block blk plus the current token in
+ *       slot 15; its (codes, scale) go to row slot_mapping[e] of out_fp8 /
+ *       out_scale (skipped if that row is >= num_out);
+ *   then, if positions[e] >= 0 and tail_slot_mapping[e] >= 0, the token's key
+ *       and score are stored in ring slot positions[e] % 16 of block blk.
+ * A completion therefore sees the stashes of the earlier tokens of the same
+ * request in the same call.  Requests must use distinct ring blocks.
+ *   tail_ring        device bf16 [num_ring_blocks, 2, 16, 128] (half 0 keys,
+ *                    half 1 gate scores), updated in place.
+ *   key, score       device bf16, token (r, t) at r*stride_b + t*stride_t
+ *                    (elements, multiples of 8).
+ *   ape              device fp32 [16, 128].
+ *   tail_slot_mapping, slot_mapping, positions  device int32 [num_requests,
+ *                    next_n], contiguous; -1 marks padding.
+ *   out_fp8, out_scale  device [num_out, 128] uint8 / [num_out] fp32.
+ * Errors: as kvc_compress_prefill. */
+int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
+                             const int32_t* tail_slot_mapping,
+                             const uint16_t* key, int64_t key_stride_b, int64_t key_stride_t,
+                             const uint16_t* score, int64_t score_stride_b, int64_t score_stride_t,
+                             const float* ape,
+                             const int32_t* slot_mapping, const int32_t* positions,
+                             int64_t num_requests, int next_n, int pool_size,
+                             uint8_t* out_fp8, float* out_scale, int64_t num_out,
+                             int round_scale, void* stream);
+
+/* Pool-128 online decode (c128_online.cuh page, flash_c128_online_decode).
+ * Request b appends one token at position seq_lens[b]-1; c = that position
+ * mod 128 picks bias row ape[c]; s = score + ape[c].
+ *   c == 0:   state := (s, 1, kv)
+ *   c != 0:   state := online merge of the state with (s, 1, kv)
+ *   c == 127: out[b] := merged kv (the state row is left as it was);
+ *   otherwise the merged state is written back to row indices[b].
+ * Rows with seq_lens[b] <= 0 or indices[b] outside [0, num_slots) are skipped.
+ *   state        device fp32 [num_slots, 384] = max[128] | sum[128] | kv[128]
+ *   kv_score_in  device fp32 [batch, 256] = kv[128] | score[128]
+ *   out          device fp32 [batch, 128]; only emitting rows are written
+ *   ape          device fp32 [128, 128]
+ *   indices, seq_lens  device int32 [batch]
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_HIP. */
+int kvc_c128_online_decode(float* state, int64_t num_slots, const float* kv_score_in,
+                           float* out, const float* ape, const int32_t* indices,
+                           const int32_t* seq_lens, int64_t batch, void* stream);
+
+/* Pool-128 online ragged prefill (c128_online.cuh page,
+ * flash_c128_online_prefill and run_prefill).  Two launches in stream order:
+ *   1. every compress plan: the segment's softmax state, merged with state
+ *      row load_indices[b] when the segment starts mid-chunk, is normalised
+ *      and written to out row ragged_id.  The state buffer is only read.
+ *   2. every write plan: the same, but the (max, sum, kv) state is written to
+ *      row indices[b].
+ * Because pass 1 finishes before pass 2 starts, every read sees the state as
+ * it was when the call was made.
+ *   state          device fp32 [num_slots, 384]
+ *   kv_score_in    device fp32 [num_tokens, 256]
+ *   out            device fp32 [num_tokens, 128]; only chunk-closing rows
+ *   ape            device fp32 [128, 128]
+ *   indices        device int32 [batch]; load_indices device int32 [batch]
+ *                  or NULL (= indices)
+ *   compress_plan  device [n_compress]; write_plan device [n_write]; both as
+ *                  produced by kvc_c128_plan_prefill for these lengths.
+ *                  Malformed entries (out-of-range rows, batches or slots, or
+ *                  window_len outside 1..position%128+1) are skipped.
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_HIP. */
+int kvc_c128_online_prefill(float* state, int64_t num_slots, const float* kv_score_in,
+                            float* out, int64_t num_tokens, const float* ape,
+                            const int32_t* indices, const int32_t* load_indices, int64_t batch,
+                            const kvc_online_plan* compress_plan, uint32_t n_compress,
+                            const kvc_online_plan* write_plan, uint32_t n_write, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.
+ * ------------------------------------------------------------------------ */
+
+/* Runs the device number-format conversions the kernels use, elementwise:
+ *   bf16_out[i] = bf16 round-to-nearest-even of in[i]          (may be NULL)
+ *   fp8_out[i]  = e4m3 code of clamp(in[i], -448, 448)         (may be NULL)
+ * in: device fp32 [n]; n must be a multiple of 2.  For verifying the
+ * hardware conversion against an independent encoder. */
+int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,13 @@
+"""Softmax-gated token-pool KV compression for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libkvc.so`` (HIP kernels behind the C ABI in
+``include/kvc.h``); ``kvc`` is its ctypes binding.  Importing the package does
+not load the library; the first call does and fails loudly if it is missing.
+"""
+from .kvc import (KvcError, PLAN_DTYPE, kvc_c128_online_decode, kvc_c128_online_prefill,
+                  kvc_c128_plan_prefill, kvc_compress_decode_ring, kvc_compress_prefill,
+                  kvc_diag_convert, kvc_plan_pool_prefill, plans_to_device)
+
+__all__ = ["KvcError", "PLAN_DTYPE", "kvc_c128_online_decode", "kvc_c128_online_prefill",
+           "kvc_c128_plan_prefill", "kvc_compress_decode_ring", "kvc_compress_prefill",
+           "kvc_diag_convert", "kvc_plan_pool_prefill", "plans_to_device"]

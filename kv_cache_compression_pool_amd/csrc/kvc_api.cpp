@@ -1,0 +1,257 @@
+// kvc_api.cpp -- the C ABI of libkvc: argument validation, host planners and
+// dispatch to the HIP launchers.  Nothing here allocates device memory or
+// synchronises; every device entry point only enqueues work on `stream`.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kvc.h"
+#include "kvc_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return KVC_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kHeadDim = 128;
+constexpr int kPool = 16;
+constexpr int64_t kMaxI32 = 0x7fffffffLL;
+
+}  // namespace
+
+extern "C" {
+
+int kvc_version(void) { return 100; }
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+// --------------------------------------------------------------- planners
+int kvc_plan_pool_prefill(const int64_t* seq_lens, int64_t batch, int pool_size,
+                          int32_t* pool_src_row, int64_t cap, int64_t* n_pools) {
+  if (!n_pools) return fail(KVC_ERR_NULL, "kvc_plan_pool_prefill: n_pools is NULL");
+  *n_pools = 0;
+  if (pool_size != kPool)
+    return fail(KVC_ERR_UNSUPPORTED, "kvc_plan_pool_prefill: pool_size %d (only 16)", pool_size);
+  if (batch < 0 || cap < 0) return fail(KVC_ERR_SHAPE, "kvc_plan_pool_prefill: negative size");
+  if (batch > 0 && !seq_lens) return fail(KVC_ERR_NULL, "kvc_plan_pool_prefill: seq_lens is NULL");
+  if (cap > 0 && !pool_src_row)
+    return fail(KVC_ERR_NULL, "kvc_plan_pool_prefill: pool_src_row is NULL");
+  int64_t rows = 0, need = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0)
+      return fail(KVC_ERR_SHAPE, "kvc_plan_pool_prefill: seq_lens[%lld] < 0", (long long)b);
+    need += seq_lens[b] / pool_size;
+    rows += seq_lens[b];
+    if (rows > kMaxI32) return fail(KVC_ERR_SHAPE, "kvc_plan_pool_prefill: rows exceed 2^31-1");
+  }
+  *n_pools = need;
+  if (need > cap)
+    return fail(KVC_ERR_PLAN, "kvc_plan_pool_prefill: %lld pools exceed capacity %lld",
+                (long long)need, (long long)cap);
+  int64_t n = 0, start = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t full = seq_lens[b] / pool_size;
+    for (int64_t j = 0; j < full; ++j) pool_src_row[n++] = (int32_t)(start + j * pool_size);
+    start += seq_lens[b];
+  }
+  return ok();
+}
+
+int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, int64_t batch,
+                          int64_t num_tokens, kvc_online_plan* compress_plan,
+                          kvc_online_plan* write_plan, int pad_to_capacity,
+                          uint32_t* n_compress, uint32_t* n_write) {
+  if (!n_compress || !n_write) return fail(KVC_ERR_NULL, "kvc_c128_plan_prefill: NULL count");
+  *n_compress = *n_write = 0;
+  if (batch < 0 || num_tokens < 0)
+    return fail(KVC_ERR_SHAPE, "kvc_c128_plan_prefill: negative size");
+  if (num_tokens > (int64_t)0xfffffffeLL)
+    return fail(KVC_ERR_SHAPE, "kvc_c128_plan_prefill: num_tokens exceeds 2^32-2");
+  if (batch > 0 && (!seq_lens || !extend_lens))
+    return fail(KVC_ERR_NULL, "kvc_c128_plan_prefill: NULL lengths");
+  if (num_tokens > 0 && (!compress_plan || !write_plan))
+    return fail(KVC_ERR_NULL, "kvc_c128_plan_prefill: NULL plan buffer");
+  uint64_t row = 0;
+  uint32_t nc = 0, nw = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t L = seq_lens[b], E = extend_lens[b];
+    if (!(E > 0 && E <= L))
+      return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: request %lld extend %lld not in (0, %lld]",
+                  (long long)b, (long long)E, (long long)L);
+    if (L > (int64_t)0xffffffffLL)
+      return fail(KVC_ERR_SHAPE, "kvc_c128_plan_prefill: seq_len exceeds 2^32-1");
+    const int64_t prefix = L - E;
+    int64_t pos = prefix;
+    while (pos < L) {
+      const int64_t chunk_end = (pos / 128 + 1) * 128;          // exclusive
+      const int64_t seg_end = chunk_end < L ? chunk_end : L;
+      kvc_online_plan p;
+      p.ragged_id = (uint32_t)(row + (uint64_t)(seg_end - 1 - prefix));
+      p.batch_id = (uint32_t)b;
+      p.position = (uint32_t)(seg_end - 1);
+      p.window_len = (uint32_t)(seg_end - pos);
+      if (seg_end == chunk_end) {
+        if ((int64_t)nc >= num_tokens)
+          return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: compress plans exceed capacity");
+        compress_plan[nc++] = p;
+      } else {
+        if ((int64_t)nw >= num_tokens)
+          return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: write plans exceed capacity");
+        write_plan[nw++] = p;
+      }
+      pos = seg_end;
+    }
+    row += (uint64_t)E;
+  }
+  if (row != (uint64_t)num_tokens)
+    return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: extends sum to %llu, num_tokens %lld",
+                (unsigned long long)row, (long long)num_tokens);
+  if (pad_to_capacity) {
+    const kvc_online_plan pad = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+    for (int64_t i = nc; i < num_tokens; ++i) compress_plan[i] = pad;
+    for (int64_t i = nw; i < num_tokens; ++i) write_plan[i] = pad;
+    nc = nw = (uint32_t)num_tokens;
+  }
+  *n_compress = nc;
+  *n_write = nw;
+  return ok();
+}
+
+// --------------------------------------------------------------- pool-16
+int kvc_compress_prefill(const uint16_t* keys, int64_t key_row_stride, const uint16_t* scores,
+                         int64_t score_row_stride, int64_t num_rows, const float* ape,
+                         int pool_size, const int32_t* pool_src_row, int64_t n_pools,
+                         uint8_t* out_fp8, float* out_scale, int round_scale, float* dbg_pooled,
+                         void* stream) {
+  if (pool_size != kPool)
+    return fail(KVC_ERR_UNSUPPORTED, "kvc_compress_prefill: pool_size %d (only 16)", pool_size);
+  if (n_pools < 0 || num_rows < 0)
+    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: negative size");
+  if (n_pools == 0) return ok();
+  if (!keys || !scores || !ape || !out_fp8 || !out_scale)
+    return fail(KVC_ERR_NULL, "kvc_compress_prefill: NULL pointer");
+  if (key_row_stride < kHeadDim || score_row_stride < kHeadDim || key_row_stride % 8 ||
+      score_row_stride % 8)
+    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: row strides must be >= 128 and a multiple of 8");
+  if (!aligned(keys, 16) || !aligned(scores, 16) || !aligned(ape, 16) || !aligned(out_fp8, 8) ||
+      !aligned(out_scale, 4) || (dbg_pooled && !aligned(dbg_pooled, 16)))
+    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: misaligned pointer");
+  if (n_pools > kMaxI32 || num_rows > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: sizes exceed 2^31-1");
+  if (!pool_src_row && n_pools * kPool > num_rows)
+    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: %lld pools need %lld rows, have %lld",
+                (long long)n_pools, (long long)(n_pools * kPool), (long long)num_rows);
+  return hip_status(kvc::launch_pool16_prefill(keys, key_row_stride, scores, score_row_stride,
+                                               num_rows, ape, pool_src_row, n_pools, out_fp8,
+                                               out_scale, round_scale != 0, dbg_pooled,
+                                               (hipStream_t)stream),
+                    "kvc_compress_prefill launch");
+}
+
+int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
+                             const int32_t* tail_slot_mapping, const uint16_t* key,
+                             int64_t key_stride_b, int64_t key_stride_t, const uint16_t* score,
+                             int64_t score_stride_b, int64_t score_stride_t, const float* ape,
+                             const int32_t* slot_mapping, const int32_t* positions,
+                             int64_t num_requests, int next_n, int pool_size, uint8_t* out_fp8,
+                             float* out_scale, int64_t num_out, int round_scale, void* stream) {
+  if (pool_size != kPool)
+    return fail(KVC_ERR_UNSUPPORTED, "kvc_compress_decode_ring: pool_size %d (only 16)", pool_size);
+  if (num_requests < 0 || next_n < 0 || num_ring_blocks < 0 || num_out < 0)
+    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: negative size");
+  if (num_requests == 0 || next_n == 0) return ok();
+  if (!tail_ring || !tail_slot_mapping || !key || !score || !ape || !slot_mapping || !positions ||
+      (num_out > 0 && (!out_fp8 || !out_scale)))
+    return fail(KVC_ERR_NULL, "kvc_compress_decode_ring: NULL pointer");
+  if (key_stride_b < 0 || key_stride_t < 0 || score_stride_b < 0 || score_stride_t < 0 ||
+      key_stride_b % 8 || key_stride_t % 8 || score_stride_b % 8 || score_stride_t % 8)
+    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: strides must be non-negative multiples of 8");
+  if (!aligned(tail_ring, 16) || !aligned(key, 16) || !aligned(score, 16) || !aligned(ape, 16) ||
+      (num_out > 0 && (!aligned(out_fp8, 8) || !aligned(out_scale, 4))))
+    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: misaligned pointer");
+  if (num_requests * (int64_t)next_n > kMaxI32 || num_out > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: sizes exceed 2^31-1");
+  return hip_status(kvc::launch_pool16_ring(tail_ring, num_ring_blocks, tail_slot_mapping, key,
+                                            key_stride_b, key_stride_t, score, score_stride_b,
+                                            score_stride_t, ape, slot_mapping, positions,
+                                            num_requests, next_n, out_fp8, out_scale, num_out,
+                                            round_scale != 0, (hipStream_t)stream),
+                    "kvc_compress_decode_ring launch");
+}
+
+// --------------------------------------------------------------- pool-128
+int kvc_c128_online_decode(float* state, int64_t num_slots, const float* kv_score_in, float* out,
+                           const float* ape, const int32_t* indices, const int32_t* seq_lens,
+                           int64_t batch, void* stream) {
+  if (batch < 0 || num_slots < 0) return fail(KVC_ERR_SHAPE, "kvc_c128_online_decode: negative size");
+  if (batch == 0) return ok();
+  if (!state || !kv_score_in || !out || !ape || !indices || !seq_lens)
+    return fail(KVC_ERR_NULL, "kvc_c128_online_decode: NULL pointer");
+  if (!aligned(state, 16) || !aligned(kv_score_in, 16) || !aligned(out, 16) || !aligned(ape, 16))
+    return fail(KVC_ERR_SHAPE, "kvc_c128_online_decode: misaligned pointer");
+  if (batch > kMaxI32 || num_slots > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "kvc_c128_online_decode: sizes exceed 2^31-1");
+  return hip_status(kvc::launch_c128_decode(state, num_slots, kv_score_in, out, ape, indices,
+                                            seq_lens, batch, (hipStream_t)stream),
+                    "kvc_c128_online_decode launch");
+}
+
+int kvc_c128_online_prefill(float* state, int64_t num_slots, const float* kv_score_in, float* out,
+                            int64_t num_tokens, const float* ape, const int32_t* indices,
+                            const int32_t* load_indices, int64_t batch,
+                            const kvc_online_plan* compress_plan, uint32_t n_compress,
+                            const kvc_online_plan* write_plan, uint32_t n_write, void* stream) {
+  if (batch < 0 || num_slots < 0 || num_tokens < 0)
+    return fail(KVC_ERR_SHAPE, "kvc_c128_online_prefill: negative size");
+  if (n_compress == 0 && n_write == 0) return ok();
+  if (!state || !kv_score_in || !ape || !indices || (n_compress && (!compress_plan || !out)) ||
+      (n_write && !write_plan))
+    return fail(KVC_ERR_NULL, "kvc_c128_online_prefill: NULL pointer");
+  if (!aligned(state, 16) || !aligned(kv_score_in, 16) || !aligned(ape, 16) ||
+      (out && !aligned(out, 16)) || (compress_plan && !aligned(compress_plan, 16)) ||
+      (write_plan && !aligned(write_plan, 16)))
+    return fail(KVC_ERR_SHAPE, "kvc_c128_online_prefill: misaligned pointer");
+  if (num_tokens > (int64_t)0xfffffffeLL || num_slots > kMaxI32 || batch > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "kvc_c128_online_prefill: sizes out of range");
+  return hip_status(kvc::launch_c128_prefill(state, num_slots, kv_score_in, out, num_tokens, ape,
+                                             indices, load_indices, batch, compress_plan,
+                                             n_compress, write_plan, n_write,
+                                             (hipStream_t)stream),
+                    "kvc_c128_online_prefill launch");
+}
+
+// --------------------------------------------------------------- diagnostics
+int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
+                     void* stream) {
+  if (n < 0 || n % 2) return fail(KVC_ERR_SHAPE, "kvc_diag_convert: n must be even and >= 0");
+  if (n == 0) return ok();
+  if (!in) return fail(KVC_ERR_NULL, "kvc_diag_convert: NULL input");
+  return hip_status(kvc::launch_diag_convert(in, bf16_out, fp8_out, n, (hipStream_t)stream),
+                    "kvc_diag_convert launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+// kvc_c128.hip -- pool-128 online compression kernels for gfx950.
+//
+// Method (SGLang page "c128_online.cuh": flash_c128_online_decode,
+// flash_c128_online_prefill, c128_prefill_forward): a per-sequence fp32 state
+// (max, sum, kv) holds the softmax statistics of the tokens folded into the
+// open 128-token chunk; a closing chunk emits its weighted mean.
+//
+// Work mapping on MI355X:
+//   decode   one request per half-wave (32 lanes x float4 = one 512 B state
+//            row); two requests per 64-thread workgroup so even a small batch
+//            spreads over many CUs.  Loads that do not depend on the slot
+//            index (input row, lengths) are issued before the state load.
+//   prefill  one 256-thread workgroup per plan.  Wave w covers chunk
+//            positions [32w, 32w+32); its two half-waves take even / odd
+//            positions, 4 channels per lane, so every token row is read with
+//            128-bit loads and each lane keeps a private two-pass softmax over
+//            16 tokens in registers.  Partial (max, sum, weighted sum) states
+//            are merged across half-waves with a lane shuffle and across waves
+//            through LDS, then merged with the stored state when the segment
+//            starts mid-chunk.  Sums stay unnormalised until the end, so an
+//            empty partial (max = -FLT_MAX, sums 0) merges as a no-op and never
+//            produces NaN.
+#include <cfloat>
+
+#include "kvc_device.hpp"
+#include "kvc_internal.hpp"
+
+namespace kvc {
+namespace {
+
+// ------------------------------------------------------------------ decode
+constexpr int kDecodeReqPerBlock = 2;
+
+__global__ __launch_bounds__(64) void c128_decode_kernel(
+    float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
+    float* __restrict__ out, const float* __restrict__ ape, const int32_t* __restrict__ indices,
+    const int32_t* __restrict__ seq_lens, int64_t batch) {
+  const int64_t b = (int64_t)blockIdx.x * kDecodeReqPerBlock + (threadIdx.x >> 5);
+  const int q = threadIdx.x & 31;                       // channels 4q..4q+3
+  if (b >= batch) return;
+  const int32_t idx = indices[b];
+  const int32_t L = seq_lens[b];
+  const float4* row = reinterpret_cast<const float4*>(in + b * 256);
+  const float4 kv = row[q];
+  const float4 sc = row[32 + q];
+  if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
+  const int c = (L - 1) & 127;
+  const float4 bias = reinterpret_cast<const float4*>(ape + c * 128)[q];
+  float4* st = reinterpret_cast<float4*>(state + (int64_t)idx * 384);
+
+  float s[4] = {sc.x + bias.x, sc.y + bias.y, sc.z + bias.z, sc.w + bias.w};
+  float k[4] = {kv.x, kv.y, kv.z, kv.w};
+  float M[4], S[4], K[4];
+  if (c != 0) {
+    const float4 m4 = st[q], s4 = st[32 + q], k4 = st[64 + q];
+    const float om[4] = {m4.x, m4.y, m4.z, m4.w};
+    const float os[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float ok[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mx = fmaxf(om[i], s[i]);
+      const float a = os[i] * exp2_hw((om[i] - mx) * kLog2e);
+      const float e = exp2_hw((s[i] - mx) * kLog2e);
+      const float sum = a + e;
+      M[i] = mx;
+      S[i] = sum;
+      K[i] = (ok[i] * a + k[i] * e) / sum;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { M[i] = s[i]; S[i] = 1.0f; K[i] = k[i]; }
+  }
+  if (c == 127) {
+    reinterpret_cast<float4*>(out + b * 128)[q] = make_float4(K[0], K[1], K[2], K[3]);
+  } else {
+    st[q] = make_float4(M[0], M[1], M[2], M[3]);
+    st[32 + q] = make_float4(S[0], S[1], S[2], S[3]);
+    st[64 + q] = make_float4(K[0], K[1], K[2], K[3]);
+  }
+}
+
+// ------------------------------------------------------------------ prefill
+constexpr int kPrefillBlock = 256;           // 4 waves
+constexpr int kTokPerLane = 16;              // 128 positions / (4 waves * 2 halves)
+
+// Merge partial (m2, d2, a2) into (M, D, A); d = sum of e^{s-m}, a = sum of
+// k e^{s-m} (unnormalised).
+__device__ __forceinline__ void merge_partial(float& M, float& D, float& A, float m2, float d2,
+                                              float a2) {
+  const float mx = fmaxf(M, m2);
+  const float f1 = exp2_hw((M - mx) * kLog2e);
+  const float f2 = exp2_hw((m2 - mx) * kLog2e);
+  D = D * f1 + d2 * f2;
+  A = A * f1 + a2 * f2;
+  M = mx;
+}
+
+template <bool kWrite>
+__global__ __launch_bounds__(kPrefillBlock) void c128_prefill_kernel(
+    float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
+    float* __restrict__ out, int64_t num_tokens, const float* __restrict__ ape,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ load_indices, int64_t batch,
+    const kvc_online_plan* __restrict__ plans, uint32_t n_plans) {
+  __shared__ float s_m[4][128], s_d[4][128], s_a[4][128];
+
+  const uint32_t pid = blockIdx.x;
+  if (pid >= n_plans) return;
+  const kvc_online_plan p = plans[pid];
+  if (p.ragged_id == 0xFFFFFFFFu) return;                       // padding entry
+  const uint32_t len = p.window_len;
+  const uint32_t pos127 = p.position & 127u;
+  if (len < 1u || len > pos127 + 1u || (int64_t)p.batch_id >= batch ||
+      (int64_t)p.ragged_id >= num_tokens || p.ragged_id + 1u < len)
+    return;                                                     // malformed: skip
+  const uint32_t off = pos127 + 1u - len;                       // first chunk position
+  const uint32_t end = pos127 + 1u;                             // one past the last
+  const int64_t seg0 = (int64_t)p.ragged_id - (int64_t)pos127;  // row of chunk position 0
+  int32_t load_idx = -1;
+  if (off != 0u) {
+    load_idx = load_indices[p.batch_id];
+    if (load_idx < 0 || (int64_t)load_idx >= num_slots) return;
+  }
+  int32_t store_idx = -1;
+  if constexpr (kWrite) {
+    store_idx = indices[p.batch_id];
+    if (store_idx < 0 || (int64_t)store_idx >= num_slots) return;
+  }
+
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;                 // even / odd chunk positions
+  const int q = lane & 31;                 // channels 4q..4q+3
+  const float4* in4 = reinterpret_cast<const float4*>(in);
+  const float4* ape4 = reinterpret_cast<const float4*>(ape);
+
+  float4 kv[kTokPerLane], u[kTokPerLane];
+  bool valid[kTokPerLane];
+#pragma unroll
+  for (int i = 0; i < kTokPerLane; ++i) {
+    const uint32_t j = 32u * w + 2u * i + h;
+    valid[i] = j >= off && j < end;
+    kv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    u[i] = make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
+    if (valid[i]) {
+      const int64_t r = seg0 + j;
+      kv[i] = in4[r * 64 + q];
+      const float4 sc = in4[r * 64 + 32 + q];
+      const float4 bi = ape4[j * 32 + q];
+      u[i] = make_float4(sc.x + bi.x, sc.y + bi.y, sc.z + bi.z, sc.w + bi.w);
+    }
+  }
+  float m[4] = {-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX};
+#pragma unroll
+  for (int i = 0; i < kTokPerLane; ++i) {
+    m[0] = fmaxf(m[0], u[i].x); m[1] = fmaxf(m[1], u[i].y);
+    m[2] = fmaxf(m[2], u[i].z); m[3] = fmaxf(m[3], u[i].w);
+  }
+  float d[4] = {0.f, 0.f, 0.f, 0.f}, a[4] = {0.f, 0.f, 0.f, 0.f};
+  const float ml[4] = {m[0] * kLog2e, m[1] * kLog2e, m[2] * kLog2e, m[3] * kLog2e};
+#pragma unroll
+  for (int i = 0; i < kTokPerLane; ++i) {
+    if (valid[i]) {
+      const float uu[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+      const float kk[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e = exp2_hw(__builtin_fmaf(uu[k], kLog2e, -ml[k]));
+        d[k] += e;
+        a[k] = __builtin_fmaf(kk[k], e, a[k]);
+      }
+    }
+  }
+  // half-wave merge (lane q with lane q + 32)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float m2 = __shfl_xor(m[k], 32);
+    const float d2 = __shfl_xor(d[k], 32);
+    const float a2 = __shfl_xor(a[k], 32);
+    merge_partial(m[k], d[k], a[k], m2, d2, a2);
+  }
+  if (h == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      s_m[w][4 * q + k] = m[k];
+      s_d[w][4 * q + k] = d[k];
+      s_a[w][4 * q + k] = a[k];
+    }
+  }
+  __syncthreads();
+  if (w != 0 || h != 0) return;
+
+  float M[4], D[4], A[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    M[k] = s_m[0][4 * q + k]; D[k] = s_d[0][4 * q + k]; A[k] = s_a[0][4 * q + k];
+  }
+#pragma unroll
+  for (int ww = 1; ww < 4; ++ww)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      merge_partial(M[k], D[k], A[k], s_m[ww][4 * q + k], s_d[ww][4 * q + k], s_a[ww][4 * q + k]);
+
+  float K[4];
+  if (off != 0u) {
+    // Merge with the stored state of the open chunk: (m1, s1, k1) with k1 a
+    // normalised mean, i.e. an unnormalised sum k1 * s1.
+    const float4* st = reinterpret_cast<const float4*>(state + (int64_t)load_idx * 384);
+    const float4 m4 = st[q], s4 = st[32 + q], k4 = st[64 + q];
+    const float m1[4] = {m4.x, m4.y, m4.z, m4.w};
+    const float s1[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float k1[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float mx = fmaxf(m1[k], M[k]);
+      const float f1 = s1[k] * exp2_hw((m1[k] - mx) * kLog2e);
+      const float f2 = exp2_hw((M[k] - mx) * kLog2e);
+      const float sum = f1 + D[k] * f2;
+      K[k] = (k1[k] * f1 + A[k] * f2) / sum;
+      D[k] = sum;
+      M[k] = mx;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) K[k] = A[k] / D[k];
+  }
+  if constexpr (kWrite) {
+    float4* st = reinterpret_cast<float4*>(state + (int64_t)store_idx * 384);
+    st[q] = make_float4(M[0], M[1], M[2], M[3]);
+    st[32 + q] = make_float4(D[0], D[1], D[2], D[3]);
+    st[64 + q] = make_float4(K[0], K[1], K[2], K[3]);
+  } else {
+    reinterpret_cast<float4*>(out + (int64_t)p.ragged_id * 128)[q] =
+        make_float4(K[0], K[1], K[2], K[3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_c128_decode(float* state, int64_t num_slots, const float* in, float* out,
+                              const float* ape, const int32_t* indices, const int32_t* seq_lens,
+                              int64_t batch, hipStream_t stream) {
+  const dim3 grid((unsigned)((batch + kDecodeReqPerBlock - 1) / kDecodeReqPerBlock));
+  hipLaunchKernelGGL(c128_decode_kernel, grid, dim3(64), 0, stream, state, num_slots, in, out,
+                     ape, indices, seq_lens, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in, float* out,
+                               int64_t num_tokens, const float* ape, const int32_t* indices,
+                               const int32_t* load_indices, int64_t batch,
+                               const kvc_online_plan* cplan, uint32_t n_c,
+                               const kvc_online_plan* wplan, uint32_t n_w, hipStream_t stream) {
+  if (!load_indices) load_indices = indices;
+  // Pass 1 (compress plans) only reads the state; pass 2 (write plans) writes
+  // it.  Stream order puts every pass-1 read before any pass-2 write.
+  if (n_c) {
+    hipLaunchKernelGGL((c128_prefill_kernel<false>), dim3(n_c), dim3(kPrefillBlock), 0, stream,
+                       state, num_slots, in, out, num_tokens, ape, indices, load_indices, batch,
+                       cplan, n_c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (n_w) {
+    hipLaunchKernelGGL((c128_prefill_kernel<true>), dim3(n_w), dim3(kPrefillBlock), 0, stream,
+                       state, num_slots, in, out, num_tokens, ape, indices, load_indices, batch,
+                       wplan, n_w);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvc

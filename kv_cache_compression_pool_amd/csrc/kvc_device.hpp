@@ -1,0 +1,131 @@
+// kvc_device.hpp -- gfx950 device building blocks shared by the kernels:
+// bf16 widening / rounding, base-2 exponentials, DPP lane exchanges inside a
+// 16-lane row, the in-row 128-point Walsh-Hadamard butterfly, and the e4m3
+// quantiser.  Everything here is wave64 code for CDNA4; no other target.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr float kLog2e = 1.4426950408889634f;
+// fp32 nearest to 1/sqrt(128); the rotation's normalisation factor.
+constexpr float kInvSqrt128 = 0.088388347648318440550f;
+constexpr float kFp8Max = 448.0f;
+// fp32(1/448): the scale multiplies the absmax by this constant.
+constexpr float kInvFp8Max = (float)(1.0 / 448.0);
+constexpr float kScaleFloor = 1e-4f;
+
+// ---- bf16 ---------------------------------------------------------------
+// A 32-bit word holds two bf16 values: channel 2j in the low half, 2j+1 in
+// the high half.  Widening is a shift / mask (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to bf16 (nearest-even, v_cvt_pk_bf16_f32 on gfx950) and widen back.
+__device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ---- exponentials ---------------------------------------------------------
+// e^x evaluated as 2^(x*log2 e) on the hardware exp2 unit (v_exp_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- DPP lane exchanges inside one 16-lane row ----------------------------
+// Lane l of a row receives the value of lane l ^ m.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xf, 0xf, true));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kQuadRev = 0x1B;        // quad_perm [3,2,1,0]  (l ^ 3)
+constexpr int kRowHalfMirror = 0x141; // l -> 7 - l within each 8 lanes (l ^ 7)
+constexpr int kRowRor8 = 0x128;       // rotate the 16-lane row by 8 (l ^ 8)
+
+template <int kMask>
+__device__ __forceinline__ float row_xor(float v) {
+  if constexpr (kMask == 1) return dpp<kQuadXor1>(v);
+  else if constexpr (kMask == 2) return dpp<kQuadXor2>(v);
+  else if constexpr (kMask == 4) return dpp<kQuadRev>(dpp<kRowHalfMirror>(v));
+  else return dpp<kRowRor8>(v);
+}
+
+// Max over the 16 lanes of a row (every lane receives the result).
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));   // quad max with the mirrored quad
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  return v;
+}
+
+// ---- Walsh-Hadamard over a row-distributed 128-vector ---------------------
+// Lane c (0..15 within its row) holds channels 8c..8c+7 in v[0..7].  Channel
+// index bits 0-2 live in the register index, bits 3-6 in the lane index.
+// Each stage maps the pair (a, b) at indices (i, i + h) to (a + b, a - b).
+// Result: unnormalised Sylvester-ordered transform H v.
+template <int kMask>
+__device__ __forceinline__ void wht_lane_stage(float (&v)[8], int c) {
+  const float sgn = (c & kMask) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float p = row_xor<kMask>(v[j]);
+    v[j] = __builtin_fmaf(v[j], sgn, p);   // lane bit clear: v + p; set: p - v
+  }
+}
+
+__device__ __forceinline__ void wht128_row(float (&v)[8], int c) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!(j & h)) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+  wht_lane_stage<1>(v, c);
+  wht_lane_stage<2>(v, c);
+  wht_lane_stage<4>(v, c);
+  wht_lane_stage<8>(v, c);
+}
+
+// ---- scale + e4m3 -----------------------------------------------------------
+// Smallest power of two >= t for a positive normal t (bit-exact).
+__device__ __forceinline__ float pow2_ceil(float t) {
+  uint32_t u = __float_as_uint(t);
+  if ((u & 0x007fffffu) == 0u) return t;
+  return __uint_as_float(((u >> 23) + 1u) << 23);
+}
+
+// Reciprocal of a power of two 2^k (exact as long as 2^-k is normal).
+__device__ __forceinline__ float pow2_recip(float p) {
+  uint32_t e = __float_as_uint(p) >> 23;
+  return __uint_as_float((254u - e) << 23);
+}
+
+// Pack four fp32 values (already clamped to +-448) into four e4m3 codes,
+// nearest-even, byte i = code of value i (v_cvt_pk_fp8_f32, OCP e4m3 on gfx950).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ float clamp_fp8(float q) {
+  return __builtin_amdgcn_fmed3f(q, -kFp8Max, kFp8Max);
+}
+
+// Per-vector scale from the row's absmax (the pages' formula, fp32).
+__device__ __forceinline__ float fp8_scale(float absmax, bool round_scale) {
+  float a = fmaxf(absmax, kScaleFloor);
+  float t = a * kInvFp8Max;
+  return round_scale ? pow2_ceil(t) : t;
+}
+
+}  // namespace kvc

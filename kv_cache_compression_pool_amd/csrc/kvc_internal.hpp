@@ -1,0 +1,40 @@
+// kvc_internal.hpp -- launcher interface between the C-ABI layer (argument
+// validation, planners) and the HIP kernel translation units.  Launchers
+// assume validated arguments and only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const uint16_t* scores,
+                                 int64_t score_stride, int64_t num_rows, const float* ape,
+                                 const int32_t* src_rows, int64_t n_pools, uint8_t* out_fp8,
+                                 float* out_scale, bool round_scale, float* dbg,
+                                 hipStream_t stream);
+
+hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot,
+                              const uint16_t* key, int64_t key_sb, int64_t key_st,
+                              const uint16_t* score, int64_t score_sb, int64_t score_st,
+                              const float* ape, const int32_t* slot_mapping,
+                              const int32_t* positions, int64_t num_requests, int next_n,
+                              uint8_t* out_fp8, float* out_scale, int64_t num_out,
+                              bool round_scale, hipStream_t stream);
+
+hipError_t launch_c128_decode(float* state, int64_t num_slots, const float* in, float* out,
+                              const float* ape, const int32_t* indices, const int32_t* seq_lens,
+                              int64_t batch, hipStream_t stream);
+
+hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in, float* out,
+                               int64_t num_tokens, const float* ape, const int32_t* indices,
+                               const int32_t* load_indices, int64_t batch,
+                               const kvc_online_plan* cplan, uint32_t n_c,
+                               const kvc_online_plan* wplan, uint32_t n_w, hipStream_t stream);
+
+hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
+                               hipStream_t stream);
+
+}  // namespace kvc

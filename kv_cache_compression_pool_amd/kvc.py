@@ -1,0 +1,282 @@
+"""Thin Python binding of libkvc (ctypes).  Argument marshalling only: every
+step of the compression runs in the HIP kernels behind the C ABI declared in
+``include/kvc.h``.  torch provides device memory and the current stream.
+
+The library must have been built (``python -m kv_cache_compression_pool_amd._build``);
+importing this module does not load it, the first call does, and a missing
+library raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+KVC_OK = 0
+KVC_ERR_NULL = -1
+KVC_ERR_SHAPE = -2
+KVC_ERR_UNSUPPORTED = -3
+KVC_ERR_PLAN = -4
+KVC_ERR_HIP = -5
+
+PLAN_DTYPE = np.dtype([("ragged_id", "<u4"), ("batch_id", "<u4"), ("position", "<u4"),
+                       ("window_len", "<u4")])
+PLAN_SENTINEL = 0xFFFFFFFF
+
+EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_plan_prefill",
+           "kvc_compress_prefill", "kvc_compress_decode_ring", "kvc_c128_online_decode",
+           "kvc_c128_online_prefill", "kvc_diag_convert")
+
+
+class KvcError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libkvc error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_u32 = ctypes.c_uint32
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m kv_cache_compression_pool_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kvc_version.restype = _i32
+        L.kvc_last_error.restype = ctypes.c_char_p
+        L.kvc_plan_pool_prefill.argtypes = [_p, _i64, _i32, _p, _i64, _p]
+        L.kvc_c128_plan_prefill.argtypes = [_p, _p, _i64, _i64, _p, _p, _i32, _p, _p]
+        L.kvc_compress_prefill.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i32, _p, _i64, _p, _p,
+                                           _i32, _p, _p]
+        L.kvc_compress_decode_ring.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p,
+                                               _p, _p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p]
+        L.kvc_c128_online_decode.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]
+        L.kvc_c128_online_prefill.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _p, _u32,
+                                              _p, _u32, _p]
+        L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
+        for name in EXPORTS[2:]:
+            getattr(L, name).restype = _i32
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != KVC_OK:
+        raise KvcError(rc, lib().kvc_last_error().decode())
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dptr(t, dtype, name, optional=False):
+    """Device pointer of a CUDA/HIP tensor of the given torch dtype."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _shape_ok(t, shape, name, contiguous=True):
+    """t has exactly ``shape`` (None = any extent) and is contiguous."""
+    _need(t.dim() == len(shape) and all(e is None or t.shape[i] == e
+                                        for i, e in enumerate(shape)),
+          f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if contiguous:
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+# ------------------------------------------------------------------ planners
+def kvc_plan_pool_prefill(seq_lens, pool_size: int = 16) -> np.ndarray:
+    """First row of every complete pool of a ragged batch (host int32 array)."""
+    sl = np.ascontiguousarray(seq_lens, np.int64)
+    n = ctypes.c_int64()
+    cap = int(np.sum(np.maximum(sl, 0) // pool_size)) if pool_size > 0 else 0
+    out = np.empty(max(cap, 1), np.int32)
+    _check(lib().kvc_plan_pool_prefill(_np_ptr(sl), sl.size, pool_size, _np_ptr(out), cap,
+                                       ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+def kvc_c128_plan_prefill(seq_lens, extend_lens, num_tokens: int, pad_to_capacity: bool = False):
+    """(compress_plan, write_plan) host structured arrays of PLAN_DTYPE."""
+    sl = np.ascontiguousarray(seq_lens, np.int64)
+    el = np.ascontiguousarray(extend_lens, np.int64)
+    if sl.size != el.size:
+        raise ValueError("seq_lens and extend_lens differ in length")
+    cap = max(int(num_tokens), 1)
+    cp = np.zeros(cap, PLAN_DTYPE)
+    wp = np.zeros(cap, PLAN_DTYPE)
+    nc, nw = ctypes.c_uint32(), ctypes.c_uint32()
+    _check(lib().kvc_c128_plan_prefill(_np_ptr(sl), _np_ptr(el), sl.size, int(num_tokens),
+                                       _np_ptr(cp), _np_ptr(wp), int(pad_to_capacity),
+                                       ctypes.byref(nc), ctypes.byref(nw)))
+    return cp[:nc.value].copy(), wp[:nw.value].copy()
+
+
+# ------------------------------------------------------------------ device entry points
+def kvc_compress_prefill(keys, scores, ape, pool_src_row, n_pools: int, out_fp8, out_scale,
+                         round_scale: bool, dbg_pooled=None, pool_size: int = 16, stream=None):
+    """keys/scores: device int16/uint16-viewed bf16 [rows, >=128] (or torch.bfloat16);
+    ape fp32 [16,128]; pool_src_row int32 [n_pools] or None; out_fp8 uint8
+    [n_pools,128]; out_scale fp32 [n_pools]."""
+    import torch
+    k = _bf16_view(keys, "keys")
+    s = _bf16_view(scores, "scores")
+    if k.shape[0] != s.shape[0]:
+        raise ValueError("keys and scores must have the same number of rows")
+    n_pools = int(n_pools)
+    _shape_ok(ape, (pool_size, 128), "ape")
+    _need(out_fp8.dim() == 2 and out_fp8.shape[0] >= n_pools and out_fp8.shape[1] == 128
+          and out_fp8.is_contiguous(), "out_fp8 must be a contiguous [>=n_pools, 128] tensor")
+    _need(out_scale.dim() == 1 and out_scale.shape[0] >= n_pools, "out_scale must hold n_pools")
+    if pool_src_row is not None:
+        _need(pool_src_row.dim() == 1 and pool_src_row.shape[0] >= n_pools
+              and pool_src_row.is_contiguous(), "pool_src_row must hold n_pools entries")
+    if dbg_pooled is not None:
+        _need(dbg_pooled.dim() == 2 and dbg_pooled.shape[0] >= n_pools
+              and dbg_pooled.shape[1] == 128 and dbg_pooled.is_contiguous(),
+              "dbg_pooled must be a contiguous [>=n_pools, 128] tensor")
+    _check(lib().kvc_compress_prefill(
+        k.data_ptr(), k.stride(0), s.data_ptr(), s.stride(0), k.shape[0],
+        _dptr(ape, torch.float32, "ape"), pool_size,
+        _dptr(pool_src_row, torch.int32, "pool_src_row", optional=True), int(n_pools),
+        _dptr(out_fp8, torch.uint8, "out_fp8"), _dptr(out_scale, torch.float32, "out_scale"),
+        int(round_scale), _dptr(dbg_pooled, torch.float32, "dbg_pooled", optional=True),
+        _stream(stream)))
+
+
+def kvc_compress_decode_ring(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,
+                             positions, out_fp8, out_scale, round_scale: bool,
+                             pool_size: int = 16, stream=None):
+    """tail_ring bf16 [nb,2,16,128] (updated); key/score bf16 [R,next_n,128];
+    maps int32 [R,next_n]; out_fp8 uint8 [num_out,128]; out_scale fp32 [num_out]."""
+    import torch
+    ring = _bf16_view(tail_ring, "tail_ring", min_last=None)
+    k = _bf16_view(key, "key", min_last=None)
+    s = _bf16_view(score, "score", min_last=None)
+    R, N = k.shape[0], k.shape[1]
+    for name, t in (("tail_slot_mapping", tail_slot_mapping), ("slot_mapping", slot_mapping),
+                    ("positions", positions)):
+        if tuple(t.shape) != (R, N) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{R}, {N}] tensor")
+    if not ring.is_contiguous() or tuple(ring.shape[1:]) != (2, pool_size, 128):
+        raise ValueError(f"tail_ring must be a contiguous [nb, 2, {pool_size}, 128] tensor")
+    _need(k.dim() == 3 and k.shape[2] == 128 and tuple(s.shape) == tuple(k.shape),
+          "key and score must be [R, next_n, 128]")
+    _shape_ok(ape, (pool_size, 128), "ape")
+    _need(out_fp8.dim() == 2 and out_fp8.shape[1] == 128 and out_fp8.is_contiguous(),
+          "out_fp8 must be a contiguous [num_out, 128] tensor")
+    _need(out_scale.dim() == 1 and out_scale.shape[0] >= out_fp8.shape[0],
+          "out_scale must hold num_out entries")
+    _check(lib().kvc_compress_decode_ring(
+        ring.data_ptr(), ring.shape[0], _dptr(tail_slot_mapping, torch.int32, "tail_slot_mapping"),
+        k.data_ptr(), k.stride(0), k.stride(1), s.data_ptr(), s.stride(0), s.stride(1),
+        _dptr(ape, torch.float32, "ape"), _dptr(slot_mapping, torch.int32, "slot_mapping"),
+        _dptr(positions, torch.int32, "positions"), R, N, pool_size,
+        _dptr(out_fp8, torch.uint8, "out_fp8"), _dptr(out_scale, torch.float32, "out_scale"),
+        out_fp8.shape[0], int(round_scale), _stream(stream)))
+
+
+def kvc_c128_online_decode(state, kv_score_in, out, ape, indices, seq_lens, stream=None):
+    import torch
+    B = kv_score_in.shape[0]
+    _shape_ok(state, (None, 384), "state")
+    _shape_ok(kv_score_in, (B, 256), "kv_score_in")
+    _shape_ok(out, (B, 128), "out")
+    _shape_ok(ape, (128, 128), "ape")
+    _shape_ok(indices, (B,), "indices")
+    _shape_ok(seq_lens, (B,), "seq_lens")
+    _check(lib().kvc_c128_online_decode(
+        _dptr(state, torch.float32, "state"), state.shape[0],
+        _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out, torch.float32, "out"),
+        _dptr(ape, torch.float32, "ape"), _dptr(indices, torch.int32, "indices"),
+        _dptr(seq_lens, torch.int32, "seq_lens"), kv_score_in.shape[0], _stream(stream)))
+
+
+def kvc_c128_online_prefill(state, kv_score_in, out, ape, indices, compress_plan, n_compress,
+                            write_plan, n_write, load_indices=None, stream=None):
+    """compress_plan / write_plan: device uint8 tensors of 16-byte entries (or
+    int32 [n,4]); n_compress / n_write: entries to process."""
+    import torch
+    N, B = kv_score_in.shape[0], indices.shape[0]
+    _shape_ok(state, (None, 384), "state")
+    _shape_ok(kv_score_in, (N, 256), "kv_score_in")
+    _shape_ok(out, (N, 128), "out")
+    _shape_ok(ape, (128, 128), "ape")
+    _shape_ok(indices, (B,), "indices")
+    if load_indices is not None:
+        _shape_ok(load_indices, (B,), "load_indices")
+    for name, plan, n in (("compress_plan", compress_plan, n_compress),
+                          ("write_plan", write_plan, n_write)):
+        if int(n) > 0:
+            _need(plan is not None and plan.is_cuda and plan.is_contiguous()
+                  and plan.numel() * plan.element_size() >= 16 * int(n),
+                  f"{name} must be a contiguous device tensor of at least {int(n)} entries")
+    cp = None if compress_plan is None else compress_plan.data_ptr()
+    wp = None if write_plan is None else write_plan.data_ptr()
+    _check(lib().kvc_c128_online_prefill(
+        _dptr(state, torch.float32, "state"), state.shape[0],
+        _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out, torch.float32, "out"),
+        kv_score_in.shape[0], _dptr(ape, torch.float32, "ape"),
+        _dptr(indices, torch.int32, "indices"),
+        _dptr(load_indices, torch.int32, "load_indices", optional=True), indices.shape[0],
+        cp, int(n_compress), wp, int(n_write), _stream(stream)))
+
+
+def kvc_diag_convert(x, bf16_out=None, fp8_out=None, stream=None):
+    import torch
+    _check(lib().kvc_diag_convert(
+        _dptr(x, torch.float32, "x"), _dptr(bf16_out, torch.int16, "bf16_out", optional=True),
+        _dptr(fp8_out, torch.uint8, "fp8_out", optional=True), x.numel(), _stream(stream)))
+
+
+def plans_to_device(plan: np.ndarray, device="cuda"):
+    """Host PLAN_DTYPE array -> device uint8 tensor [n, 16] (16-byte aligned)."""
+    import torch
+    raw = np.ascontiguousarray(plan, PLAN_DTYPE).view(np.uint8).reshape(-1, 16)
+    if raw.shape[0] == 0:
+        return torch.empty((1, 16), dtype=torch.uint8, device=device)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+def _bf16_view(t, name, min_last=128):
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    if t.dtype not in (torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 bit patterns (bfloat16/int16), got {t.dtype}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+    if min_last is not None and t.shape[-1] < min_last:
+        raise ValueError(f"{name} rows must hold at least {min_last} channels")
+    return t

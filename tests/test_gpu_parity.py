@@ -1,0 +1,366 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Tolerances (the specification's bar):
+  * fp32 vectors (pool-16 pre-rounding mean, pool-128 outputs and state kv /
+    sum): per vector max-abs error <= 2e-3 of the vector's max-abs value.
+  * pool-128 state max: bit-exact.
+  * e4m3 codes: at most 1 step apart (ordered code line, +0 == -0) on at most
+    0.1% of codes, identical elsewhere.
+  * scales: bit-exact with power-of-two rounding; without it, identical except
+    on at most 0.1% of vectors whose absmax moved by one bf16 ulp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kv_cache_compression_pool_amd as kvc
+from kv_cache_compression_pool_amd import synth
+from tests.helpers import c128_decode_case, c128_prefill_case, e4m3_ordinal, rel_err_rows
+
+pytestmark = pytest.mark.gpu
+
+VEC_TOL = 2e-3
+
+
+def dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    t = torch.from_numpy(a)
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def note(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def check_codes(got, ref, what):
+    d = np.abs(e4m3_ordinal(got) - e4m3_ordinal(ref))
+    n_off = int((d != 0).sum())
+    assert d.max(initial=0) <= 1, f"{what}: code off by {d.max()}"
+    assert n_off <= 0.001 * d.size, f"{what}: {n_off} of {d.size} codes differ"
+    return n_off
+
+
+def check_scales(got, ref, round_scale, what):
+    if round_scale:
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+            f"{what}: {(got != ref).sum()} power-of-two scales differ"
+    else:
+        bad = got != ref
+        assert bad.sum() <= max(1, 0.001 * got.size), f"{what}: {bad.sum()} scales differ"
+        if bad.any():
+            assert np.all(np.abs(got[bad] / ref[bad] - 1) <= 2.0**-7)
+
+
+# ------------------------------------------------------------------ pool-16 prefill
+def run_prefill_gpu(keys, scores, ape, rows, n_pools, round_scale, key_stride=None):
+    T = keys.shape[0]
+    if key_stride:
+        kbuf = np.full((T, key_stride), synth.BF16_NAN, np.uint16)
+        kbuf[:, :128] = keys
+        sbuf = np.full((T, key_stride), synth.BF16_NAN, np.uint16)
+        sbuf[:, :128] = scores
+        kt, st = dev(kbuf, torch.int16), dev(sbuf, torch.int16)
+    else:
+        kt, st = dev(keys, torch.int16), dev(scores, torch.int16)
+    rows_t = None if rows is None else dev(rows.astype(np.int32))
+    out = torch.full((max(n_pools, 1), 128), 0x7F, dtype=torch.uint8, device="cuda")
+    scale = torch.full((max(n_pools, 1),), float("nan"), device="cuda")
+    dbg = torch.full((max(n_pools, 1), 128), float("nan"), device="cuda")
+    kvc.kvc_compress_prefill(kt, st, dev(ape), rows_t, n_pools, out, scale, round_scale, dbg)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), scale.cpu().numpy(), dbg.cpu().numpy()
+
+
+def compare_prefill(d, rows, round_scale, what, key_stride=None):
+    n = rows.size if rows is not None else d["keys"].shape[0] // 16
+    note(f"{what}: {n} pools round_scale={round_scale}")
+    gc, gs, gx = run_prefill_gpu(d["keys"], d["scores"], d["ape"], rows, n, round_scale, key_stride)
+    rc, rs, rx = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
+    err = rel_err_rows(gx[:n], rx)
+    assert err.max() <= VEC_TOL, f"{what}: fp32 mean rel err {err.max():.3g}"
+    n_off = check_codes(gc[:n], rc, what)
+    check_scales(gs[:n], rs, round_scale, what)
+    note(f"{what}: max rel err {err.max():.3g}, codes off by one: {n_off}")
+
+
+def test_pool16_single_sequence_c1():
+    d = synth.pool16_single(seed=0)
+    compare_prefill(d, kvc.kvc_plan_pool_prefill(d["seq_lens"]), False, "pool16 1x256")
+
+
+@pytest.mark.parametrize("round_scale", [True, False])
+def test_pool16_ragged_prefill_full_size_c2(round_scale):
+    d = synth.pool16_ragged(seed=0)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    assert np.array_equal(rows, oracle.pool_plan(d["seq_lens"]))
+    compare_prefill(d, rows, round_scale, "pool16 ragged 64 seqs")
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_pool16_ragged_small_with_nan_tails(seed):
+    d = synth.pool16_ragged(seed=seed, num_seqs=7, max_len=200)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    covered = np.zeros(d["keys"].shape[0], bool)
+    for r in rows:
+        covered[r:r + 16] = True
+    d["keys"][~covered] = synth.BF16_NAN          # tail tokens must never be read
+    d["scores"][~covered] = synth.BF16_NAN
+    compare_prefill(d, rows, seed % 2 == 0, f"pool16 ragged small seed {seed}")
+
+
+def test_pool16_null_rows_and_wide_row_stride():
+    d = synth.pool16_single(seed=4, tokens=16 * 37)
+    compare_prefill(d, None, True, "pool16 contiguous pools, NULL src rows")
+    compare_prefill(d, np.arange(37, dtype=np.int32)[::-1] * 16, False,
+                    "pool16 reversed pools, row stride 192", key_stride=192)
+
+
+def test_pool16_extreme_values():
+    g = np.random.default_rng(5)
+    P = 9 * 16
+    keys = np.zeros((P, 128), np.float32)
+    scores = np.zeros((P, 128), np.float32)
+    keys[0:16] = 0.0                                   # zero vector -> floor scale
+    keys[16:32] = g.standard_normal((16, 128)) * 1e4   # large keys
+    keys[32:48] = g.standard_normal((16, 128)) * 1e-6  # tiny keys
+    keys[48:64] = 1.0                                  # constant keys
+    scores[64:80] = g.standard_normal((16, 128)) * 60  # peaked softmax
+    keys[64:80] = g.standard_normal((16, 128))
+    scores[80:96, :] = -3e4                            # huge negative scores
+    keys[80:96] = g.standard_normal((16, 128))
+    keys[96:] = g.standard_normal((48, 128))
+    scores[96:] = g.standard_normal((48, 128))
+    d = dict(keys=synth.to_bf16_bits(keys), scores=synth.to_bf16_bits(scores),
+             ape=synth.ape_pool16(g))
+    for rs in (True, False):
+        compare_prefill(d, None, rs, "pool16 extreme values")
+
+
+def test_pool16_empty_and_invalid_rows_untouched():
+    d = synth.pool16_single(seed=6, tokens=64)
+    kt, st = dev(d["keys"], torch.int16), dev(d["scores"], torch.int16)
+    out = torch.full((4, 128), 0x55, dtype=torch.uint8, device="cuda")
+    scale = torch.full((4,), 3.0, device="cuda")
+    kvc.kvc_compress_prefill(kt, st, dev(d["ape"]), None, 0, out, scale, True)
+    rows = dev(np.array([0, 50, -16, 48], np.int32))     # 50 and -16 fall outside 64 rows
+    kvc.kvc_compress_prefill(kt, st, dev(d["ape"]), rows, 4, out, scale, True)
+    torch.cuda.synchronize()
+    o, s = out.cpu().numpy(), scale.cpu().numpy()
+    assert np.all(o[1] == 0x55) and np.all(o[2] == 0x55) and s[1] == 3.0 and s[2] == 3.0
+    rc, rs, _ = oracle.compress_prefill(d["keys"], d["scores"], d["ape"],
+                                        np.array([0, 48], np.int32), True)
+    check_codes(o[[0, 3]], rc, "valid rows")
+    check_scales(s[[0, 3]], rs, True, "valid rows")
+
+
+# ------------------------------------------------------------------ number formats
+def test_device_fp8_encoder_matches_oracle_on_every_bf16_value():
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x) & (np.abs(x) <= 448)].copy()
+    if x.size % 2:
+        x = x[:-1]
+    xt = dev(x)
+    f8 = torch.empty(x.size, dtype=torch.uint8, device="cuda")
+    kvc.kvc_diag_convert(xt, None, f8)
+    torch.cuda.synchronize()
+    got = f8.cpu().numpy()
+    ref = oracle.e4m3_encode(x)
+    assert np.array_equal(e4m3_ordinal(got), e4m3_ordinal(ref))
+    nz = x != 0
+    assert np.array_equal(got[nz], ref[nz])
+
+
+def test_device_bf16_rounding_matches_oracle():
+    g = np.random.default_rng(8)
+    bits = g.integers(0, 2**32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    ties = ((np.arange(1 << 16, dtype=np.uint32) << 16) | 0x8000)
+    x = np.concatenate([bits, ties]).view(np.float32)
+    x = x[np.isfinite(x)].copy()
+    if x.size % 2:
+        x = x[:-1]
+    bf = torch.empty(x.size, dtype=torch.int16, device="cuda")
+    kvc.kvc_diag_convert(dev(x), bf, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf.cpu().numpy().view(np.uint16), oracle.bf16_rne(x))
+
+
+# ------------------------------------------------------------------ pool-16 ring decode
+def run_ring(d):
+    ring = d["ring"].copy()
+    n_out = d["num_out"]
+    rc = np.full((n_out, 128), 0x33, np.uint8)
+    rs = np.full(n_out, 5.0, np.float32)
+    oracle.ring_decode(ring, d["tail_slot_mapping"], d["key"], d["score"], d["ape"],
+                       d["slot_mapping"], d["positions"], n_out, d["round_scale"],
+                       out_code=rc, out_scale=rs)
+    gring = dev(d["ring"], torch.int16)
+    go = torch.full((n_out, 128), 0x33, dtype=torch.uint8, device="cuda")
+    gs = torch.full((n_out,), 5.0, device="cuda")
+    kvc.kvc_compress_decode_ring(gring, dev(d["tail_slot_mapping"]), dev(d["key"], torch.int16),
+                                 dev(d["score"], torch.int16), dev(d["ape"]),
+                                 dev(d["slot_mapping"]), dev(d["positions"]), go, gs,
+                                 d["round_scale"])
+    torch.cuda.synchronize()
+    return (gring.cpu().numpy().view(np.uint16), go.cpu().numpy(), gs.cpu().numpy(),
+            ring, rc, rs)
+
+
+def test_ring_decode_full_size_c3():
+    d = synth.pool16_ring(seed=0)
+    note("ring decode 256x4")
+    gring, gc, gs, ring, rc, rs = run_ring(d)
+    assert np.array_equal(gring, ring)                 # stashes are exact copies
+    done = np.unique(d["slot_mapping"][d["slot_mapping"] >= 0])
+    assert done.size > 30
+    check_codes(gc, rc, "ring codes")
+    check_scales(gs, rs, True, "ring scales")
+    untouched = np.setdiff1d(np.arange(d["num_out"]), done)
+    assert np.all(gc[untouched] == 0x33) and np.all(gs[untouched] == 5.0)
+
+
+@pytest.mark.parametrize("next_n", [1, 5, 16, 21])
+def test_ring_decode_ordered_verify_tokens(next_n):
+    d = synth.pool16_ring(seed=10 + next_n, num_requests=37, next_n=next_n, pad_frac=0.1)
+    d["round_scale"] = next_n % 2 == 1
+    note(f"ring decode 37x{next_n}")
+    gring, gc, gs, ring, rc, rs = run_ring(d)
+    assert np.array_equal(gring, ring)
+    check_codes(gc, rc, "ring codes")
+    check_scales(gs, rs, d["round_scale"], "ring scales")
+
+
+def test_ring_decode_sentinel_tail_slot_and_out_of_range_loc():
+    d = synth.pool16_ring(seed=3, num_requests=4, next_n=2, pad_frac=0.0)
+    # requests own ring blocks 1..4; block 0 is read only through the sentinel
+    d["ring"] = synth.bf16_normal(np.random.default_rng(33), (5, 2, 16, 128))
+    d["positions"][:] = [[14, 15], [30, 31], [46, 47], [62, 63]]
+    d["tail_slot_mapping"][:] = (np.arange(4)[:, None] + 1) * 16 + d["positions"] % 16
+    d["tail_slot_mapping"][1, 1] = -1        # completion reads block 0, no stash
+    d["slot_mapping"][:] = -1
+    d["slot_mapping"][:, 1] = [0, 1, 2, 99]  # 99 >= num_out: skipped
+    gring, gc, gs, ring, rc, rs = run_ring(d)
+    assert np.array_equal(gring, ring)
+    check_codes(gc, rc, "ring codes")
+    check_scales(gs, rs, True, "ring scales")
+    assert np.all(gc[3] == 0x33)
+
+
+# ------------------------------------------------------------------ pool-128 decode
+def test_c128_decode_full_size_c4():
+    d = c128_decode_case(seed=0)
+    note("c128 decode 1024")
+    st = d["state"].copy()
+    ref_out = np.full((1024, 128), np.nan, np.float32)
+    oracle.c128_decode(st, d["kv_score_in"], d["ape"], d["indices"], d["seq_lens"], out=ref_out)
+    gst = dev(d["state"])
+    gout = torch.full((1024, 128), float("nan"), device="cuda")
+    kvc.kvc_c128_online_decode(gst, dev(d["kv_score_in"]), gout, dev(d["ape"]),
+                               dev(d["indices"]), dev(d["seq_lens"]))
+    torch.cuda.synchronize()
+    gst, gout = gst.cpu().numpy(), gout.cpu().numpy()
+    emit = (d["seq_lens"] - 1) % 128 == 127
+    assert np.array_equal(np.isnan(gout), np.isnan(ref_out))
+    if emit.any():
+        assert rel_err_rows(gout[emit], ref_out[emit]).max() <= VEC_TOL
+    compare_state(gst, st, "c128 decode state")
+
+
+def compare_state(g, r, what):
+    assert np.array_equal(np.isnan(g), np.isnan(r)), f"{what}: NaN pattern differs"
+    rows = ~np.isnan(r[:, 0])
+    assert np.array_equal(g[rows, :128], r[rows, :128]), f"{what}: max not bit-exact"
+    e_sum = rel_err_rows(g[rows, 128:256], r[rows, 128:256]).max(initial=0)
+    e_kv = rel_err_rows(g[rows, 256:], r[rows, 256:]).max(initial=0)
+    assert e_sum <= VEC_TOL and e_kv <= VEC_TOL, f"{what}: sum {e_sum:.3g} kv {e_kv:.3g}"
+    note(f"{what}: sum err {e_sum:.3g}, kv err {e_kv:.3g}")
+
+
+def test_c128_decode_chunk_edges_and_invalid_rows():
+    g = np.random.default_rng(12)
+    B = 9
+    seq = np.array([1, 128, 129, 256, 2, 127, 0, 300, 5], np.int32)
+    idx = np.array([0, 1, 2, 3, 4, 5, 6, -1, 99], np.int32)   # 7, 8 invalid slots; 6 seq 0
+    state = g.standard_normal((8, 384)).astype(np.float32)
+    state[:, 128:256] = np.abs(state[:, 128:256]) + 1
+    x = g.standard_normal((B, 256)).astype(np.float32)
+    ape = (g.standard_normal((128, 128)) * 0.1).astype(np.float32)
+    st = state.copy()
+    ref = np.full((B, 128), 9.0, np.float32)
+    oracle.c128_decode(st, x, ape, idx, seq, out=ref)
+    gst = dev(state)
+    gout = torch.full((B, 128), 9.0, device="cuda")
+    kvc.kvc_c128_online_decode(gst, dev(x), gout, dev(ape), dev(idx), dev(seq))
+    torch.cuda.synchronize()
+    gout = gout.cpu().numpy()
+    assert np.array_equal(gout == 9.0, ref == 9.0)
+    em = ref[:, 0] != 9.0
+    assert rel_err_rows(gout[em], ref[em]).max() <= VEC_TOL
+    compare_state(gst.cpu().numpy(), st, "c128 decode edges")
+
+
+# ------------------------------------------------------------------ pool-128 prefill
+def run_c128_prefill_gpu(d, state, pad=False, load_indices=None):
+    n = int(d["extend_lens"].sum())
+    cp, wp = kvc.kvc_c128_plan_prefill(d["seq_lens"], d["extend_lens"], n, pad_to_capacity=pad)
+    gst = dev(state)
+    gout = torch.full((n, 128), float("nan"), device="cuda")
+    kvc.kvc_c128_online_prefill(gst, dev(d["kv_score_in"]), gout, dev(d["ape"]),
+                                dev(d["indices"]), kvc.plans_to_device(cp), cp.size,
+                                kvc.plans_to_device(wp), wp.size,
+                                load_indices=None if load_indices is None else dev(load_indices))
+    torch.cuda.synchronize()
+    return gst.cpu().numpy(), gout.cpu().numpy(), cp, wp
+
+
+def compare_c128_prefill(d, what, pad=False):
+    note(what)
+    st = d["state"].copy()
+    ref = np.full((int(d["extend_lens"].sum()), 128), np.nan, np.float32)
+    oracle.c128_prefill(st, d["kv_score_in"], d["ape"], d["indices"], d["cplan"], d["wplan"],
+                        out=ref)
+    gst, gout, cp, wp = run_c128_prefill_gpu(d, d["state"], pad=pad)
+    if not pad:
+        assert np.array_equal(cp, d["cplan"]) and np.array_equal(wp, d["wplan"])
+    assert np.array_equal(np.isnan(gout), np.isnan(ref))
+    rows = ~np.isnan(ref[:, 0])
+    e = rel_err_rows(gout[rows], ref[rows]).max(initial=0)
+    assert e <= VEC_TOL, f"{what}: out err {e:.3g}"
+    note(f"{what}: {rows.sum()} vectors, out err {e:.3g}")
+    compare_state(gst, st, what + " state")
+
+
+def test_c128_prefill_full_size_c5():
+    compare_c128_prefill(c128_prefill_case(seed=0), "c128 prefill 32 seqs")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_c128_prefill_small_and_padded_plans(seed):
+    d = c128_prefill_case(seed=seed, batch=5, max_prior=700, max_extend=900)
+    compare_c128_prefill(d, f"c128 prefill small seed {seed}")
+    compare_c128_prefill(d, f"c128 prefill small seed {seed} padded", pad=True)
+
+
+def test_c128_prefill_distinct_load_indices():
+    d = c128_prefill_case(seed=3, batch=6, max_prior=400, max_extend=300)
+    # the open-chunk state lives in other slots than the ones written back
+    load = np.setdiff1d(np.arange(d["num_slots"]), d["indices"])[:d["indices"].size]
+    load = np.random.default_rng(4).permutation(load).astype(np.int32)
+    state = d["state"].copy()
+    state[load] = d["state"][d["indices"]]
+    state[d["indices"]] = np.nan
+    st = state.copy()
+    ref = np.full((int(d["extend_lens"].sum()), 128), np.nan, np.float32)
+    oracle.c128_prefill(st, d["kv_score_in"], d["ape"], d["indices"], d["cplan"], d["wplan"],
+                        load_indices=load, out=ref)
+    gst, gout, _, _ = run_c128_prefill_gpu(d, state, load_indices=load)
+    assert np.array_equal(np.isnan(gout), np.isnan(ref))
+    rows = ~np.isnan(ref[:, 0])
+    assert rel_err_rows(gout[rows], ref[rows]).max(initial=0) <= VEC_TOL
+    compare_state(gst, st, "c128 prefill load_indices")
