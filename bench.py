@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the softmax-gated token-pool KV compression path on
+one MI355X.
+
+Headline workload (one "step" = one pass of the pool-16 path over the batch):
+  pool-16 ragged prefill, 64 sequences with lengths uniform in [1, 8192],
+  head_dim 128, bf16 keys / gate scores ~ N(0,1), ape ~ N(0,0.1) (bf16 values),
+  power-of-two scales; tokens after each sequence's last full pool are not
+  compressed.  Output: packed e4m3 [pools,128] + fp32 scales.
+
+The same JSON line also reports the pool-128 online decode (1024 requests),
+the pool-128 online ragged prefill (32 sequences) and the pool-16 ring decode
+(256 x 4 verify tokens), each against the HBM roofline, and the CPU oracle
+timed on the host.
+
+Inputs are rotated over several device replicas whose combined footprint
+exceeds the 256 MB Infinity Cache, so the timed reads come from HBM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E peak, GB/s
+MALL_BYTES = 256 << 20                # Infinity Cache capacity
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pool16_prefill_ragged64_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_compression_pool_amd", "csrc", f)
+                  for f in ("kvc_pool16.hip", "kvc_device.hpp")]
+METRIC = ("compressed vectors/s + achieved HBM GB/s (% of peak), "
+          "pool-16 prefill & c128 decode")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def timed(fn, steps, warmup, torch, stream):
+    """Run fn(i) warmup + steps times; time the last `steps` with events on
+    the launch stream and with the host clock."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn(warmup + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [a.elapsed_time(b) for a, b in evs]
+    return wall, sum(ev_ms) / len(ev_ms), min(ev_ms)
+
+
+def to_dev(torch, a):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+# ------------------------------------------------------------------ pool-16 prefill
+def bench_pool16_prefill(args, torch, kvc, synth, stream):
+    d = synth.pool16_ragged(seed=0)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    n = int(rows.size)
+    T = d["keys"].shape[0]
+    per_replica = 2 * T * 256
+    R = max(2, -(-(2 * MALL_BYTES) // per_replica)) if args.replicas is None else args.replicas
+    keys = [to_dev(torch, d["keys"]) for _ in range(R)]
+    scores = [to_dev(torch, d["scores"]) for _ in range(R)]
+    ape = to_dev(torch, d["ape"])
+    rows_t = to_dev(torch, rows)
+    outs = [torch.empty((n, 128), dtype=torch.uint8, device="cuda") for _ in range(R)]
+    scl = [torch.empty((n,), dtype=torch.float32, device="cuda") for _ in range(R)]
+
+    def step(i):
+        r = i % R
+        kvc.kvc_compress_prefill(keys[r], scores[r], ape, rows_t, n, outs[r], scl[r], True)
+
+    wall, ev_ms, ev_min = timed(step, args.steps, args.warmup, torch, stream)
+    bytes_per_vec = 16 * 256 * 2 + 128 + 4 + 4      # keys+scores rows, codes, scale, plan entry
+    alg = bytes_per_vec * n
+    return dict(n=n, tokens=T, replicas=R, wall=wall, ev_ms=ev_ms, ev_min=ev_min,
+                alg_bytes=alg, bytes_per_vec=bytes_per_vec, d=d, rows=rows)
+
+
+# ------------------------------------------------------------------ pool-128 decode
+def bench_c128_decode(args, torch, kvc, synth, stream):
+    import numpy as np
+    d = synth.c128_decode(seed=0)
+    B, S = d["indices"].size, d["num_slots"]
+    # Build each request's open-chunk state on the GPU from its prior tokens
+    # (one planned prefill of the prior tokens into a NaN-filled state).
+    keep, sl, el = synth.state_seed_lengths(d["prior_counts"], d["seq_lens"].astype(np.int64) - 1)
+    n_prior = int(el.sum())
+    cp, wp = kvc.kvc_c128_plan_prefill(sl, el, n_prior)
+    state0 = torch.full((S, 384), float("nan"), device="cuda")
+    prior_in = to_dev(torch, d["prior_in"][:n_prior])
+    ape = to_dev(torch, d["ape"])
+    kvc.kvc_c128_online_prefill(state0, prior_in, torch.empty((n_prior, 128), device="cuda"), ape,
+                                to_dev(torch, d["indices"][keep]), kvc.plans_to_device(cp), cp.size,
+                                kvc.plans_to_device(wp), wp.size)
+    c = (d["seq_lens"].astype(np.int64) - 1) % 128
+    # algorithmic bytes: lengths + index, input row, ape row (cache resident
+    # but counted), state read unless c == 0, state write or 512 B emit
+    alg = int(np.sum(8 + 1024 + 512 + np.where(c != 0, 1536, 0) + np.where(c == 127, 512, 1536)))
+    per_replica = S * 384 * 4 + B * 256 * 4
+    R = max(2, -(-(2 * MALL_BYTES) // per_replica)) if args.replicas is None else args.replicas
+    states = [state0.clone() for _ in range(R)]
+    ins = [to_dev(torch, d["kv_score_in"]) for _ in range(R)]
+    outs = [torch.empty((B, 128), device="cuda") for _ in range(R)]
+    idx = to_dev(torch, d["indices"])
+    sl_t = to_dev(torch, d["seq_lens"])
+
+    def step(i):
+        r = i % R
+        kvc.kvc_c128_online_decode(states[r], ins[r], outs[r], ape, idx, sl_t)
+
+    steps = max(args.steps, 50)
+    wall, ev_ms, ev_min = timed(step, steps, max(args.warmup, 5), torch, stream)
+    return dict(batch=B, emitted=int((c == 127).sum()), replicas=R, wall=wall, steps=steps,
+                ev_ms=ev_ms, ev_min=ev_min, alg_bytes=alg)
+
+
+# ------------------------------------------------------------------ pool-128 prefill
+def bench_c128_prefill(args, torch, kvc, synth, stream):
+    import numpy as np
+    d = synth.c128_prefill(seed=0)
+    S = d["num_slots"]
+    N = int(d["extend_lens"].sum())
+    ape = to_dev(torch, d["ape"])
+    prior = d["seq_lens"] - d["extend_lens"]
+    keep, sl, el = synth.state_seed_lengths(d["prior_counts"], prior)
+    n_prior = int(el.sum())
+    state0 = torch.full((S, 384), float("nan"), device="cuda")
+    if n_prior:
+        cp0, wp0 = kvc.kvc_c128_plan_prefill(sl, el, n_prior)
+        kvc.kvc_c128_online_prefill(state0, to_dev(torch, d["prior_in"][:n_prior]),
+                                    torch.empty((n_prior, 128), device="cuda"), ape,
+                                    to_dev(torch, d["indices"][keep]), kvc.plans_to_device(cp0),
+                                    cp0.size, kvc.plans_to_device(wp0), wp0.size)
+    cp, wp = kvc.kvc_c128_plan_prefill(d["seq_lens"], d["extend_lens"], N)
+    cp_t, wp_t = kvc.plans_to_device(cp), kvc.plans_to_device(wp)
+    loads = int(np.sum(d["prior_counts"] > 0))
+    alg = N * 1024 + cp.size * 512 + (cp.size + wp.size) * 16 + loads * 1536 + wp.size * 1536
+    per_replica = N * 1024
+    R = max(2, -(-(2 * MALL_BYTES) // per_replica)) if args.replicas is None else args.replicas
+    states = [state0.clone() for _ in range(R)]
+    ins = [to_dev(torch, d["kv_score_in"]) for _ in range(R)]
+    outs = [torch.empty((N, 128), device="cuda") for _ in range(R)]
+    idx = to_dev(torch, d["indices"])
+
+    def step(i):
+        r = i % R
+        kvc.kvc_c128_online_prefill(states[r], ins[r], outs[r], ape, idx, cp_t, cp.size, wp_t,
+                                    wp.size)
+
+    steps = max(args.steps // 2, 10)
+    wall, ev_ms, ev_min = timed(step, steps, max(args.warmup, 3), torch, stream)
+    return dict(tokens=N, vectors=int(cp.size), write_plans=int(wp.size), replicas=R, wall=wall,
+                steps=steps, ev_ms=ev_ms, ev_min=ev_min, alg_bytes=alg)
+
+
+# ------------------------------------------------------------------ pool-16 ring decode
+def bench_ring(args, torch, kvc, synth, stream):
+    import numpy as np
+    d = synth.pool16_ring(seed=0)
+    R_req, N = d["key"].shape[:2]
+    ring = to_dev(torch, d["ring"])
+    key, score = to_dev(torch, d["key"]), to_dev(torch, d["score"])
+    ape = to_dev(torch, d["ape"])
+    ts, sm, pos = (to_dev(torch, d[k]) for k in ("tail_slot_mapping", "slot_mapping", "positions"))
+    out = torch.empty((d["num_out"], 128), dtype=torch.uint8, device="cuda")
+    scl = torch.empty((d["num_out"],), device="cuda")
+    valid = d["positions"] >= 0
+    comps = int(((d["slot_mapping"] >= 0) & valid).sum())
+    alg = int(valid.sum()) * (512 + 512 + 12) + comps * (15 * 512 + 132)
+
+    def step(i):
+        kvc.kvc_compress_decode_ring(ring, ts, key, score, ape, sm, pos, out, scl, True)
+
+    steps = max(args.steps, 50)
+    wall, ev_ms, ev_min = timed(step, steps, max(args.warmup, 5), torch, stream)
+    return dict(requests=R_req, next_n=N, completions=comps, wall=wall, steps=steps, ev_ms=ev_ms,
+                ev_min=ev_min, alg_bytes=alg)
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline(res, passes=10):
+    """The oracle as it stands, on the host's cores, over the same batch."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import oracle
+    d, rows = res["d"], res["rows"]
+    n = rows.size
+    threads = max(1, min(16, os.cpu_count() or 1))
+    code = np.empty((n, 128), np.uint8)
+    scale = np.empty(n, np.float32)
+    x = np.empty((n, 128), np.float32)
+    bounds = np.linspace(0, n, threads + 1).astype(int)
+    oracle.lib()
+
+    def work(k):
+        oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, True,
+                                pool_range=(int(bounds[k]), int(bounds[k + 1])),
+                                out=(code, scale, x))
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        for _ in range(passes):
+            list(ex.map(work, range(threads)))
+    dt = time.perf_counter() - t0
+    return {"value": round(n * passes / dt, 1), "unit": "vectors/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full pool-16 ragged batch ({n} pools), {passes} passes split over "
+                      f"{threads} threads, {dt:.2f} s wall"}
+
+
+def gbs(alg_bytes, ms):
+    return alg_bytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--replicas", type=int, default=None)
+    ap.add_argument("--only", choices=["prefill", "all"], default="all",
+                    help="prefill: the headline kernel only (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the compression path has no cross-GPU step).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_compression_pool_amd as kvc
+    from kv_cache_compression_pool_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kvc.kvc.lib()
+    stream = torch.cuda.current_stream()
+
+    log("pool-16 ragged prefill")
+    p = bench_pool16_prefill(args, torch, kvc, synth, stream)
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calib_copy_mib} MiB done")
+    achieved = gbs(p["alg_bytes"], p["ev_ms"])
+    line = {
+        "metric": METRIC,
+        "value": round(p["n"] * args.steps / p["wall"], 1),
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p["wall"] / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "pool16_ragged_prefill", "num_seqs": 64, "len_range": [1, 8192],
+                   "tokens": p["tokens"], "pools": p["n"], "pool": 16, "head_dim": 128,
+                   "round_scale": True, "io": "bf16 in, e4m3 + fp32 scale out",
+                   "input_replicas": p["replicas"]},
+        "hbm_gbs": round(achieved, 1),
+        "hbm_frac": round(achieved / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "pool16_prefill_kernel",
+                     "bytes_per_launch": p["alg_bytes"],
+                     "bytes_per_vector": p["bytes_per_vec"],
+                     "launch_us": round(p["ev_ms"] * 1e3, 3),
+                     "launch_us_min": round(p["ev_min"] * 1e3, 3)},
+    }
+    if args.only == "all":
+        log("pool-128 online decode")
+        c4 = bench_c128_decode(args, torch, kvc, synth, stream)
+        g4 = gbs(c4["alg_bytes"], c4["ev_ms"])
+        line["c128_decode"] = {
+            "workload": "c128_online_decode_1024", "batch": c4["batch"],
+            "token_updates_per_s": round(c4["batch"] * c4["steps"] / c4["wall"], 1),
+            "emitted_vectors_per_call": c4["emitted"],
+            "launch_us": round(c4["ev_ms"] * 1e3, 3), "bytes_per_launch": c4["alg_bytes"],
+            "hbm_gbs": round(g4, 1), "hbm_frac": round(g4 / PEAK_HBM_GBS, 4),
+            "state_replicas": c4["replicas"]}
+        log("pool-128 online prefill")
+        c5 = bench_c128_prefill(args, torch, kvc, synth, stream)
+        g5 = gbs(c5["alg_bytes"], c5["ev_ms"])
+        line["c128_prefill"] = {
+            "workload": "c128_online_prefill_32seq", "tokens": c5["tokens"],
+            "vectors_per_s": round(c5["vectors"] * c5["steps"] / c5["wall"], 1),
+            "tokens_per_s": round(c5["tokens"] * c5["steps"] / c5["wall"], 1),
+            "call_us": round(c5["ev_ms"] * 1e3, 3), "bytes_per_call": c5["alg_bytes"],
+            "hbm_gbs": round(g5, 1), "hbm_frac": round(g5 / PEAK_HBM_GBS, 4),
+            "input_replicas": c5["replicas"]}
+        log("pool-16 ring decode")
+        c3 = bench_ring(args, torch, kvc, synth, stream)
+        g3 = gbs(c3["alg_bytes"], c3["ev_ms"])
+        line["ring_decode"] = {
+            "workload": "pool16_ring_decode_256x4", "completions_per_call": c3["completions"],
+            "tokens_per_s": round(c3["requests"] * c3["next_n"] * c3["steps"] / c3["wall"], 1),
+            "launch_us": round(c3["ev_ms"] * 1e3, 3), "bytes_per_launch": c3["alg_bytes"],
+            "hbm_gbs": round(g3, 1), "hbm_frac": round(g3 / PEAK_HBM_GBS, 4)}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

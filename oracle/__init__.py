@@ -74,10 +74,11 @@ def _declare(L):
     L.orc_pool_compress.argtypes = [_p, _i64, _p, _i64, _p, _i32, _i32, _p, _p, _p, _p]
     L.orc_compress_prefill.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i32, _i32,
                                        _p, _p, _p]
+    L.orc_pool_epilogue_rows.argtypes = [_p, _i64, _i32, _p, _p]
     L.orc_pool_plan.argtypes = [_p, _i64, _i32, _p, _i64]
     L.orc_pool_plan.restype = _i64
     L.orc_ring_decode.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _p,
-                                  _i64, _i32, _i32, _i32, _p, _p, _i64]
+                                  _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _p]
     L.orc_c128_decode.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _i64]
     L.orc_c128_plan.argtypes = [_p, _p, _i64, _i64, _p, _p, _i32, _p, _p]
     L.orc_c128_plan.restype = _i32
@@ -156,6 +157,18 @@ def pool_compress(keys_bf16, scores_bf16, ape, round_scale: bool):
     return code, float(scale[0]), x, y
 
 
+def pool_epilogue(x_rows, round_scale: bool):
+    """Epilogue only (bf16, rotate, bf16, quantise) from given fp32 pooled
+    vectors [n,128] -> (codes [n,128] u8, scales [n] f32)."""
+    x = _c(x_rows, np.float32).reshape(-1, 128)
+    n = x.shape[0]
+    code = np.empty((n, 128), np.uint8)
+    scale = np.empty(n, np.float32)
+    if n:
+        lib().orc_pool_epilogue_rows(_ptr(x), n, int(round_scale), _ptr(code), _ptr(scale))
+    return code, scale
+
+
 def pool_plan(seq_lens, pool_size: int = 16) -> np.ndarray:
     """Row of the first token of every complete pool in a ragged packing."""
     sl = _c(seq_lens, np.int64)
@@ -194,11 +207,13 @@ def compress_prefill(keys_bf16, scores_bf16, ape, pool_src_row, round_scale: boo
 
 def ring_decode(ring, tail_slot_mapping, key, score, ape, slot_mapping, positions,
                 num_out: int, round_scale: bool, pool_size: int = 16,
-                out_code=None, out_scale=None):
+                out_code=None, out_scale=None, pools_out=None):
     """Tail-ring decode.  ``ring`` ([nb,2,P,128] u16) is updated in place.
     key/score: [R, next_n, 128] bf16 patterns; maps: [R, next_n] int32.
     Returns (out_code [num_out,128], out_scale [num_out]); rows not written
-    keep the content of the supplied arrays (zeros if None)."""
+    keep the content of the supplied arrays (zeros if None).  ``pools_out``
+    (optional pair of uint16 [num_out,P,128] arrays) receives the gathered
+    keys / scores of every completion."""
     assert ring.dtype == np.uint16 and ring.flags["C_CONTIGUOUS"]
     nb = ring.shape[0]
     R, nn = key.shape[0], key.shape[1]
@@ -214,7 +229,9 @@ def ring_decode(ring, tail_slot_mapping, key, score, ape, slot_mapping, position
         out_scale = np.zeros(num_out, np.float32)
     lib().orc_ring_decode(_ptr(ring), nb, _ptr(ts), _ptr(k), nn * 128, 128, _ptr(s), nn * 128,
                           128, _ptr(a), _ptr(sm), _ptr(pos), R, nn, pool_size,
-                          int(round_scale), _ptr(out_code), _ptr(out_scale), num_out)
+                          int(round_scale), _ptr(out_code), _ptr(out_scale), num_out,
+                          _ptr(pools_out[0]) if pools_out else None,
+                          _ptr(pools_out[1]) if pools_out else None)
     return out_code, out_scale
 
 

@@ -208,6 +208,20 @@ void orc_pool_compress(const uint16_t* keys, int64_t key_stride,
     if (y_out) memcpy(y_out, y, sizeof y);
 }
 
+/* The epilogue alone, from a given fp32 pooled vector x (rows of 128):
+ * bf16 round, rotate, bf16 round, quantise.  Used where two fp32 evaluations
+ * of the mean legitimately round to different bf16 values. */
+void orc_pool_epilogue_rows(const float* x, int64_t rows, int round_scale,
+                            uint8_t* code, float* scale) {
+    for (int64_t r = 0; r < rows; ++r) {
+        float xb[128], h[128], y[128];
+        for (int d = 0; d < 128; ++d) xb[d] = orc_round_bf16(x[r * 128 + d]);
+        orc_hadamard128(xb, h);
+        for (int d = 0; d < 128; ++d) y[d] = orc_round_bf16(h[d]);
+        quantise128(y, round_scale, code + r * 128, scale + r);
+    }
+}
+
 /* Ragged prefill: pool p reads rows pool_src_row[p] .. +P-1 of the packed
  * key / score matrices (row strides in elements).  A NULL pool_src_row means
  * pool p starts at row p*P.  Outputs: code[p*128 + d], scale[p], optional
@@ -257,13 +271,16 @@ int64_t orc_pool_plan(const int64_t* seq_lens, int64_t batch, int P,
  *       store (code, scale) at output row loc (rows >= num_out are skipped).
  *   then, if pos >= 0 && ts >= 0: ring[blk][0][pos%P] = key, [1][..] = score.
  * The completion read precedes the stash, and tokens are visited in order, so
- * a completion sees the stashes of earlier tokens of the same request. */
+ * a completion sees the stashes of earlier tokens of the same request.
+ * pool_keys_out / pool_scores_out (nullable, [num_out][P][128]) receive the
+ * gathered pool of every completion written to row loc. */
 void orc_ring_decode(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot_mapping,
                      const uint16_t* key, int64_t key_sb, int64_t key_st,
                      const uint16_t* score, int64_t score_sb, int64_t score_st,
                      const float* ape, const int32_t* slot_mapping, const int32_t* positions,
                      int64_t num_requests, int next_n, int P, int round_scale,
-                     uint8_t* out_code, float* out_scale, int64_t num_out) {
+                     uint8_t* out_code, float* out_scale, int64_t num_out,
+                     uint16_t* pool_keys_out, uint16_t* pool_scores_out) {
     uint16_t pk[128 * 128], ps[128 * 128];          /* gathered pool, P <= 128 */
     for (int64_t r = 0; r < num_requests; ++r) {
         for (int t = 0; t < next_n; ++t) {
@@ -282,9 +299,13 @@ void orc_ring_decode(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slo
                     memcpy(pk + i * 128, srck, 256);
                     memcpy(ps + i * 128, srcs, 256);
                 }
-                if (loc < num_out)
+                if (loc < num_out) {
                     orc_pool_compress(pk, 128, ps, 128, ape, P, round_scale,
                                       out_code + (int64_t)loc * 128, out_scale + loc, NULL, NULL);
+                    /* optional copy of the gathered pool, for diagnostics */
+                    if (pool_keys_out) memcpy(pool_keys_out + (int64_t)loc * P * 128, pk, P * 256);
+                    if (pool_scores_out) memcpy(pool_scores_out + (int64_t)loc * P * 128, ps, P * 256);
+                }
             }
             if (pos >= 0 && ts >= 0) {
                 int slot = pos % P;

@@ -57,6 +57,28 @@ def check_scales(got, ref, round_scale, what):
             assert np.all(np.abs(got[bad] / ref[bad] - 1) <= 2.0**-7)
 
 
+def reference_for(gx, rx, rc, rs, round_scale, what):
+    """Reference codes / scales for the GPU output.
+
+    Where the GPU's fp32 pooled vector rounds to the same bf16 vector as the
+    oracle's, the oracle's own codes are the reference.  Where some channel
+    rounds to the neighbouring bf16 value (the exact mean sits within fp32
+    rounding error of a bf16 rounding boundary, so both roundings are correct),
+    the reference is the oracle's epilogue applied to the GPU's pooled vector;
+    e4m3 resolves near-zero values far more finely than a one-bf16-ulp input
+    change, so those codes cannot be compared directly.  Such pools must stay
+    rare."""
+    n = rx.shape[0]
+    gb = oracle.bf16_rne(gx.ravel()).reshape(n, 128)
+    rb = oracle.bf16_rne(rx.ravel()).reshape(n, 128)
+    flip = (gb != rb).any(axis=1)
+    ref_c, ref_s = rc.copy(), rs.copy()
+    if flip.any():
+        ref_c[flip], ref_s[flip] = oracle.pool_epilogue(gx[flip], round_scale)
+    assert flip.sum() <= max(2, 0.02 * n), f"{what}: {flip.sum()} of {n} pools round differently"
+    return ref_c, ref_s, int(flip.sum())
+
+
 # ------------------------------------------------------------------ pool-16 prefill
 def run_prefill_gpu(keys, scores, ape, rows, n_pools, round_scale, key_stride=None):
     T = keys.shape[0]
@@ -84,9 +106,12 @@ def compare_prefill(d, rows, round_scale, what, key_stride=None):
     rc, rs, rx = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
     err = rel_err_rows(gx[:n], rx)
     assert err.max() <= VEC_TOL, f"{what}: fp32 mean rel err {err.max():.3g}"
-    n_off = check_codes(gc[:n], rc, what)
-    check_scales(gs[:n], rs, round_scale, what)
-    note(f"{what}: max rel err {err.max():.3g}, codes off by one: {n_off}")
+    raw = np.abs(e4m3_ordinal(gc[:n]) - e4m3_ordinal(rc))
+    ref_c, ref_s, flips = reference_for(gx[:n], rx, rc, rs, round_scale, what)
+    n_off = check_codes(gc[:n], ref_c, what)
+    check_scales(gs[:n], ref_s, round_scale, what)
+    note(f"{what}: max rel err {err.max():.3g}, bf16-boundary pools {flips}, codes off by one "
+         f"{n_off}; raw vs oracle: {(raw != 0).sum()} codes differ, max {raw.max()}")
 
 
 def test_pool16_single_sequence_c1():
@@ -193,13 +218,17 @@ def test_device_bf16_rounding_matches_oracle():
 
 # ------------------------------------------------------------------ pool-16 ring decode
 def run_ring(d):
+    """Run ring decode on both sides; return GPU ring / codes / scales and the
+    reference ring / codes / scales (bf16-boundary aware, see reference_for)."""
     ring = d["ring"].copy()
     n_out = d["num_out"]
     rc = np.full((n_out, 128), 0x33, np.uint8)
     rs = np.full(n_out, 5.0, np.float32)
+    pk = np.zeros((n_out, 16, 128), np.uint16)
+    ps = np.zeros((n_out, 16, 128), np.uint16)
     oracle.ring_decode(ring, d["tail_slot_mapping"], d["key"], d["score"], d["ape"],
                        d["slot_mapping"], d["positions"], n_out, d["round_scale"],
-                       out_code=rc, out_scale=rs)
+                       out_code=rc, out_scale=rs, pools_out=(pk, ps))
     gring = dev(d["ring"], torch.int16)
     go = torch.full((n_out, 128), 0x33, dtype=torch.uint8, device="cuda")
     gs = torch.full((n_out,), 5.0, device="cuda")
@@ -208,8 +237,24 @@ def run_ring(d):
                                  dev(d["slot_mapping"]), dev(d["positions"]), go, gs,
                                  d["round_scale"])
     torch.cuda.synchronize()
-    return (gring.cpu().numpy().view(np.uint16), go.cpu().numpy(), gs.cpu().numpy(),
-            ring, rc, rs)
+    gc, gsc = go.cpu().numpy(), gs.cpu().numpy()
+    # Pooled means of the completed pools, from the same device code (the
+    # prefill kernel with its diagnostic output) on the gathered pools.
+    done = np.nonzero(rs != 5.0)[0]
+    ref_c, ref_s = rc.copy(), rs.copy()
+    if done.size:
+        keys = pk[done].reshape(-1, 128)
+        scores = ps[done].reshape(-1, 128)
+        pc, pscale, px = run_prefill_gpu(keys, scores, d["ape"], None, done.size,
+                                         d["round_scale"])
+        assert np.array_equal(pc[:done.size], gc[done]), "ring and prefill kernels disagree"
+        assert np.array_equal(pscale[:done.size], gsc[done])
+        _, _, ox = oracle.compress_prefill(keys, scores, d["ape"], None, d["round_scale"])
+        assert rel_err_rows(px[:done.size], ox).max() <= VEC_TOL
+        c2, s2, flips = reference_for(px[:done.size], ox, rc[done], rs[done], d["round_scale"],
+                                      "ring decode")
+        ref_c[done], ref_s[done] = c2, s2
+    return gring.cpu().numpy().view(np.uint16), gc, gsc, ring, ref_c, ref_s
 
 
 def test_ring_decode_full_size_c3():

@@ -168,6 +168,18 @@ def test_pool_compress_epilogue_recomposed_from_libraries(round_scale):
 
 
 @pytest.mark.parametrize("round_scale", [False, True])
+def test_pool_epilogue_alone_matches_full_pool(round_scale):
+    d = synth.pool16_ragged(seed=6, num_seqs=3, max_len=500)
+    rows = oracle.pool_plan(d["seq_lens"])
+    codes, scales, x = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
+    c2, s2 = oracle.pool_epilogue(x, round_scale)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+    for p in range(0, rows.size, 5):
+        rc, rs, _ = _recompose(x[p], round_scale)
+        assert np.array_equal(c2[p], rc) and s2[p] == rs
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
 def test_pool_compress_scale_invariants(round_scale):
     d = synth.pool16_ragged(seed=5, num_seqs=4, max_len=600)
     rows = oracle.pool_plan(d["seq_lens"])
