@@ -1,7 +1,8 @@
 // kvc_device.hpp -- gfx950 device building blocks shared by the kernels:
 // bf16 widening / rounding, base-2 exponentials, DPP lane exchanges inside a
-// 16-lane row, the in-row 128-point Walsh-Hadamard butterfly, and the e4m3
-// quantiser.  Everything here is wave64 code for CDNA4; no other target.
+// 16-lane row and swizzles between two rows, the 128-point Walsh-Hadamard
+// butterfly over 32 lanes, and the e4m3 quantiser.  Everything here is wave64
+// code for CDNA4; no other target.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -53,6 +54,12 @@ __device__ __forceinline__ float row_xor(float v) {
   else return dpp<kRowRor8>(v);
 }
 
+// Lane l receives the value of lane l ^ 16: swaps the two 16-lane rows of
+// each 32-lane half (ds_swizzle bit-mask mode: and 0x1f, or 0, xor 0x10).
+__device__ __forceinline__ float swap_rows16(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+
 // Max over the 16 lanes of a row (every lane receives the result).
 __device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, dpp<kQuadXor1>(v));
@@ -62,32 +69,38 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
-// ---- Walsh-Hadamard over a row-distributed 128-vector ---------------------
-// Lane c (0..15 within its row) holds channels 8c..8c+7 in v[0..7].  Channel
-// index bits 0-2 live in the register index, bits 3-6 in the lane index.
-// Each stage maps the pair (a, b) at indices (i, i + h) to (a + b, a - b).
-// Result: unnormalised Sylvester-ordered transform H v.
+// ---- Walsh-Hadamard over a 32-lane-distributed 128-vector ----------------
+// A 128-vector is spread over two 16-lane rows: lane c of row h holds the
+// channels 8c + 4h + t, t = 0..3, in v[0..3].  Channel index bits 0-1 live in
+// the register index, bit 2 in the row index, bits 3-6 in the lane index.
+// Every stage maps the pair (a, b) at channel indices (i, i + 2^k) to
+// (a + b, a - b), giving the unnormalised Sylvester-ordered transform H v.
 template <int kMask>
-__device__ __forceinline__ void wht_lane_stage(float (&v)[8], int c) {
+__device__ __forceinline__ void wht_lane_stage(float (&v)[4], int c) {
   const float sgn = (c & kMask) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float p = row_xor<kMask>(v[j]);
-    v[j] = __builtin_fmaf(v[j], sgn, p);   // lane bit clear: v + p; set: p - v
+  for (int t = 0; t < 4; ++t) {
+    const float p = row_xor<kMask>(v[t]);
+    v[t] = __builtin_fmaf(v[t], sgn, p);   // lane bit clear: v + p; set: p - v
   }
 }
 
-__device__ __forceinline__ void wht128_row(float (&v)[8], int c) {
+__device__ __forceinline__ void wht128_split(float (&v)[4], int c, int h) {
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1) {
+  for (int k = 1; k < 4; k <<= 1) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (!(j & h)) {
-        float a = v[j], b = v[j + h];
-        v[j] = a + b;
-        v[j + h] = a - b;
+    for (int t = 0; t < 4; ++t) {
+      if (!(t & k)) {
+        const float a = v[t], b = v[t + k];
+        v[t] = a + b;
+        v[t + k] = a - b;
       }
     }
+  }
+  {
+    const float sgn = h ? -1.0f : 1.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(v[t], sgn, swap_rows16(v[t]));
   }
   wht_lane_stage<1>(v, c);
   wht_lane_stage<2>(v, c);

@@ -6,17 +6,22 @@
 // Walsh-Hadamard rotation / sqrt(128), bf16 round, per-vector fp8 e4m3 scale.
 //
 // Work mapping (MI355X-first, not the pages' one-program-per-pool layout):
-//   * A pool is owned by one 16-lane DPP row of a wave64, so a wave compresses
-//     four pools.  Lane c of the row owns channels 8c..8c+7: one 128-bit load
-//     per token row and per tensor, 16 lanes x 16 B = one 256 B bf16 row.
-//   * Each lane runs the two-pass softmax over all 16 slots of its 8 channels
-//     in fp32 registers (no cross-lane reduction on the hot loop; exp on the
-//     hardware exp2 unit).
-//   * The rotation keeps channel bits 0-2 in registers and bits 3-6 across
-//     the row's lanes (DPP quad_perm / row_half_mirror / row_ror exchanges);
-//     the absmax is a 4-step DPP row reduction; the 8 codes of a lane leave as
-//     one 8-byte store, so a row writes its 128-byte code vector coalesced.
-//   * ape ([16,128] fp32) is staged once per workgroup in LDS.
+//   * A pool is owned by 32 lanes: two 16-lane DPP rows, row h taking slots
+//     8h..8h+7.  Lane c of a row owns channels 8c..8c+7, so each slot row of
+//     keys or scores is one 128-bit load per lane (16 lanes x 16 B = the
+//     256 B bf16 row).  A wave compresses two pools.
+//   * Each lane runs the two-pass softmax over its 8 slots x 8 channels in
+//     fp32 registers.  The rows exchange only their per-channel max (before
+//     the exponentials, so no rescaling is needed) and their partial sums,
+//     with one ds_swizzle each.
+//   * The epilogue is split between the rows (4 channels per lane): the
+//     rotation keeps channel bits 0-1 in registers, bit 2 across the two rows
+//     and bits 3-6 across the 16 lanes of a row (DPP), the absmax is a DPP row
+//     reduction plus one swizzle, and each lane stores 4 codes, so the 128-byte
+//     code vector leaves as one coalesced 32-lane store.
+//   * Slot rows are streamed with non-temporal loads; ape ([16,128] fp32) is
+//     staged once per workgroup in LDS after the row loads are in flight.
+//   * At most 128 VGPRs, so four waves per SIMD keep enough loads in flight.
 // The path is HBM-bound (about 8.3 KB read per 132 B written); there is no
 // dense contraction, so no MFMA.
 #include "kvc_device.hpp"
@@ -26,8 +31,18 @@ namespace kvc {
 namespace {
 
 constexpr int kPool = 16;
-constexpr int kRowsPerBlock = 16;                 // pools (16-lane rows) per block
-constexpr int kBlock = kRowsPerBlock * 16;        // 256 threads = 4 waves
+constexpr int kHalf = 8;                       // slots per 16-lane row
+constexpr int kPoolsPerBlock = 8;              // 32 lanes per pool
+constexpr int kBlock = kPoolsPerBlock * 32;    // 256 threads = 4 waves
+constexpr int kMinWavesPerEU = 4;              // caps VGPRs at 128
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 128-bit load that does not keep the line in the caches.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ void widen8(uint4 w, float (&f)[8]) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
@@ -43,31 +58,38 @@ __device__ __forceinline__ void stage_ape(float4* s_ape, const float* __restrict
   __syncthreads();
 }
 
-// Softmax-weighted mean of one pool for the 8 channels of lane c.
-// S[i], K[i]: slot i's gate scores / keys for channels 8c..8c+7 (bf16 x 8).
-__device__ __forceinline__ void pool_mean8(const uint4 (&S)[kPool], const uint4 (&K)[kPool],
-                                           const float4* __restrict__ s_ape, int c,
-                                           float (&x)[8]) {
-  float u[kPool][8];
-  float m[8];
+// Softmax-weighted mean of one pool, 32-lane layout.  S[i], K[i]: gate scores
+// and keys of slot 8h + i, channels 8c..8c+7 (bf16 x 8).  Both rows return
+// the same x[0..7] for channels 8c..8c+7.
+__device__ __forceinline__ void pool_mean(const uint4 (&S)[kHalf], const uint4 (&K)[kHalf],
+                                          const float4* __restrict__ s_ape, int c, int h,
+                                          float (&x)[8]) {
+  const float4* ap = s_ape + (kHalf * h) * 32 + 2 * c;
+  float u[kHalf][8], m[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) m[j] = -__builtin_huge_valf();
 #pragma unroll
-  for (int i = 0; i < kPool; ++i) {
+  for (int i = 0; i < kHalf; ++i) {
     float s[8];
     widen8(S[i], s);
-    const float4 a0 = s_ape[i * 32 + 2 * c];
-    const float4 a1 = s_ape[i * 32 + 2 * c + 1];
-    u[i][0] = s[0] + a0.x; u[i][1] = s[1] + a0.y; u[i][2] = s[2] + a0.z; u[i][3] = s[3] + a0.w;
-    u[i][4] = s[4] + a1.x; u[i][5] = s[5] + a1.y; u[i][6] = s[6] + a1.z; u[i][7] = s[7] + a1.w;
+    const float4 a0 = ap[i * 32], a1 = ap[i * 32 + 1];
+    const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], u[i][j]);
+    for (int j = 0; j < 8; ++j) {
+      u[i][j] = s[j] + a[j];
+      m[j] = fmaxf(m[j], u[i][j]);
+    }
   }
   float ml[8], den[8], acc[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) { ml[j] = m[j] * kLog2e; den[j] = 0.0f; acc[j] = 0.0f; }
+  for (int j = 0; j < 8; ++j) {
+    m[j] = fmaxf(m[j], swap_rows16(m[j]));        // max over all 16 slots
+    ml[j] = m[j] * kLog2e;
+    den[j] = 0.0f;
+    acc[j] = 0.0f;
+  }
 #pragma unroll
-  for (int i = 0; i < kPool; ++i) {
+  for (int i = 0; i < kHalf; ++i) {
     float k[8];
     widen8(K[i], k);
 #pragma unroll
@@ -78,76 +100,90 @@ __device__ __forceinline__ void pool_mean8(const uint4 (&S)[kPool], const uint4 
     }
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] = acc[j] * __builtin_amdgcn_rcpf(den[j]);
+  for (int j = 0; j < 8; ++j) {
+    const float d = den[j] + swap_rows16(den[j]);
+    const float a = acc[j] + swap_rows16(acc[j]);
+    x[j] = a * __builtin_amdgcn_rcpf(d);
+  }
 }
 
-// bf16 round -> rotate -> bf16 round -> scale -> e4m3 codes for the row.
-// Returns the 8 codes of lane c packed little-endian (channel 8c in byte 0).
-__device__ __forceinline__ uint2 pool_epilogue(const float (&x)[8], int c, bool round_scale,
-                                               float& scale_out) {
-  float v[8];
+// bf16 round -> rotate -> bf16 round -> scale -> e4m3 for the pool's two
+// rows.  Row h handles channels 8c + 4h + t; returns their 4 codes packed
+// little-endian and the pool's scale.
+__device__ __forceinline__ uint32_t pool_epilogue(const float (&x)[8], int c, int h,
+                                                  bool round_scale, float& scale_out) {
+  float v[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = round_bf16(x[j]);
-  wht128_row(v, c);
+  for (int t = 0; t < 4; ++t) v[t] = round_bf16(h ? x[4 + t] : x[t]);
+  wht128_split(v, c, h);
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    v[j] = round_bf16(v[j] * kInvSqrt128);
-    amax = fmaxf(amax, fabsf(v[j]));
+  for (int t = 0; t < 4; ++t) {
+    v[t] = round_bf16(v[t] * kInvSqrt128);
+    amax = fmaxf(amax, fabsf(v[t]));
   }
   amax = row_max16(amax);
+  amax = fmaxf(amax, swap_rows16(amax));
   const float scale = fp8_scale(amax, round_scale);
-  float q[8];
+  float q[4];
   if (round_scale) {
     const float inv = pow2_recip(scale);   // exact: scale is a power of two
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = clamp_fp8(v[j] * inv);
+    for (int t = 0; t < 4; ++t) q[t] = clamp_fp8(v[t] * inv);
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = clamp_fp8(v[j] / scale);   // IEEE division
+    for (int t = 0; t < 4; ++t) q[t] = clamp_fp8(v[t] / scale);   // IEEE division
   }
   scale_out = scale;
-  return make_uint2(pack_e4m3x4(q[0], q[1], q[2], q[3]), pack_e4m3x4(q[4], q[5], q[6], q[7]));
+  return pack_e4m3x4(q[0], q[1], q[2], q[3]);
 }
 
 template <bool kRoundScale, bool kDbg>
-__global__ __launch_bounds__(kBlock) void pool16_prefill_kernel(
+__global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
     const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
     int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
     const int32_t* __restrict__ src_rows, int64_t n_pools, uint8_t* __restrict__ out_fp8,
     float* __restrict__ out_scale, float* __restrict__ dbg) {
   __shared__ float4 s_ape[kPool * 32];
-  stage_ape(s_ape, ape);
-
   const int c = threadIdx.x & 15;
-  const int64_t pool = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
-  if (pool >= n_pools) return;
-  const int64_t r0 = src_rows ? (int64_t)src_rows[pool] : pool * kPool;
-  if (r0 < 0 || r0 + kPool > num_rows) return;     // whole row leaves together
+  const int h = (threadIdx.x >> 4) & 1;
+  const int64_t pool = (int64_t)blockIdx.x * kPoolsPerBlock + (threadIdx.x >> 5);
+  int64_t r0 = -1;
+  if (pool < n_pools) r0 = src_rows ? (int64_t)src_rows[pool] : pool * kPool;
+  // Both rows of a pool take the same decision, so DPP / swizzle partners
+  // are always active.
+  const bool ok = pool < n_pools && r0 >= 0 && r0 + kPool <= num_rows;
 
-  const uint4* kp = reinterpret_cast<const uint4*>(keys + r0 * key_stride) + c;
-  const uint4* sp = reinterpret_cast<const uint4*>(scores + r0 * score_stride) + c;
-  const int64_t ks = key_stride >> 3, ss = score_stride >> 3;
-  uint4 S[kPool], K[kPool];
+  uint4 S[kHalf], K[kHalf];
+  if (ok) {
+    const int64_t row = r0 + kHalf * h;
+    const uint4* sp = reinterpret_cast<const uint4*>(scores + row * score_stride) + c;
+    const uint4* kp = reinterpret_cast<const uint4*>(keys + row * key_stride) + c;
+    const int64_t ss = score_stride >> 3, ks = key_stride >> 3;
 #pragma unroll
-  for (int i = 0; i < kPool; ++i) S[i] = sp[i * ss];
+    for (int i = 0; i < kHalf; ++i) S[i] = load_stream(sp + i * ss);
 #pragma unroll
-  for (int i = 0; i < kPool; ++i) K[i] = kp[i * ks];
+    for (int i = 0; i < kHalf; ++i) K[i] = load_stream(kp + i * ks);
+  }
+  stage_ape(s_ape, ape);                         // overlaps the row loads
+  if (!ok) return;
 
   float x[8];
-  pool_mean8(S, K, s_ape, c, x);
+  pool_mean(S, K, s_ape, c, h, x);
   if constexpr (kDbg) {
-    float4* d = reinterpret_cast<float4*>(dbg + pool * 128 + 8 * c);
-    d[0] = make_float4(x[0], x[1], x[2], x[3]);
-    d[1] = make_float4(x[4], x[5], x[6], x[7]);
+    reinterpret_cast<float4*>(dbg + pool * 128 + 8 * c)[h] =
+        h ? make_float4(x[4], x[5], x[6], x[7]) : make_float4(x[0], x[1], x[2], x[3]);
   }
   float scale;
-  const uint2 codes = pool_epilogue(x, c, kRoundScale, scale);
-  reinterpret_cast<uint2*>(out_fp8 + pool * 128)[c] = codes;
-  if (c == 0) out_scale[pool] = scale;
+  const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
+  reinterpret_cast<uint32_t*>(out_fp8 + pool * 128)[2 * c + h] = codes;
+  if (c == 0 && h == 0) out_scale[pool] = scale;
 }
 
-// Tail-ring decode: one 16-lane row per request, tokens in order.
+// Tail-ring decode: 32 lanes per request (row h owns ring slots 8h..8h+7),
+// tokens strictly in order.  A token's key / score row is stashed by the row
+// that later reads that slot in a completion, so every ring read sees the
+// stashes of earlier tokens from the same lanes in program order.
 template <bool kRoundScale>
 __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
     uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
@@ -160,7 +196,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
   stage_ape(s_ape, ape);
 
   const int c = threadIdx.x & 15;
-  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
+  const int h = (threadIdx.x >> 4) & 1;
+  const int64_t r = (int64_t)blockIdx.x * kPoolsPerBlock + (threadIdx.x >> 5);
   if (r >= num_requests) return;
 
   for (int t = 0; t < next_n; ++t) {
@@ -180,27 +217,30 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
     const uint4 sv = reinterpret_cast<const uint4*>(score + r * score_sb + t * score_st)[c];
 
     if (complete) {
-      // Slots 0..14 come from the ring (including stashes made earlier in
-      // this call by the same lanes); slot 15 is the current token.
-      uint4 S[kPool], K[kPool];
+      // Slots 0..14 come from the ring; slot 15 (row 1, i = 7) is this token.
+      uint4 S[kHalf], K[kHalf];
 #pragma unroll
-      for (int i = 0; i < kPool - 1; ++i) {
-        S[i] = reinterpret_cast<const uint4*>(ring_s + i * 128)[c];
-        K[i] = reinterpret_cast<const uint4*>(ring_k + i * 128)[c];
+      for (int i = 0; i < kHalf; ++i) {
+        const int slot = kHalf * h + i;
+        if (slot == kPool - 1) {
+          S[i] = sv;
+          K[i] = kv;
+        } else {
+          S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
+          K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
+        }
       }
-      S[kPool - 1] = sv;
-      K[kPool - 1] = kv;
       float x[8];
-      pool_mean8(S, K, s_ape, c, x);
+      pool_mean(S, K, s_ape, c, h, x);
       float scale;
-      const uint2 codes = pool_epilogue(x, c, kRoundScale, scale);
+      const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
       if (loc < num_out) {
-        reinterpret_cast<uint2*>(out_fp8 + (int64_t)loc * 128)[c] = codes;
-        if (c == 0) out_scale[loc] = scale;
+        reinterpret_cast<uint32_t*>(out_fp8 + (int64_t)loc * 128)[2 * c + h] = codes;
+        if (c == 0 && h == 0) out_scale[loc] = scale;
       }
     }
-    if (stash) {
-      const int slot = pos & (kPool - 1);
+    const int slot = pos & (kPool - 1);
+    if (stash && (slot >> 3) == h) {
       reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = kv;
       reinterpret_cast<uint4*>(ring_s + slot * 128)[c] = sv;
     }
@@ -232,7 +272,7 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
                                  const int32_t* src_rows, int64_t n_pools, uint8_t* out_fp8,
                                  float* out_scale, bool round_scale, float* dbg,
                                  hipStream_t stream) {
-  const dim3 grid((unsigned)((n_pools + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
 #define KVC_LAUNCH(RS, DBG)                                                                   \
   hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG>), grid, block, 0, stream, keys,          \
@@ -254,7 +294,7 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                               const int32_t* positions, int64_t num_requests, int next_n,
                               uint8_t* out_fp8, float* out_scale, int64_t num_out,
                               bool round_scale, hipStream_t stream) {
-  const dim3 grid((unsigned)((num_requests + kRowsPerBlock - 1) / kRowsPerBlock));
+  const dim3 grid((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
   if (round_scale)
     hipLaunchKernelGGL((pool16_ring_kernel<true>), grid, block, 0, stream, ring, num_blocks,
