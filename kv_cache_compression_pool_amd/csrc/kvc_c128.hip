@@ -80,8 +80,17 @@ __global__ __launch_bounds__(64) void c128_decode_kernel(
 }
 
 // ------------------------------------------------------------------ prefill
-constexpr int kPrefillBlock = 256;           // 4 waves
-constexpr int kTokPerLane = 16;              // 128 positions / (4 waves * 2 halves)
+#ifndef KVC_C128_COMPRESS_WAVES
+#define KVC_C128_COMPRESS_WAVES 4
+#endif
+#ifndef KVC_C128_WRITE_WAVES
+#define KVC_C128_WRITE_WAVES 8
+#endif
+// The compress pass has many plans and is bandwidth-bound: 4 waves per plan,
+// 16 chunk positions per lane.  The write pass has at most one plan per
+// request and is latency-bound: more waves per plan, fewer positions each.
+constexpr int kCompressWaves = KVC_C128_COMPRESS_WAVES;
+constexpr int kWriteWaves = KVC_C128_WRITE_WAVES;
 
 // Merge partial (m2, d2, a2) into (M, D, A); d = sum of e^{s-m}, a = sum of
 // k e^{s-m} (unnormalised).
@@ -95,13 +104,22 @@ __device__ __forceinline__ void merge_partial(float& M, float& D, float& A, floa
   M = mx;
 }
 
-template <bool kWrite>
-__global__ __launch_bounds__(kPrefillBlock) void c128_prefill_kernel(
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 128-bit load of an fp32 quad that does not keep the line cached.
+__device__ __forceinline__ float4 load_stream4(const float4* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+template <bool kWrite, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
     float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
     float* __restrict__ out, int64_t num_tokens, const float* __restrict__ ape,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ load_indices, int64_t batch,
     const kvc_online_plan* __restrict__ plans, uint32_t n_plans) {
-  __shared__ float s_m[4][128], s_d[4][128], s_a[4][128];
+  constexpr int kTokPerLane = 128 / (2 * kWaves);   // chunk positions per lane
+  __shared__ float s_m[kWaves][128], s_d[kWaves][128], s_a[kWaves][128];
 
   const uint32_t pid = blockIdx.x;
   if (pid >= n_plans) return;
@@ -115,16 +133,6 @@ __global__ __launch_bounds__(kPrefillBlock) void c128_prefill_kernel(
   const uint32_t off = pos127 + 1u - len;                       // first chunk position
   const uint32_t end = pos127 + 1u;                             // one past the last
   const int64_t seg0 = (int64_t)p.ragged_id - (int64_t)pos127;  // row of chunk position 0
-  int32_t load_idx = -1;
-  if (off != 0u) {
-    load_idx = load_indices[p.batch_id];
-    if (load_idx < 0 || (int64_t)load_idx >= num_slots) return;
-  }
-  int32_t store_idx = -1;
-  if constexpr (kWrite) {
-    store_idx = indices[p.batch_id];
-    if (store_idx < 0 || (int64_t)store_idx >= num_slots) return;
-  }
 
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -133,22 +141,39 @@ __global__ __launch_bounds__(kPrefillBlock) void c128_prefill_kernel(
   const float4* in4 = reinterpret_cast<const float4*>(in);
   const float4* ape4 = reinterpret_cast<const float4*>(ape);
 
+  // Everything below depends only on the plan, so the token rows, the slot
+  // indices and (for a segment that starts mid-chunk) the stored state are
+  // all requested before any of them is consumed.
   float4 kv[kTokPerLane], u[kTokPerLane];
   bool valid[kTokPerLane];
 #pragma unroll
   for (int i = 0; i < kTokPerLane; ++i) {
-    const uint32_t j = 32u * w + 2u * i + h;
+    const uint32_t j = 2u * kTokPerLane * w + 2u * i + h;
     valid[i] = j >= off && j < end;
     kv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     u[i] = make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
     if (valid[i]) {
       const int64_t r = seg0 + j;
-      kv[i] = in4[r * 64 + q];
-      const float4 sc = in4[r * 64 + 32 + q];
+      kv[i] = load_stream4(in4 + r * 64 + q);
+      const float4 sc = load_stream4(in4 + r * 64 + 32 + q);
       const float4 bi = ape4[j * 32 + q];
       u[i] = make_float4(sc.x + bi.x, sc.y + bi.y, sc.z + bi.z, sc.w + bi.w);
     }
   }
+  int32_t load_idx = -1;
+  if (off != 0u) load_idx = load_indices[p.batch_id];
+  int32_t store_idx = -1;
+  if constexpr (kWrite) store_idx = indices[p.batch_id];
+  const bool lead = (w == 0 && h == 0);    // the 32 lanes that finish the plan
+  const bool load_ok = load_idx >= 0 && (int64_t)load_idx < num_slots;
+  float4 m1 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = m1, k1 = m1;
+  if (lead && off != 0u && load_ok) {
+    const float4* st = reinterpret_cast<const float4*>(state + (int64_t)load_idx * 384);
+    m1 = st[q];
+    s1 = st[32 + q];
+    k1 = st[64 + q];
+  }
+
   float m[4] = {-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX};
 #pragma unroll
   for (int i = 0; i < kTokPerLane; ++i) {
@@ -187,7 +212,11 @@ __global__ __launch_bounds__(kPrefillBlock) void c128_prefill_kernel(
     }
   }
   __syncthreads();
-  if (w != 0 || h != 0) return;
+  if (!lead) return;
+  // A segment that needs the stored state but has no valid slot for it, or a
+  // write plan without a valid destination, is malformed: skip it.
+  if ((off != 0u && !load_ok) || (kWrite && (store_idx < 0 || (int64_t)store_idx >= num_slots)))
+    return;
 
   float M[4], D[4], A[4];
 #pragma unroll
@@ -195,7 +224,7 @@ __global__ __launch_bounds__(kPrefillBlock) void c128_prefill_kernel(
     M[k] = s_m[0][4 * q + k]; D[k] = s_d[0][4 * q + k]; A[k] = s_a[0][4 * q + k];
   }
 #pragma unroll
-  for (int ww = 1; ww < 4; ++ww)
+  for (int ww = 1; ww < kWaves; ++ww)
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       merge_partial(M[k], D[k], A[k], s_m[ww][4 * q + k], s_d[ww][4 * q + k], s_a[ww][4 * q + k]);
@@ -204,18 +233,16 @@ __global__ __launch_bounds__(kPrefillBlock) void c128_prefill_kernel(
   if (off != 0u) {
     // Merge with the stored state of the open chunk: (m1, s1, k1) with k1 a
     // normalised mean, i.e. an unnormalised sum k1 * s1.
-    const float4* st = reinterpret_cast<const float4*>(state + (int64_t)load_idx * 384);
-    const float4 m4 = st[q], s4 = st[32 + q], k4 = st[64 + q];
-    const float m1[4] = {m4.x, m4.y, m4.z, m4.w};
-    const float s1[4] = {s4.x, s4.y, s4.z, s4.w};
-    const float k1[4] = {k4.x, k4.y, k4.z, k4.w};
+    const float mm1[4] = {m1.x, m1.y, m1.z, m1.w};
+    const float ss1[4] = {s1.x, s1.y, s1.z, s1.w};
+    const float kk1[4] = {k1.x, k1.y, k1.z, k1.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float mx = fmaxf(m1[k], M[k]);
-      const float f1 = s1[k] * exp2_hw((m1[k] - mx) * kLog2e);
+      const float mx = fmaxf(mm1[k], M[k]);
+      const float f1 = ss1[k] * exp2_hw((mm1[k] - mx) * kLog2e);
       const float f2 = exp2_hw((M[k] - mx) * kLog2e);
       const float sum = f1 + D[k] * f2;
-      K[k] = (k1[k] * f1 + A[k] * f2) / sum;
+      K[k] = (kk1[k] * f1 + A[k] * f2) / sum;
       D[k] = sum;
       M[k] = mx;
     }
@@ -254,14 +281,16 @@ hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in,
   // Pass 1 (compress plans) only reads the state; pass 2 (write plans) writes
   // it.  Stream order puts every pass-1 read before any pass-2 write.
   if (n_c) {
-    hipLaunchKernelGGL((c128_prefill_kernel<false>), dim3(n_c), dim3(kPrefillBlock), 0, stream,
+    hipLaunchKernelGGL((c128_prefill_kernel<false, kCompressWaves>), dim3(n_c),
+                       dim3(64 * kCompressWaves), 0, stream,
                        state, num_slots, in, out, num_tokens, ape, indices, load_indices, batch,
                        cplan, n_c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n_w) {
-    hipLaunchKernelGGL((c128_prefill_kernel<true>), dim3(n_w), dim3(kPrefillBlock), 0, stream,
+    hipLaunchKernelGGL((c128_prefill_kernel<true, kWriteWaves>), dim3(n_w),
+                       dim3(64 * kWriteWaves), 0, stream,
                        state, num_slots, in, out, num_tokens, ape, indices, load_indices, batch,
                        wplan, n_w);
     return hipGetLastError();
