@@ -173,6 +173,26 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                              uint8_t* out_fp8, float* out_scale, int64_t num_out,
                              int round_scale, void* stream);
 
+/* Tail-ring seeding from a prefill batch (kpool_compress page,
+ * _kpool_tail_seed_kernel and kpool_seed_tail_cache).  Token i carries tail
+ * slot tslot[i] = block*16 + position%16, or a negative value for padding.
+ * Token i is among its request's last 16 tokens exactly when the token 16
+ * places ahead is past the batch, is padding, or lies in another block; its
+ * key and score rows are then copied into slot tslot[i]%16 of ring block
+ * tslot[i]/16 (blocks >= num_ring_blocks are skipped).  Each request's
+ * tokens must be contiguous in the batch and requests must own distinct
+ * blocks.
+ *   tail_ring     device bf16 [num_ring_blocks, 2, 16, 128], updated in place
+ *   key, score    device bf16 [n_tokens, *] with row strides in elements
+ *                 (multiples of 8, >= 128)
+ *   tslot         device int32 [n_tokens]
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_UNSUPPORTED (pool_size != 16),
+ *         KVC_ERR_HIP. */
+int kvc_seed_tail_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
+                       const uint16_t* key, int64_t key_row_stride,
+                       const uint16_t* score, int64_t score_row_stride,
+                       const int32_t* tslot, int64_t n_tokens, int pool_size, void* stream);
+
 /* Pool-128 online decode (c128_online.cuh page, flash_c128_online_decode).
  * Request b appends one token at position seq_lens[b]-1; c = that position
  * mod 128 picks bias row ape[c]; s = score + ape[c].

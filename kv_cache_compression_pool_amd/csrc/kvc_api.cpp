@@ -203,6 +203,28 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                     "kvc_compress_decode_ring launch");
 }
 
+int kvc_seed_tail_ring(uint16_t* tail_ring, int64_t num_ring_blocks, const uint16_t* key,
+                       int64_t key_row_stride, const uint16_t* score, int64_t score_row_stride,
+                       const int32_t* tslot, int64_t n_tokens, int pool_size, void* stream) {
+  if (pool_size != kPool)
+    return fail(KVC_ERR_UNSUPPORTED, "kvc_seed_tail_ring: pool_size %d (only 16)", pool_size);
+  if (n_tokens < 0 || num_ring_blocks < 0)
+    return fail(KVC_ERR_SHAPE, "kvc_seed_tail_ring: negative size");
+  if (n_tokens == 0) return ok();
+  if (!tail_ring || !key || !score || !tslot)
+    return fail(KVC_ERR_NULL, "kvc_seed_tail_ring: NULL pointer");
+  if (key_row_stride < kHeadDim || score_row_stride < kHeadDim || key_row_stride % 8 ||
+      score_row_stride % 8)
+    return fail(KVC_ERR_SHAPE, "kvc_seed_tail_ring: row strides must be >= 128 and a multiple of 8");
+  if (!aligned(tail_ring, 16) || !aligned(key, 16) || !aligned(score, 16) || !aligned(tslot, 4))
+    return fail(KVC_ERR_SHAPE, "kvc_seed_tail_ring: misaligned pointer");
+  if (n_tokens > kMaxI32) return fail(KVC_ERR_SHAPE, "kvc_seed_tail_ring: n_tokens exceeds 2^31-1");
+  return hip_status(kvc::launch_pool16_seed(tail_ring, num_ring_blocks, key, key_row_stride,
+                                            score, score_row_stride, tslot, n_tokens,
+                                            (hipStream_t)stream),
+                    "kvc_seed_tail_ring launch");
+}
+
 // --------------------------------------------------------------- pool-128
 int kvc_c128_online_decode(float* state, int64_t num_slots, const float* kv_score_in, float* out,
                            const float* ape, const int32_t* indices, const int32_t* seq_lens,

@@ -24,6 +24,10 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                               uint8_t* out_fp8, float* out_scale, int64_t num_out,
                               bool round_scale, hipStream_t stream);
 
+hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t* key,
+                              int64_t key_stride, const uint16_t* score, int64_t score_stride,
+                              const int32_t* tslot, int64_t n_tokens, hipStream_t stream);
+
 hipError_t launch_c128_decode(float* state, int64_t num_slots, const float* in, float* out,
                               const float* ape, const int32_t* indices, const int32_t* seq_lens,
                               int64_t batch, hipStream_t stream);

@@ -247,6 +247,31 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
   }
 }
 
+// Tail-ring seeding: one 16-lane row per token copies its 256 B key and
+// score rows when it is among its request's last 16 tokens.
+__global__ __launch_bounds__(256) void pool16_seed_kernel(uint16_t* __restrict__ ring,
+                                                          int64_t num_blocks,
+                                                          const uint16_t* __restrict__ key,
+                                                          int64_t key_stride,
+                                                          const uint16_t* __restrict__ score,
+                                                          int64_t score_stride,
+                                                          const int32_t* __restrict__ tslot,
+                                                          int64_t n_tokens) {
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  if (i >= n_tokens) return;
+  const int64_t t = tslot[i];
+  if (t < 0) return;
+  const int64_t blk = t / kPool;
+  const int64_t ahead = (i + kPool < n_tokens) ? (int64_t)tslot[i + kPool] : -1;
+  if (ahead >= 0 && ahead / kPool == blk) return;     // a later token owns this slot
+  if (blk >= num_blocks) return;
+  uint16_t* rk = ring + blk * (2 * kPool * 128) + (t % kPool) * 128;
+  uint16_t* rs = rk + kPool * 128;
+  reinterpret_cast<uint4*>(rk)[c] = reinterpret_cast<const uint4*>(key + i * key_stride)[c];
+  reinterpret_cast<uint4*>(rs)[c] = reinterpret_cast<const uint4*>(score + i * score_stride)[c];
+}
+
 __global__ __launch_bounds__(256) void diag_convert_kernel(const float* __restrict__ in,
                                                            uint16_t* __restrict__ bf16_out,
                                                            uint8_t* __restrict__ fp8_out,
@@ -306,6 +331,15 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                        tail_slot, key, key_sb, key_st, score, score_sb, score_st, ape,
                        slot_mapping, positions, num_requests, next_n, out_fp8, out_scale,
                        num_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t* key,
+                              int64_t key_stride, const uint16_t* score, int64_t score_stride,
+                              const int32_t* tslot, int64_t n_tokens, hipStream_t stream) {
+  const dim3 grid((unsigned)((n_tokens + 15) / 16));
+  hipLaunchKernelGGL(pool16_seed_kernel, grid, dim3(256), 0, stream, ring, num_blocks, key,
+                     key_stride, score, score_stride, tslot, n_tokens);
   return hipGetLastError();
 }
 

@@ -28,8 +28,8 @@ PLAN_DTYPE = np.dtype([("ragged_id", "<u4"), ("batch_id", "<u4"), ("position", "
 PLAN_SENTINEL = 0xFFFFFFFF
 
 EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_plan_prefill",
-           "kvc_compress_prefill", "kvc_compress_decode_ring", "kvc_c128_online_decode",
-           "kvc_c128_online_prefill", "kvc_diag_convert")
+           "kvc_compress_prefill", "kvc_compress_decode_ring", "kvc_seed_tail_ring",
+           "kvc_c128_online_decode", "kvc_c128_online_prefill", "kvc_diag_convert")
 
 
 class KvcError(RuntimeError):
@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
                                            _i32, _p, _p]
         L.kvc_compress_decode_ring.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p,
                                                _p, _p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p]
+        L.kvc_seed_tail_ring.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _p]
         L.kvc_c128_online_decode.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]
         L.kvc_c128_online_prefill.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _p, _u32,
                                               _p, _u32, _p]
@@ -203,6 +204,25 @@ def kvc_compress_decode_ring(tail_ring, tail_slot_mapping, key, score, ape, slot
         _dptr(positions, torch.int32, "positions"), R, N, pool_size,
         _dptr(out_fp8, torch.uint8, "out_fp8"), _dptr(out_scale, torch.float32, "out_scale"),
         out_fp8.shape[0], int(round_scale), _stream(stream)))
+
+
+def kvc_seed_tail_ring(tail_ring, key, score, tslot, pool_size: int = 16, stream=None):
+    """tail_ring bf16 [nb,2,16,128] (updated); key/score bf16 [n,>=128];
+    tslot int32 [n]."""
+    import torch
+    ring = _bf16_view(tail_ring, "tail_ring", min_last=None)
+    k = _bf16_view(key, "key")
+    s = _bf16_view(score, "score")
+    n = int(tslot.shape[0])
+    _need(ring.is_contiguous() and tuple(ring.shape[1:]) == (2, pool_size, 128),
+          f"tail_ring must be a contiguous [nb, 2, {pool_size}, 128] tensor")
+    _need(k.dim() == 2 and s.dim() == 2 and k.shape[0] >= n and s.shape[0] >= n,
+          "key and score must hold one row per token")
+    _shape_ok(tslot, (n,), "tslot")
+    _check(lib().kvc_seed_tail_ring(ring.data_ptr(), ring.shape[0], k.data_ptr(), k.stride(0),
+                                    s.data_ptr(), s.stride(0),
+                                    _dptr(tslot, torch.int32, "tslot"), n, pool_size,
+                                    _stream(stream)))
 
 
 def kvc_c128_online_decode(state, kv_score_in, out, ape, indices, seq_lens, stream=None):

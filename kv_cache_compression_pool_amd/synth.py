@@ -21,6 +21,8 @@ Workloads (all head_dim 128):
                   uniform in [1, 131072], prior chunk tokens to build the state.
   c128_prefill    32 sequences, prior uniform in [0, 32768], extend uniform in
                   [1, 16384], 2048 state slots, prior chunk tokens for the state.
+  pool16_seed     a prefill batch (64 sequences, lengths uniform in [1, 8192])
+                  whose last 16 tokens per request seed the tail rings.
 """
 from __future__ import annotations
 
@@ -31,7 +33,7 @@ HEAD_DIM = 128
 BF16_NAN = np.uint16(0x7FC0)
 
 _STREAMS = {"pool16_single": 1, "pool16_ragged": 2, "pool16_ring": 3,
-            "c128_decode": 4, "c128_prefill": 5, "misc": 99}
+            "c128_decode": 4, "c128_prefill": 5, "pool16_seed": 6, "misc": 99}
 
 
 def rng(seed: int, name: str) -> np.random.Generator:
@@ -102,6 +104,27 @@ def pool16_ring(seed: int = 0, num_requests: int = 256, next_n: int = 4,
     return dict(ring=ring, tail_slot_mapping=tail_slot, key=key, score=score, ape=ape,
                 slot_mapping=slot_mapping, positions=positions, num_out=R,
                 round_scale=True)
+
+
+def pool16_seed(seed: int = 0, num_seqs: int = 64, max_len: int = 8192, pad_tokens: int = 0,
+                pool: int = 16):
+    """A prefill batch whose requests seed their tail rings: request b owns
+    ring block b and seq_lens[b] consecutive tokens at positions 0..len-1;
+    tail slot = 16*b + pos%16.  ``pad_tokens`` padding entries (slot -1, NaN
+    rows) follow the last request."""
+    g = rng(seed, "pool16_seed")
+    lens = g.integers(1, max_len, size=num_seqs, endpoint=True).astype(np.int64)
+    T = int(lens.sum()) + pad_tokens
+    req = np.repeat(np.arange(num_seqs), lens)
+    pos = np.concatenate([np.arange(n) for n in lens]) if num_seqs else np.zeros(0, np.int64)
+    tslot = np.full(T, -1, np.int32)
+    tslot[:req.size] = req * pool + pos % pool
+    key = bf16_normal(g, (T, HEAD_DIM))
+    score = bf16_normal(g, (T, HEAD_DIM))
+    key[req.size:] = BF16_NAN
+    score[req.size:] = BF16_NAN
+    ring = bf16_normal(g, (num_seqs, 2, pool, HEAD_DIM))
+    return dict(key=key, score=score, tslot=tslot, ring=ring, seq_lens=lens)
 
 
 # ------------------------------------------------------------------ pool-128 online

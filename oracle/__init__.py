@@ -79,6 +79,7 @@ def _declare(L):
     L.orc_pool_plan.restype = _i64
     L.orc_ring_decode.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _p,
                                   _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _p]
+    L.orc_seed_tail_ring.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32]
     L.orc_c128_decode.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _i64]
     L.orc_c128_plan.argtypes = [_p, _p, _i64, _i64, _p, _p, _i32, _p, _p]
     L.orc_c128_plan.restype = _i32
@@ -233,6 +234,18 @@ def ring_decode(ring, tail_slot_mapping, key, score, ape, slot_mapping, position
                           _ptr(pools_out[0]) if pools_out else None,
                           _ptr(pools_out[1]) if pools_out else None)
     return out_code, out_scale
+
+
+def seed_tail_ring(ring, key, score, tslot, pool_size: int = 16):
+    """Seed the tail ring ([nb,2,P,128] u16, updated in place) from a prefill
+    batch: key/score [n,128] bf16 patterns, tslot [n] int32."""
+    assert ring.dtype == np.uint16 and ring.flags["C_CONTIGUOUS"]
+    k = _c(key, np.uint16)
+    s = _c(score, np.uint16)
+    ts = _c(tslot, np.int32)
+    lib().orc_seed_tail_ring(_ptr(ring), ring.shape[0], _ptr(k), k.shape[1], _ptr(s), s.shape[1],
+                             _ptr(ts), ts.size, pool_size)
+    return ring
 
 
 # ---------------------------------------------------------------- pool-128 online

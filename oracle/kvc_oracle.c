@@ -316,6 +316,30 @@ void orc_ring_decode(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slo
     }
 }
 
+/* Tail-ring seeding from a prefill batch ([KP] _kpool_tail_seed_kernel).
+ * Token i of the batch carries tail slot tslot[i] = block*P + pos%P, or a
+ * negative value for padding.  Token i belongs to its request's last P tokens
+ * exactly when the token P places ahead is past the batch, is padding, or
+ * lies in another block; such a token's key and score rows are copied into
+ * slot tslot%P of its block.  Blocks at or beyond num_blocks are skipped. */
+void orc_seed_tail_ring(uint16_t* ring, int64_t num_blocks,
+                        const uint16_t* key, int64_t key_stride,
+                        const uint16_t* score, int64_t score_stride,
+                        const int32_t* tslot, int64_t n_tokens, int P) {
+    for (int64_t i = 0; i < n_tokens; ++i) {
+        int64_t t = tslot[i];
+        if (t < 0) continue;
+        int64_t blk = t / P;
+        int64_t ahead = (i + P < n_tokens) ? (int64_t)tslot[i + P] : -1;
+        if (ahead >= 0 && ahead / P == blk) continue;
+        if (blk >= num_blocks) continue;
+        uint16_t* rk = ring + blk * 2 * P * 128 + (t % P) * 128;
+        uint16_t* rs = rk + P * 128;
+        memcpy(rk, key + i * key_stride, 256);
+        memcpy(rs, score + i * score_stride, 256);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Pool-128 online state ([C128] decode and prefill kernels)                */
 /* ------------------------------------------------------------------------ */

@@ -409,3 +409,63 @@ def test_c128_prefill_distinct_load_indices():
     rows = ~np.isnan(ref[:, 0])
     assert rel_err_rows(gout[rows], ref[rows]).max(initial=0) <= VEC_TOL
     compare_state(gst, st, "c128 prefill load_indices")
+
+
+# ------------------------------------------------------------------ tail-ring seeding
+@pytest.mark.parametrize("num_seqs,max_len,pad,blocks", [(64, 8192, 0, None), (30, 40, 13, None),
+                                                         (7, 5, 0, None), (12, 100, 3, 9)])
+def test_seed_tail_ring_bit_exact(num_seqs, max_len, pad, blocks):
+    d = synth.pool16_seed(seed=num_seqs, num_seqs=num_seqs, max_len=max_len, pad_tokens=pad)
+    ring0 = d["ring"] if blocks is None else d["ring"][:blocks].copy()
+    note(f"seed tail ring: {num_seqs} seqs, {d['tslot'].size} tokens, {ring0.shape[0]} blocks")
+    ref = ring0.copy()
+    oracle.seed_tail_ring(ref, d["key"], d["score"], d["tslot"])
+    g = dev(ring0, torch.int16)
+    kvc.kvc_seed_tail_ring(g, dev(d["key"], torch.int16), dev(d["score"], torch.int16),
+                           dev(d["tslot"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(g.cpu().numpy().view(np.uint16), ref)
+
+
+def test_seed_then_decode_continues_the_sequence():
+    """Seed rings from a prefill batch, then decode the next tokens: every pool
+    completed in decode must equal the prefill-path compression of the same
+    16 consecutive tokens."""
+    d = synth.pool16_seed(seed=5, num_seqs=16, max_len=300)
+    g = np.random.default_rng(6)
+    ape = synth.ape_pool16(g)
+    R, N = 16, 20
+    lens = d["seq_lens"]
+    nk = synth.bf16_normal(g, (R, N, 128))
+    ns = synth.bf16_normal(g, (R, N, 128))
+    pos = (lens[:, None] + np.arange(N)).astype(np.int32)
+    ts = (np.arange(R)[:, None] * 16 + pos % 16).astype(np.int32)
+    loc = np.where(pos % 16 == 15, np.arange(R)[:, None] * 2 + (pos // 16) % 2, -1).astype(np.int32)
+    gring = dev(d["ring"], torch.int16)
+    kvc.kvc_seed_tail_ring(gring, dev(d["key"], torch.int16), dev(d["score"], torch.int16),
+                           dev(d["tslot"]))
+    out = torch.full((2 * R, 128), 0x33, dtype=torch.uint8, device="cuda")
+    scl = torch.full((2 * R,), 5.0, device="cuda")
+    kvc.kvc_compress_decode_ring(gring, dev(ts), dev(nk, torch.int16), dev(ns, torch.int16),
+                                 dev(ape), dev(loc), dev(pos), out, scl, True)
+    torch.cuda.synchronize()
+    gc, gs = out.cpu().numpy(), scl.cpu().numpy()
+    starts = synth.ragged_starts(lens)
+    checked = 0
+    for r in range(R):
+        allk = np.concatenate([d["key"][starts[r]:starts[r] + lens[r]], nk[r]])
+        alls = np.concatenate([d["score"][starts[r]:starts[r] + lens[r]], ns[r]])
+        for t in range(N):
+            p = int(pos[r, t])
+            if p % 16 != 15 or p < 15:
+                continue
+            rows = np.arange(p - 15, p + 1)
+            rc, rs, rx = oracle.compress_prefill(allk[rows], alls[rows], ape, None, True)
+            pc, ps, px = run_prefill_gpu(allk[rows], alls[rows], ape, None, 1, True)
+            l = loc[r, t]
+            assert np.array_equal(gc[l], pc[0]) and gs[l] == ps[0]
+            ref_c, ref_s, _ = reference_for(px[:1], rx, rc, rs, True, "seeded ring")
+            check_codes(gc[l][None], ref_c, "seeded ring")
+            check_scales(gs[l:l + 1], ref_s, True, "seeded ring")
+            checked += 1
+    assert checked >= 16

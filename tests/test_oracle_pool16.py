@@ -316,3 +316,34 @@ def test_ring_decode_negative_tail_slot_reads_block_zero():
     c2, s2, _, _ = oracle.pool_compress(pk, ps, ape, False)
     assert np.array_equal(c[0], c2) and s[0] == s2
     assert np.array_equal(ring, ring0)
+
+
+# ------------------------------------------------------------------ tail seeding
+def _seed_bruteforce(ring, d):
+    """Plain definition: each request's last min(16, len) tokens land in slot
+    pos % 16 of its block; nothing else changes."""
+    out = ring.copy()
+    start = 0
+    for b, n in enumerate(d["seq_lens"]):
+        for pos in range(max(0, n - 16), n):
+            out[b, 0, pos % 16] = d["key"][start + pos]
+            out[b, 1, pos % 16] = d["score"][start + pos]
+        start += n
+    return out
+
+
+@pytest.mark.parametrize("seed,num_seqs,max_len,pad", [(0, 9, 60, 0), (1, 12, 20, 7), (2, 3, 3, 30),
+                                                       (3, 40, 300, 16)])
+def test_seed_tail_ring_matches_last_tokens_per_request(seed, num_seqs, max_len, pad):
+    d = synth.pool16_seed(seed=seed, num_seqs=num_seqs, max_len=max_len, pad_tokens=pad)
+    ref = _seed_bruteforce(d["ring"], d)
+    ring = d["ring"].copy()
+    oracle.seed_tail_ring(ring, d["key"], d["score"], d["tslot"])
+    assert np.array_equal(ring, ref)
+
+
+def test_seed_tail_ring_skips_blocks_beyond_the_ring():
+    d = synth.pool16_seed(seed=4, num_seqs=5, max_len=40)
+    ring = d["ring"][:3].copy()            # requests 3 and 4 have no block
+    oracle.seed_tail_ring(ring, d["key"], d["score"], d["tslot"])
+    assert np.array_equal(ring, _seed_bruteforce(d["ring"], d)[:3])
