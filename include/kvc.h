@@ -141,6 +141,28 @@ int kvc_compress_prefill(const uint16_t* keys, int64_t key_row_stride,
                          uint8_t* out_fp8, float* out_scale, int round_scale,
                          float* dbg_pooled, void* stream);
 
+/* Pool-16 prefill compression written into a paged indexer K cache
+ * (kpool_compress page, kpool_compress_and_write_cache with write_cache and an
+ * optional write_mask).  Only page_size 1 is supported: the page's token
+ * order for larger pages (its preshuffled 16-token tiles) is not specified.
+ * With page_size 1 the cache is [num_pages, 1, 132] bytes: page loc[p] holds
+ * the 128 e4m3 codes of pool p at bytes 0..127 and its fp32 scale at bytes
+ * 128..131.  Pools whose write_mask byte is 0, or whose page is outside
+ * [0, num_pages), are skipped (no rows read, nothing written).
+ *   keys, scores, ape, pool_src_row, n_pools, round_scale: as
+ *                 kvc_compress_prefill
+ *   kv_cache      device uint8 [num_pages, 132], 4-byte aligned
+ *   loc           device int64 [n_pools]
+ *   write_mask    device uint8 (bool) [n_pools] or NULL (write all)
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_UNSUPPORTED (pool_size != 16
+ *         or page_size != 1), KVC_ERR_HIP. */
+int kvc_compress_prefill_paged(const uint16_t* keys, int64_t key_row_stride,
+                               const uint16_t* scores, int64_t score_row_stride, int64_t num_rows,
+                               const float* ape, int pool_size, const int32_t* pool_src_row,
+                               int64_t n_pools, uint8_t* kv_cache, int64_t num_pages,
+                               int page_size, const int64_t* loc, const uint8_t* write_mask,
+                               int round_scale, void* stream);
+
 /* Pool-16 decode with a tail ring and ordered verify tokens (kpool_compress
  * page, _kpool_decode_update_batched_kernel).  Request r processes its tokens
  * t = 0..next_n-1 strictly in order; for entry e = r*next_n + t:
@@ -172,6 +194,21 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                              int64_t num_requests, int next_n, int pool_size,
                              uint8_t* out_fp8, float* out_scale, int64_t num_out,
                              int round_scale, void* stream);
+
+/* kvc_compress_decode_ring writing completions into a page-size-1 paged cache
+ * instead of packed arrays (the page's cache-write path): slot_mapping[e] is
+ * the page; pages outside [0, num_pages) are skipped.  kv_cache as in
+ * kvc_compress_prefill_paged.  Errors: as kvc_compress_decode_ring, plus
+ * KVC_ERR_UNSUPPORTED for page_size != 1. */
+int kvc_compress_decode_ring_paged(uint16_t* tail_ring, int64_t num_ring_blocks,
+                                   const int32_t* tail_slot_mapping,
+                                   const uint16_t* key, int64_t key_stride_b,
+                                   int64_t key_stride_t, const uint16_t* score,
+                                   int64_t score_stride_b, int64_t score_stride_t,
+                                   const float* ape, const int32_t* slot_mapping,
+                                   const int32_t* positions, int64_t num_requests, int next_n,
+                                   int pool_size, uint8_t* kv_cache, int64_t num_pages,
+                                   int page_size, int round_scale, void* stream);
 
 /* Tail-ring seeding from a prefill batch (kpool_compress page,
  * _kpool_tail_seed_kernel and kpool_seed_tail_cache).  Token i carries tail

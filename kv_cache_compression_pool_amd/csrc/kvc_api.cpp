@@ -142,34 +142,93 @@ int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, i
 }
 
 // --------------------------------------------------------------- pool-16
+namespace {
+
+// Checks shared by the packed and paged prefill entry points; returns KVC_OK
+// when the pool inputs are usable.
+int check_prefill_inputs(const char* fn, const uint16_t* keys, int64_t key_row_stride,
+                         const uint16_t* scores, int64_t score_row_stride, int64_t num_rows,
+                         const float* ape, int pool_size, const int32_t* pool_src_row,
+                         int64_t n_pools) {
+  if (pool_size != kPool) return fail(KVC_ERR_UNSUPPORTED, "%s: pool_size %d (only 16)", fn, pool_size);
+  if (!keys || !scores || !ape) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (key_row_stride < kHeadDim || score_row_stride < kHeadDim || key_row_stride % 8 ||
+      score_row_stride % 8)
+    return fail(KVC_ERR_SHAPE, "%s: row strides must be >= 128 and a multiple of 8", fn);
+  if (!aligned(keys, 16) || !aligned(scores, 16) || !aligned(ape, 16))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  if (n_pools > kMaxI32 || num_rows > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "%s: sizes exceed 2^31-1", fn);
+  if (!pool_src_row && n_pools * kPool > num_rows)
+    return fail(KVC_ERR_SHAPE, "%s: %lld pools need %lld rows, have %lld", fn, (long long)n_pools,
+                (long long)(n_pools * kPool), (long long)num_rows);
+  return KVC_OK;
+}
+
+int check_ring_inputs(const char* fn, const uint16_t* tail_ring, const int32_t* tail_slot_mapping,
+                      const uint16_t* key, int64_t key_stride_b, int64_t key_stride_t,
+                      const uint16_t* score, int64_t score_stride_b, int64_t score_stride_t,
+                      const float* ape, const int32_t* slot_mapping, const int32_t* positions,
+                      int64_t num_requests, int next_n) {
+  if (!tail_ring || !tail_slot_mapping || !key || !score || !ape || !slot_mapping || !positions)
+    return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (key_stride_b < 0 || key_stride_t < 0 || score_stride_b < 0 || score_stride_t < 0 ||
+      key_stride_b % 8 || key_stride_t % 8 || score_stride_b % 8 || score_stride_t % 8)
+    return fail(KVC_ERR_SHAPE, "%s: strides must be non-negative multiples of 8", fn);
+  if (!aligned(tail_ring, 16) || !aligned(key, 16) || !aligned(score, 16) || !aligned(ape, 16))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  if (num_requests * (int64_t)next_n > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "%s: sizes exceed 2^31-1", fn);
+  return KVC_OK;
+}
+
+}  // namespace
+
 int kvc_compress_prefill(const uint16_t* keys, int64_t key_row_stride, const uint16_t* scores,
                          int64_t score_row_stride, int64_t num_rows, const float* ape,
                          int pool_size, const int32_t* pool_src_row, int64_t n_pools,
                          uint8_t* out_fp8, float* out_scale, int round_scale, float* dbg_pooled,
                          void* stream) {
-  if (pool_size != kPool)
-    return fail(KVC_ERR_UNSUPPORTED, "kvc_compress_prefill: pool_size %d (only 16)", pool_size);
-  if (n_pools < 0 || num_rows < 0)
-    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: negative size");
+  const char* fn = "kvc_compress_prefill";
+  if (pool_size != kPool) return fail(KVC_ERR_UNSUPPORTED, "%s: pool_size %d (only 16)", fn, pool_size);
+  if (n_pools < 0 || num_rows < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
   if (n_pools == 0) return ok();
-  if (!keys || !scores || !ape || !out_fp8 || !out_scale)
-    return fail(KVC_ERR_NULL, "kvc_compress_prefill: NULL pointer");
-  if (key_row_stride < kHeadDim || score_row_stride < kHeadDim || key_row_stride % 8 ||
-      score_row_stride % 8)
-    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: row strides must be >= 128 and a multiple of 8");
-  if (!aligned(keys, 16) || !aligned(scores, 16) || !aligned(ape, 16) || !aligned(out_fp8, 8) ||
-      !aligned(out_scale, 4) || (dbg_pooled && !aligned(dbg_pooled, 16)))
-    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: misaligned pointer");
-  if (n_pools > kMaxI32 || num_rows > kMaxI32)
-    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: sizes exceed 2^31-1");
-  if (!pool_src_row && n_pools * kPool > num_rows)
-    return fail(KVC_ERR_SHAPE, "kvc_compress_prefill: %lld pools need %lld rows, have %lld",
-                (long long)n_pools, (long long)(n_pools * kPool), (long long)num_rows);
+  int rc = check_prefill_inputs(fn, keys, key_row_stride, scores, score_row_stride, num_rows, ape,
+                                pool_size, pool_src_row, n_pools);
+  if (rc != KVC_OK) return rc;
+  if (!out_fp8 || !out_scale) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (!aligned(out_fp8, 8) || !aligned(out_scale, 4) || (dbg_pooled && !aligned(dbg_pooled, 16)))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
   return hip_status(kvc::launch_pool16_prefill(keys, key_row_stride, scores, score_row_stride,
                                                num_rows, ape, pool_src_row, n_pools, out_fp8,
-                                               out_scale, round_scale != 0, dbg_pooled,
-                                               (hipStream_t)stream),
+                                               out_scale, n_pools, false, nullptr, nullptr,
+                                               round_scale != 0, dbg_pooled, (hipStream_t)stream),
                     "kvc_compress_prefill launch");
+}
+
+int kvc_compress_prefill_paged(const uint16_t* keys, int64_t key_row_stride,
+                               const uint16_t* scores, int64_t score_row_stride, int64_t num_rows,
+                               const float* ape, int pool_size, const int32_t* pool_src_row,
+                               int64_t n_pools, uint8_t* kv_cache, int64_t num_pages,
+                               int page_size, const int64_t* loc, const uint8_t* write_mask,
+                               int round_scale, void* stream) {
+  const char* fn = "kvc_compress_prefill_paged";
+  if (pool_size != kPool) return fail(KVC_ERR_UNSUPPORTED, "%s: pool_size %d (only 16)", fn, pool_size);
+  if (page_size != 1)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: page_size %d (only 1: the larger pages' token order is not specified)", fn, page_size);
+  if (n_pools < 0 || num_rows < 0 || num_pages < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (n_pools == 0) return ok();
+  int rc = check_prefill_inputs(fn, keys, key_row_stride, scores, score_row_stride, num_rows, ape,
+                                pool_size, pool_src_row, n_pools);
+  if (rc != KVC_OK) return rc;
+  if (!kv_cache || !loc) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (!aligned(kv_cache, 4) || !aligned(loc, 8))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  return hip_status(kvc::launch_pool16_prefill(keys, key_row_stride, scores, score_row_stride,
+                                               num_rows, ape, pool_src_row, n_pools, kv_cache,
+                                               nullptr, num_pages, true, loc, write_mask,
+                                               round_scale != 0, nullptr, (hipStream_t)stream),
+                    "kvc_compress_prefill_paged launch");
 }
 
 int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
@@ -179,28 +238,55 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                              const int32_t* slot_mapping, const int32_t* positions,
                              int64_t num_requests, int next_n, int pool_size, uint8_t* out_fp8,
                              float* out_scale, int64_t num_out, int round_scale, void* stream) {
-  if (pool_size != kPool)
-    return fail(KVC_ERR_UNSUPPORTED, "kvc_compress_decode_ring: pool_size %d (only 16)", pool_size);
+  const char* fn = "kvc_compress_decode_ring";
+  if (pool_size != kPool) return fail(KVC_ERR_UNSUPPORTED, "%s: pool_size %d (only 16)", fn, pool_size);
   if (num_requests < 0 || next_n < 0 || num_ring_blocks < 0 || num_out < 0)
-    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: negative size");
+    return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
   if (num_requests == 0 || next_n == 0) return ok();
-  if (!tail_ring || !tail_slot_mapping || !key || !score || !ape || !slot_mapping || !positions ||
-      (num_out > 0 && (!out_fp8 || !out_scale)))
-    return fail(KVC_ERR_NULL, "kvc_compress_decode_ring: NULL pointer");
-  if (key_stride_b < 0 || key_stride_t < 0 || score_stride_b < 0 || score_stride_t < 0 ||
-      key_stride_b % 8 || key_stride_t % 8 || score_stride_b % 8 || score_stride_t % 8)
-    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: strides must be non-negative multiples of 8");
-  if (!aligned(tail_ring, 16) || !aligned(key, 16) || !aligned(score, 16) || !aligned(ape, 16) ||
-      (num_out > 0 && (!aligned(out_fp8, 8) || !aligned(out_scale, 4))))
-    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: misaligned pointer");
-  if (num_requests * (int64_t)next_n > kMaxI32 || num_out > kMaxI32)
-    return fail(KVC_ERR_SHAPE, "kvc_compress_decode_ring: sizes exceed 2^31-1");
+  int rc = check_ring_inputs(fn, tail_ring, tail_slot_mapping, key, key_stride_b, key_stride_t,
+                             score, score_stride_b, score_stride_t, ape, slot_mapping, positions,
+                             num_requests, next_n);
+  if (rc != KVC_OK) return rc;
+  if (num_out > 0 && (!out_fp8 || !out_scale)) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (num_out > 0 && (!aligned(out_fp8, 8) || !aligned(out_scale, 4)))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  if (num_out > kMaxI32) return fail(KVC_ERR_SHAPE, "%s: num_out exceeds 2^31-1", fn);
   return hip_status(kvc::launch_pool16_ring(tail_ring, num_ring_blocks, tail_slot_mapping, key,
                                             key_stride_b, key_stride_t, score, score_stride_b,
                                             score_stride_t, ape, slot_mapping, positions,
                                             num_requests, next_n, out_fp8, out_scale, num_out,
-                                            round_scale != 0, (hipStream_t)stream),
+                                            false, round_scale != 0, (hipStream_t)stream),
                     "kvc_compress_decode_ring launch");
+}
+
+int kvc_compress_decode_ring_paged(uint16_t* tail_ring, int64_t num_ring_blocks,
+                                   const int32_t* tail_slot_mapping, const uint16_t* key,
+                                   int64_t key_stride_b, int64_t key_stride_t,
+                                   const uint16_t* score, int64_t score_stride_b,
+                                   int64_t score_stride_t, const float* ape,
+                                   const int32_t* slot_mapping, const int32_t* positions,
+                                   int64_t num_requests, int next_n, int pool_size,
+                                   uint8_t* kv_cache, int64_t num_pages, int page_size,
+                                   int round_scale, void* stream) {
+  const char* fn = "kvc_compress_decode_ring_paged";
+  if (pool_size != kPool) return fail(KVC_ERR_UNSUPPORTED, "%s: pool_size %d (only 16)", fn, pool_size);
+  if (page_size != 1)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: page_size %d (only 1: the larger pages' token order is not specified)", fn, page_size);
+  if (num_requests < 0 || next_n < 0 || num_ring_blocks < 0 || num_pages < 0)
+    return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (num_requests == 0 || next_n == 0) return ok();
+  int rc = check_ring_inputs(fn, tail_ring, tail_slot_mapping, key, key_stride_b, key_stride_t,
+                             score, score_stride_b, score_stride_t, ape, slot_mapping, positions,
+                             num_requests, next_n);
+  if (rc != KVC_OK) return rc;
+  if (num_pages > 0 && !kv_cache) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (num_pages > 0 && !aligned(kv_cache, 4)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  return hip_status(kvc::launch_pool16_ring(tail_ring, num_ring_blocks, tail_slot_mapping, key,
+                                            key_stride_b, key_stride_t, score, score_stride_b,
+                                            score_stride_t, ape, slot_mapping, positions,
+                                            num_requests, next_n, kv_cache, nullptr, num_pages,
+                                            true, round_scale != 0, (hipStream_t)stream),
+                    "kvc_compress_decode_ring_paged launch");
 }
 
 int kvc_seed_tail_ring(uint16_t* tail_ring, int64_t num_ring_blocks, const uint16_t* key,

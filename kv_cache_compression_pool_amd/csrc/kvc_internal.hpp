@@ -10,18 +10,23 @@
 
 namespace kvc {
 
+// out_fp8 / out_scale: packed [out_rows,128] codes and [out_rows] scales, or
+// (paged) out_fp8 is a [out_rows, 132] byte cache and out_scale is unused.
+// loc (optional) maps pool p to its output row; write_mask (optional) skips
+// pools whose byte is 0.
 hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const uint16_t* scores,
                                  int64_t score_stride, int64_t num_rows, const float* ape,
                                  const int32_t* src_rows, int64_t n_pools, uint8_t* out_fp8,
-                                 float* out_scale, bool round_scale, float* dbg,
-                                 hipStream_t stream);
+                                 float* out_scale, int64_t out_rows, bool paged,
+                                 const int64_t* loc, const uint8_t* write_mask, bool round_scale,
+                                 float* dbg, hipStream_t stream);
 
 hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot,
                               const uint16_t* key, int64_t key_sb, int64_t key_st,
                               const uint16_t* score, int64_t score_sb, int64_t score_st,
                               const float* ape, const int32_t* slot_mapping,
                               const int32_t* positions, int64_t num_requests, int next_n,
-                              uint8_t* out_fp8, float* out_scale, int64_t num_out,
+                              uint8_t* out_fp8, float* out_scale, int64_t out_rows, bool paged,
                               bool round_scale, hipStream_t stream);
 
 hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t* key,

@@ -35,6 +35,7 @@ constexpr int kHalf = 8;                       // slots per 16-lane row
 constexpr int kPoolsPerBlock = 8;              // 32 lanes per pool
 constexpr int kBlock = kPoolsPerBlock * 32;    // 256 threads = 4 waves
 constexpr int kMinWavesPerEU = 4;              // caps VGPRs at 128
+constexpr int64_t kPagedBytes = 132;           // page of one token: 128 codes + fp32 scale
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -138,21 +139,48 @@ __device__ __forceinline__ uint32_t pool_epilogue(const float (&x)[8], int c, in
   return pack_e4m3x4(q[0], q[1], q[2], q[3]);
 }
 
+// Where a compressed vector goes.  Packed: codes row `row` of a [n,128]
+// array and scales[row].  Paged (page size 1): page `row` of a [pages, 132]
+// byte cache holding the 128 codes followed by the fp32 scale.
+struct OutSink {
+  uint8_t* codes;      // packed codes or the paged cache
+  float* scales;       // packed scales (unused when paged)
+  int64_t rows;        // rows / pages available
+  bool paged;
+  __device__ __forceinline__ void store(int64_t row, int c, int h, uint32_t code4,
+                                        float scale) const {
+    if (paged) {
+      uint8_t* page = codes + row * kPagedBytes;
+      reinterpret_cast<uint32_t*>(page)[2 * c + h] = code4;
+      if (c == 0 && h == 0) *reinterpret_cast<float*>(page + 128) = scale;
+    } else {
+      reinterpret_cast<uint32_t*>(codes + row * 128)[2 * c + h] = code4;
+      if (c == 0 && h == 0) scales[row] = scale;
+    }
+  }
+};
+
 template <bool kRoundScale, bool kDbg>
 __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
     const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
     int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
-    const int32_t* __restrict__ src_rows, int64_t n_pools, uint8_t* __restrict__ out_fp8,
-    float* __restrict__ out_scale, float* __restrict__ dbg) {
+    const int32_t* __restrict__ src_rows, int64_t n_pools, OutSink sink,
+    const int64_t* __restrict__ loc, const uint8_t* __restrict__ write_mask,
+    float* __restrict__ dbg) {
   __shared__ float4 s_ape[kPool * 32];
   const int c = threadIdx.x & 15;
   const int h = (threadIdx.x >> 4) & 1;
   const int64_t pool = (int64_t)blockIdx.x * kPoolsPerBlock + (threadIdx.x >> 5);
-  int64_t r0 = -1;
-  if (pool < n_pools) r0 = src_rows ? (int64_t)src_rows[pool] : pool * kPool;
+  int64_t r0 = -1, dst = pool;
+  bool ok = pool < n_pools;
+  if (ok) {
+    r0 = src_rows ? (int64_t)src_rows[pool] : pool * kPool;
+    if (loc) dst = loc[pool];
+    if (write_mask && !write_mask[pool]) ok = false;
+  }
   // Both rows of a pool take the same decision, so DPP / swizzle partners
   // are always active.
-  const bool ok = pool < n_pools && r0 >= 0 && r0 + kPool <= num_rows;
+  ok = ok && r0 >= 0 && r0 + kPool <= num_rows && dst >= 0 && dst < sink.rows;
 
   uint4 S[kHalf], K[kHalf];
   if (ok) {
@@ -176,8 +204,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   }
   float scale;
   const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
-  reinterpret_cast<uint32_t*>(out_fp8 + pool * 128)[2 * c + h] = codes;
-  if (c == 0 && h == 0) out_scale[pool] = scale;
+  sink.store(dst, c, h, codes, scale);
 }
 
 // Tail-ring decode: 32 lanes per request (row h owns ring slots 8h..8h+7),
@@ -190,8 +217,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
     const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
     const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
     const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
-    const int32_t* __restrict__ positions, int64_t num_requests, int next_n,
-    uint8_t* __restrict__ out_fp8, float* __restrict__ out_scale, int64_t num_out) {
+    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink) {
   __shared__ float4 s_ape[kPool * 32];
   stage_ape(s_ape, ape);
 
@@ -234,10 +260,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
       pool_mean(S, K, s_ape, c, h, x);
       float scale;
       const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
-      if (loc < num_out) {
-        reinterpret_cast<uint32_t*>(out_fp8 + (int64_t)loc * 128)[2 * c + h] = codes;
-        if (c == 0 && h == 0) out_scale[loc] = scale;
-      }
+      if (loc < sink.rows) sink.store(loc, c, h, codes, scale);
     }
     const int slot = pos & (kPool - 1);
     if (stash && (slot >> 3) == h) {
@@ -295,14 +318,16 @@ __global__ __launch_bounds__(256) void diag_convert_kernel(const float* __restri
 hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const uint16_t* scores,
                                  int64_t score_stride, int64_t num_rows, const float* ape,
                                  const int32_t* src_rows, int64_t n_pools, uint8_t* out_fp8,
-                                 float* out_scale, bool round_scale, float* dbg,
-                                 hipStream_t stream) {
+                                 float* out_scale, int64_t out_rows, bool paged,
+                                 const int64_t* loc, const uint8_t* write_mask, bool round_scale,
+                                 float* dbg, hipStream_t stream) {
   const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
+  const OutSink sink{out_fp8, out_scale, out_rows, paged};
 #define KVC_LAUNCH(RS, DBG)                                                                   \
   hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG>), grid, block, 0, stream, keys,          \
                      key_stride, scores, score_stride, num_rows, ape, src_rows, n_pools,     \
-                     out_fp8, out_scale, dbg)
+                     sink, loc, write_mask, dbg)
   if (round_scale) {
     if (dbg) KVC_LAUNCH(true, true); else KVC_LAUNCH(true, false);
   } else {
@@ -317,20 +342,19 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                               const uint16_t* score, int64_t score_sb, int64_t score_st,
                               const float* ape, const int32_t* slot_mapping,
                               const int32_t* positions, int64_t num_requests, int next_n,
-                              uint8_t* out_fp8, float* out_scale, int64_t num_out,
+                              uint8_t* out_fp8, float* out_scale, int64_t out_rows, bool paged,
                               bool round_scale, hipStream_t stream) {
   const dim3 grid((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
+  const OutSink sink{out_fp8, out_scale, out_rows, paged};
   if (round_scale)
     hipLaunchKernelGGL((pool16_ring_kernel<true>), grid, block, 0, stream, ring, num_blocks,
                        tail_slot, key, key_sb, key_st, score, score_sb, score_st, ape,
-                       slot_mapping, positions, num_requests, next_n, out_fp8, out_scale,
-                       num_out);
+                       slot_mapping, positions, num_requests, next_n, sink);
   else
     hipLaunchKernelGGL((pool16_ring_kernel<false>), grid, block, 0, stream, ring, num_blocks,
                        tail_slot, key, key_sb, key_st, score, score_sb, score_st, ape,
-                       slot_mapping, positions, num_requests, next_n, out_fp8, out_scale,
-                       num_out);
+                       slot_mapping, positions, num_requests, next_n, sink);
   return hipGetLastError();
 }
 

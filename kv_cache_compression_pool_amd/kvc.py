@@ -28,7 +28,8 @@ PLAN_DTYPE = np.dtype([("ragged_id", "<u4"), ("batch_id", "<u4"), ("position", "
 PLAN_SENTINEL = 0xFFFFFFFF
 
 EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_plan_prefill",
-           "kvc_compress_prefill", "kvc_compress_decode_ring", "kvc_seed_tail_ring",
+           "kvc_compress_prefill", "kvc_compress_prefill_paged", "kvc_compress_decode_ring",
+           "kvc_compress_decode_ring_paged", "kvc_seed_tail_ring",
            "kvc_c128_online_decode", "kvc_c128_online_prefill", "kvc_diag_convert")
 
 
@@ -60,6 +61,11 @@ def lib() -> ctypes.CDLL:
                                            _i32, _p, _p]
         L.kvc_compress_decode_ring.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p,
                                                _p, _p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p]
+        L.kvc_compress_prefill_paged.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i32, _p, _i64,
+                                                 _p, _i64, _i32, _p, _p, _i32, _p]
+        L.kvc_compress_decode_ring_paged.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64,
+                                                     _p, _p, _p, _i64, _i32, _i32, _p, _i64, _i32,
+                                                     _i32, _p]
         L.kvc_seed_tail_ring.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32, _p]
         L.kvc_c128_online_decode.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]
         L.kvc_c128_online_prefill.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _p, _u32,
@@ -171,6 +177,68 @@ def kvc_compress_prefill(keys, scores, ape, pool_src_row, n_pools: int, out_fp8,
         _dptr(pool_src_row, torch.int32, "pool_src_row", optional=True), int(n_pools),
         _dptr(out_fp8, torch.uint8, "out_fp8"), _dptr(out_scale, torch.float32, "out_scale"),
         int(round_scale), _dptr(dbg_pooled, torch.float32, "dbg_pooled", optional=True),
+        _stream(stream)))
+
+
+def kvc_compress_prefill_paged(keys, scores, ape, pool_src_row, n_pools: int, kv_cache, loc,
+                               round_scale: bool, write_mask=None, pool_size: int = 16,
+                               stream=None):
+    """As kvc_compress_prefill, writing into a page-size-1 cache: kv_cache
+    uint8 [pages, 132] (or [pages, 1, 132]); loc int64 [n_pools]; write_mask
+    bool/uint8 [n_pools] or None."""
+    import torch
+    k = _bf16_view(keys, "keys")
+    s = _bf16_view(scores, "scores")
+    n_pools = int(n_pools)
+    _need(k.shape[0] == s.shape[0], "keys and scores must have the same number of rows")
+    _shape_ok(ape, (pool_size, 128), "ape")
+    _need(kv_cache.is_contiguous() and kv_cache.shape[-1] == 132 and kv_cache.numel() %
+          132 == 0, "kv_cache must be a contiguous [pages, 132] uint8 tensor")
+    _need(loc.dim() == 1 and loc.shape[0] >= n_pools and loc.is_contiguous(),
+          "loc must hold n_pools entries")
+    if pool_src_row is not None:
+        _need(pool_src_row.dim() == 1 and pool_src_row.shape[0] >= n_pools
+              and pool_src_row.is_contiguous(), "pool_src_row must hold n_pools entries")
+    wm = None
+    if write_mask is not None:
+        _need(write_mask.dim() == 1 and write_mask.shape[0] >= n_pools and write_mask.is_cuda
+              and write_mask.element_size() == 1 and write_mask.is_contiguous(),
+              "write_mask must be a contiguous 1-byte device tensor of n_pools entries")
+        wm = write_mask.data_ptr()
+    _check(lib().kvc_compress_prefill_paged(
+        k.data_ptr(), k.stride(0), s.data_ptr(), s.stride(0), k.shape[0],
+        _dptr(ape, torch.float32, "ape"), pool_size,
+        _dptr(pool_src_row, torch.int32, "pool_src_row", optional=True), n_pools,
+        _dptr(kv_cache, torch.uint8, "kv_cache"), kv_cache.numel() // 132, 1,
+        _dptr(loc, torch.int64, "loc"), wm, int(round_scale), _stream(stream)))
+
+
+def kvc_compress_decode_ring_paged(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,
+                                   positions, kv_cache, round_scale: bool, pool_size: int = 16,
+                                   stream=None):
+    """As kvc_compress_decode_ring, completions written into a page-size-1
+    cache (kv_cache uint8 [pages, 132]) at page slot_mapping[r, t]."""
+    import torch
+    ring = _bf16_view(tail_ring, "tail_ring", min_last=None)
+    k = _bf16_view(key, "key", min_last=None)
+    s = _bf16_view(score, "score", min_last=None)
+    R, N = k.shape[0], k.shape[1]
+    for name, t in (("tail_slot_mapping", tail_slot_mapping), ("slot_mapping", slot_mapping),
+                    ("positions", positions)):
+        _shape_ok(t, (R, N), name)
+    _need(ring.is_contiguous() and tuple(ring.shape[1:]) == (2, pool_size, 128),
+          f"tail_ring must be a contiguous [nb, 2, {pool_size}, 128] tensor")
+    _need(k.dim() == 3 and k.shape[2] == 128 and tuple(s.shape) == tuple(k.shape),
+          "key and score must be [R, next_n, 128]")
+    _shape_ok(ape, (pool_size, 128), "ape")
+    _need(kv_cache.is_contiguous() and kv_cache.shape[-1] == 132 and kv_cache.numel() %
+          132 == 0, "kv_cache must be a contiguous [pages, 132] uint8 tensor")
+    _check(lib().kvc_compress_decode_ring_paged(
+        ring.data_ptr(), ring.shape[0], _dptr(tail_slot_mapping, torch.int32, "tail_slot_mapping"),
+        k.data_ptr(), k.stride(0), k.stride(1), s.data_ptr(), s.stride(0), s.stride(1),
+        _dptr(ape, torch.float32, "ape"), _dptr(slot_mapping, torch.int32, "slot_mapping"),
+        _dptr(positions, torch.int32, "positions"), R, N, pool_size,
+        _dptr(kv_cache, torch.uint8, "kv_cache"), kv_cache.numel() // 132, 1, int(round_scale),
         _stream(stream)))
 
 

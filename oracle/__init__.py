@@ -80,6 +80,10 @@ def _declare(L):
     L.orc_ring_decode.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _p,
                                   _i64, _i32, _i32, _i32, _p, _p, _i64, _p, _p]
     L.orc_seed_tail_ring.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i32]
+    L.orc_compress_prefill_paged.argtypes = [_p, _i64, _p, _i64, _p, _p, _i64, _i32, _i32, _p,
+                                             _i64, _p, _p]
+    L.orc_ring_decode_paged.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p, _p, _p,
+                                        _i64, _i32, _i32, _i32, _p, _i64]
     L.orc_c128_decode.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _i64]
     L.orc_c128_plan.argtypes = [_p, _p, _i64, _i64, _p, _p, _i32, _p, _p]
     L.orc_c128_plan.restype = _i32
@@ -234,6 +238,39 @@ def ring_decode(ring, tail_slot_mapping, key, score, ape, slot_mapping, position
                           _ptr(pools_out[0]) if pools_out else None,
                           _ptr(pools_out[1]) if pools_out else None)
     return out_code, out_scale
+
+
+def compress_prefill_paged(keys_bf16, scores_bf16, ape, pool_src_row, round_scale: bool,
+                           cache, loc, write_mask=None, pool_size: int = 16):
+    """Pool-16 prefill into a page-size-1 cache ([pages,132] uint8, updated in
+    place): codes at bytes 0..127 of page loc[p], fp32 scale at 128..131."""
+    k = _c(keys_bf16, np.uint16)
+    s = _c(scores_bf16, np.uint16)
+    assert cache.dtype == np.uint8 and cache.flags["C_CONTIGUOUS"] and cache.shape[1] == 132
+    lc = _c(loc, np.int64)
+    rows = None if pool_src_row is None else _c(pool_src_row, np.int32)
+    n = lc.size
+    wm = None if write_mask is None else _c(write_mask, np.uint8)
+    lib().orc_compress_prefill_paged(_ptr(k), k.shape[1], _ptr(s), s.shape[1],
+                                     _ptr(_c(ape, np.float32)), _ptr(rows), n, pool_size,
+                                     int(round_scale), _ptr(cache), cache.shape[0], _ptr(lc),
+                                     _ptr(wm))
+    return cache
+
+
+def ring_decode_paged(ring, tail_slot_mapping, key, score, ape, slot_mapping, positions,
+                      cache, round_scale: bool, pool_size: int = 16):
+    """Ring decode writing completions into a page-size-1 cache."""
+    assert ring.dtype == np.uint16 and ring.flags["C_CONTIGUOUS"]
+    assert cache.dtype == np.uint8 and cache.flags["C_CONTIGUOUS"] and cache.shape[1] == 132
+    R, nn = key.shape[0], key.shape[1]
+    lib().orc_ring_decode_paged(_ptr(ring), ring.shape[0], _ptr(_c(tail_slot_mapping, np.int32)),
+                                _ptr(_c(key, np.uint16)), nn * 128, 128,
+                                _ptr(_c(score, np.uint16)), nn * 128, 128,
+                                _ptr(_c(ape, np.float32)), _ptr(_c(slot_mapping, np.int32)),
+                                _ptr(_c(positions, np.int32)), R, nn, pool_size,
+                                int(round_scale), _ptr(cache), cache.shape[0])
+    return cache
 
 
 def seed_tail_ring(ring, key, score, tslot, pool_size: int = 16):

@@ -240,6 +240,35 @@ void orc_compress_prefill(const uint16_t* keys, int64_t key_stride,
     }
 }
 
+/* Paged output ([KP] softmax kernel, cache-write branch, page size 1): the
+ * cache is [num_pages][132] bytes per token page, the 128 e4m3 codes at
+ * offset 0 and the fp32 scale at byte offset 128 (the page's scale region
+ * starts after page_size*head_dim code bytes).  Pool p goes to page loc[p];
+ * pools whose write_mask byte is 0, or whose page is out of range, are not
+ * written. */
+static void put_paged(uint8_t* cache, int64_t page, const uint8_t* code, float scale) {
+    memcpy(cache + page * 132, code, 128);
+    memcpy(cache + page * 132 + 128, &scale, 4);
+}
+
+void orc_compress_prefill_paged(const uint16_t* keys, int64_t key_stride,
+                                const uint16_t* scores, int64_t score_stride,
+                                const float* ape, const int32_t* pool_src_row, int64_t n_pools,
+                                int P, int round_scale, uint8_t* cache, int64_t num_pages,
+                                const int64_t* loc, const uint8_t* write_mask) {
+    for (int64_t p = 0; p < n_pools; ++p) {
+        if (write_mask && !write_mask[p]) continue;
+        int64_t dst = loc[p];
+        if (dst < 0 || dst >= num_pages) continue;
+        int64_t r0 = pool_src_row ? (int64_t)pool_src_row[p] : p * P;
+        uint8_t code[128];
+        float scale;
+        orc_pool_compress(keys + r0 * key_stride, key_stride, scores + r0 * score_stride,
+                          score_stride, ape, P, round_scale, code, &scale, NULL, NULL);
+        put_paged(cache, dst, code, scale);
+    }
+}
+
 /* Pool plan for ragged prefill (the packing the configs describe): sequence
  * b holds seq_lens[b] consecutive rows; its complete pools j are at rows
  * start_b + j*P; tokens after the last complete pool are not compressed.
@@ -274,13 +303,14 @@ int64_t orc_pool_plan(const int64_t* seq_lens, int64_t batch, int P,
  * a completion sees the stashes of earlier tokens of the same request.
  * pool_keys_out / pool_scores_out (nullable, [num_out][P][128]) receive the
  * gathered pool of every completion written to row loc. */
-void orc_ring_decode(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot_mapping,
-                     const uint16_t* key, int64_t key_sb, int64_t key_st,
-                     const uint16_t* score, int64_t score_sb, int64_t score_st,
-                     const float* ape, const int32_t* slot_mapping, const int32_t* positions,
-                     int64_t num_requests, int next_n, int P, int round_scale,
-                     uint8_t* out_code, float* out_scale, int64_t num_out,
-                     uint16_t* pool_keys_out, uint16_t* pool_scores_out) {
+static void ring_decode_impl(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot_mapping,
+                             const uint16_t* key, int64_t key_sb, int64_t key_st,
+                             const uint16_t* score, int64_t score_sb, int64_t score_st,
+                             const float* ape, const int32_t* slot_mapping,
+                             const int32_t* positions, int64_t num_requests, int next_n, int P,
+                             int round_scale, uint8_t* out_code, float* out_scale,
+                             int64_t num_out, uint16_t* pool_keys_out, uint16_t* pool_scores_out,
+                             uint8_t* paged_cache) {
     uint16_t pk[128 * 128], ps[128 * 128];          /* gathered pool, P <= 128 */
     for (int64_t r = 0; r < num_requests; ++r) {
         for (int t = 0; t < next_n; ++t) {
@@ -299,7 +329,13 @@ void orc_ring_decode(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slo
                     memcpy(pk + i * 128, srck, 256);
                     memcpy(ps + i * 128, srcs, 256);
                 }
-                if (loc < num_out) {
+                if (loc < num_out && paged_cache) {
+                    uint8_t code[128];
+                    float scale;
+                    orc_pool_compress(pk, 128, ps, 128, ape, P, round_scale, code, &scale,
+                                      NULL, NULL);
+                    put_paged(paged_cache, loc, code, scale);
+                } else if (loc < num_out) {
                     orc_pool_compress(pk, 128, ps, 128, ape, P, round_scale,
                                       out_code + (int64_t)loc * 128, out_scale + loc, NULL, NULL);
                     /* optional copy of the gathered pool, for diagnostics */
@@ -314,6 +350,31 @@ void orc_ring_decode(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slo
             }
         }
     }
+}
+
+void orc_ring_decode(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot_mapping,
+                     const uint16_t* key, int64_t key_sb, int64_t key_st,
+                     const uint16_t* score, int64_t score_sb, int64_t score_st,
+                     const float* ape, const int32_t* slot_mapping, const int32_t* positions,
+                     int64_t num_requests, int next_n, int P, int round_scale,
+                     uint8_t* out_code, float* out_scale, int64_t num_out,
+                     uint16_t* pool_keys_out, uint16_t* pool_scores_out) {
+    ring_decode_impl(ring, num_blocks, tail_slot_mapping, key, key_sb, key_st, score, score_sb,
+                     score_st, ape, slot_mapping, positions, num_requests, next_n, P, round_scale,
+                     out_code, out_scale, num_out, pool_keys_out, pool_scores_out, NULL);
+}
+
+/* Ring decode writing completions into a page-size-1 cache (see put_paged);
+ * slot_mapping holds the page of each completion. */
+void orc_ring_decode_paged(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot_mapping,
+                           const uint16_t* key, int64_t key_sb, int64_t key_st,
+                           const uint16_t* score, int64_t score_sb, int64_t score_st,
+                           const float* ape, const int32_t* slot_mapping,
+                           const int32_t* positions, int64_t num_requests, int next_n, int P,
+                           int round_scale, uint8_t* cache, int64_t num_pages) {
+    ring_decode_impl(ring, num_blocks, tail_slot_mapping, key, key_sb, key_st, score, score_sb,
+                     score_st, ape, slot_mapping, positions, num_requests, next_n, P, round_scale,
+                     NULL, NULL, num_pages, NULL, NULL, cache);
 }
 
 /* Tail-ring seeding from a prefill batch ([KP] _kpool_tail_seed_kernel).

@@ -469,3 +469,64 @@ def test_seed_then_decode_continues_the_sequence():
             check_scales(gs[l:l + 1], ref_s, True, "seeded ring")
             checked += 1
     assert checked >= 16
+
+
+# ------------------------------------------------------------------ paged cache output
+def _paged_expect(codes, scales, loc, mask, pages, fill):
+    cache = np.full((pages, 132), fill, np.uint8)
+    for p in range(loc.size):
+        if (mask is None or mask[p]) and 0 <= loc[p] < pages:
+            cache[loc[p], :128] = codes[p]
+            cache[loc[p], 128:] = np.frombuffer(np.float32(scales[p]).tobytes(), np.uint8)
+    return cache
+
+
+@pytest.mark.parametrize("round_scale,masked", [(True, True), (False, False)])
+def test_paged_prefill_matches_packed_and_oracle(round_scale, masked):
+    d = synth.pool16_ragged(seed=12, num_seqs=9, max_len=900)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    n = rows.size
+    g = np.random.default_rng(13)
+    pages = n + 37
+    loc = g.permutation(pages)[:n].astype(np.int64)
+    loc[1] = -5                                          # skipped: outside the cache
+    mask = (g.random(n) < 0.75).astype(np.uint8) if masked else None
+    note(f"paged prefill: {n} pools into {pages} pages, masked={masked}")
+    # packed device result (already held to the oracle by the prefill tests)
+    gc, gs, gx = run_prefill_gpu(d["keys"], d["scores"], d["ape"], rows, n, round_scale)
+    rc, rs, rx = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
+    ref_c, ref_s, _ = reference_for(gx[:n], rx, rc, rs, round_scale, "paged prefill")
+    check_codes(gc[:n], ref_c, "paged prefill")
+    check_scales(gs[:n], ref_s, round_scale, "paged prefill")
+    cache = torch.full((pages, 132), 0xA5, dtype=torch.uint8, device="cuda")
+    kvc.kvc_compress_prefill_paged(dev(d["keys"], torch.int16), dev(d["scores"], torch.int16),
+                                   dev(d["ape"]), dev(rows), n, cache, dev(loc), round_scale,
+                                   write_mask=None if mask is None else dev(mask))
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    assert np.array_equal(got, _paged_expect(gc[:n], gs[:n], loc, mask, pages, 0xA5))
+    # layout and skip rules agree with the oracle's paged writer
+    oc = np.full((pages, 132), 0xA5, np.uint8)
+    oracle.compress_prefill_paged(d["keys"], d["scores"], d["ape"], rows, round_scale, oc, loc,
+                                  mask)
+    assert np.array_equal(np.all(got == 0xA5, axis=1), np.all(oc == 0xA5, axis=1))
+
+
+def test_paged_ring_decode_matches_packed():
+    d = synth.pool16_ring(seed=14, num_requests=64, next_n=6, pad_frac=0.05)
+    note("paged ring decode 64x6")
+    gring, gc, gsc, ring, ref_c, ref_s = run_ring(d)
+    assert np.array_equal(gring, ring)
+    check_codes(gc, ref_c, "ring codes")
+    check_scales(gsc, ref_s, True, "ring scales")
+    pring = dev(d["ring"], torch.int16)
+    cache = torch.full((d["num_out"], 132), 0x5A, dtype=torch.uint8, device="cuda")
+    kvc.kvc_compress_decode_ring_paged(pring, dev(d["tail_slot_mapping"]),
+                                       dev(d["key"], torch.int16), dev(d["score"], torch.int16),
+                                       dev(d["ape"]), dev(d["slot_mapping"]), dev(d["positions"]),
+                                       cache, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(pring.cpu().numpy().view(np.uint16), ring)
+    written = ref_s != 5.0
+    exp = _paged_expect(gc, gsc, np.arange(d["num_out"]), written, d["num_out"], 0x5A)
+    assert np.array_equal(cache.cpu().numpy(), exp)

@@ -347,3 +347,46 @@ def test_seed_tail_ring_skips_blocks_beyond_the_ring():
     ring = d["ring"][:3].copy()            # requests 3 and 4 have no block
     oracle.seed_tail_ring(ring, d["key"], d["score"], d["tslot"])
     assert np.array_equal(ring, _seed_bruteforce(d["ring"], d)[:3])
+
+
+# ------------------------------------------------------------------ paged cache layout
+def _paged_from_packed(codes, scales, loc, mask, pages, fill=0xA5):
+    cache = np.full((pages, 132), fill, np.uint8)
+    for p in range(loc.size):
+        if mask is not None and not mask[p]:
+            continue
+        if 0 <= loc[p] < pages:
+            cache[loc[p], :128] = codes[p]
+            cache[loc[p], 128:] = np.frombuffer(np.float32(scales[p]).tobytes(), np.uint8)
+    return cache
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_paged_prefill_equals_packed_scattered(round_scale):
+    d = synth.pool16_ragged(seed=8, num_seqs=5, max_len=400)
+    rows = oracle.pool_plan(d["seq_lens"])
+    g = np.random.default_rng(9)
+    pages = rows.size + 10
+    loc = g.permutation(pages)[:rows.size].astype(np.int64)
+    loc[3] = pages + 4                                   # out of range: not written
+    mask = (g.random(rows.size) < 0.7).astype(np.uint8)
+    codes, scales, _ = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
+    cache = np.full((pages, 132), 0xA5, np.uint8)
+    oracle.compress_prefill_paged(d["keys"], d["scores"], d["ape"], rows, round_scale, cache, loc,
+                                  mask)
+    assert np.array_equal(cache, _paged_from_packed(codes, scales, loc, mask, pages))
+
+
+def test_paged_ring_decode_equals_packed_scattered():
+    d = synth.pool16_ring(seed=11, num_requests=40, next_n=6, pad_frac=0.1)
+    ring_a, ring_b = d["ring"].copy(), d["ring"].copy()
+    args = (d["tail_slot_mapping"], d["key"], d["score"], d["ape"], d["slot_mapping"],
+            d["positions"])
+    codes, scales = oracle.ring_decode(ring_a, *args, 40, True)
+    cache = np.full((40, 132), 0xA5, np.uint8)
+    oracle.ring_decode_paged(ring_b, *args, cache, True)
+    written = np.unique(d["slot_mapping"][(d["slot_mapping"] >= 0) & (d["positions"] >= 0)])
+    mask = np.zeros(40, bool)
+    mask[written] = True
+    assert np.array_equal(cache, _paged_from_packed(codes, scales, np.arange(40), mask, 40))
+    assert np.array_equal(ring_a, ring_b)
