@@ -179,8 +179,30 @@ def bench_c128_decode(args, torch, kvc, synth, stream):
 
     steps = max(args.steps, 50)
     total_ms, ev_ms, host = timed(step, steps, max(args.warmup, 5), torch, stream)
-    return dict(batch=B, emitted=int((c == 127).sum()), replicas=R, total_ms=total_ms,
-                steps=steps, ev_ms=ev_ms, host_s=host, alg_bytes=alg)
+    res = dict(batch=B, emitted=int((c == 127).sum()), replicas=R, total_ms=total_ms,
+               steps=steps, ev_ms=ev_ms, host_s=host, alg_bytes=alg)
+    del states, ins, outs
+
+    # Multi-layer form: the same 1024 requests decode one token in each of
+    # `layers` layers (own state, input, output and ape per layer) in one launch.
+    layers = args.decode_layers
+    if layers:
+        per_layer = alg
+        RL = 2
+        st_l = [state0.unsqueeze(0).repeat(layers, 1, 1) for _ in range(RL)]
+        in_l = [to_dev(torch, d["kv_score_in"]).unsqueeze(0).repeat(layers, 1, 1) for _ in range(RL)]
+        out_l = [torch.empty((layers, B, 128), device="cuda") for _ in range(RL)]
+        ape_l = ape.unsqueeze(0).repeat(layers, 1, 1).contiguous()
+
+        def step_l(i):
+            r = i % RL
+            kvc.kvc_c128_online_decode_layers(st_l[r], in_l[r], out_l[r], ape_l, idx, sl_t)
+
+        tl, evl, hl = timed(step_l, max(args.steps // 4, 20), 3, torch, stream)
+        res["layers"] = dict(layers=layers, total_ms=tl, ev_ms=evl,
+                             steps=max(args.steps // 4, 20),
+                             alg_bytes=per_layer * layers)
+    return res
 
 
 # ------------------------------------------------------------------ pool-128 prefill
@@ -292,6 +314,8 @@ def main():
     ap.add_argument("--only", choices=["prefill", "all"], default="all",
                     help="prefill: the headline kernel only (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-layers", type=int, default=64,
+                    help="layers in the multi-layer c128 decode measurement (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -357,6 +381,14 @@ def main():
             "launch_us": round(c4["ev_ms"] * 1e3, 3), "bytes_per_launch": c4["alg_bytes"],
             "hbm_gbs": round(g4, 1), "hbm_frac": round(g4 / PEAK_HBM_GBS, 4),
             "state_replicas": c4["replicas"]}
+        if "layers" in c4:
+            cl = c4["layers"]
+            gl = gbs(cl["alg_bytes"], cl["ev_ms"])
+            line["c128_decode"]["multi_layer"] = {
+                "layers": cl["layers"], "launch_us": round(cl["ev_ms"] * 1e3, 3),
+                "token_updates_per_s": round(c4["batch"] * cl["layers"] / (cl["ev_ms"] * 1e-3), 1),
+                "bytes_per_launch": cl["alg_bytes"], "hbm_gbs": round(gl, 1),
+                "hbm_frac": round(gl / PEAK_HBM_GBS, 4)}
         log("pool-128 online prefill")
         c5 = bench_c128_prefill(args, torch, kvc, synth, stream)
         g5 = gbs(c5["alg_bytes"], c5["ev_ms"])

@@ -248,6 +248,32 @@ int kvc_c128_online_decode(float* state, int64_t num_slots, const float* kv_scor
                            float* out, const float* ape, const int32_t* indices,
                            const int32_t* seq_lens, int64_t batch, void* stream);
 
+/* Multi-layer form of kvc_c128_online_decode: the same requests (indices,
+ * seq_lens) decode one token in each of num_layers layers in one launch.
+ * Layer l uses state + l*state_layer_stride, kv_score_in + l*in_layer_stride,
+ * out + l*out_layer_stride and ape + l*ape_layer_stride (strides in floats,
+ * multiples of 4, each covering a whole layer when num_layers > 1).  Each
+ * layer behaves exactly as a separate kvc_c128_online_decode call.
+ * Errors: as kvc_c128_online_decode; KVC_ERR_SHAPE for num_layers > 65535 or
+ *         strides that overlap layers. */
+int kvc_c128_online_decode_layers(float* state, int64_t state_layer_stride, int64_t num_slots,
+                                  const float* kv_score_in, int64_t in_layer_stride, float* out,
+                                  int64_t out_layer_stride, const float* ape,
+                                  int64_t ape_layer_stride, const int32_t* indices,
+                                  const int32_t* seq_lens, int64_t batch, int64_t num_layers,
+                                  void* stream);
+
+/* kvc_c128_online_decode with the pool-16 epilogue applied to every emitted
+ * vector: bf16 round, 128-point Walsh-Hadamard / sqrt(128), bf16 round,
+ * e4m3 with one scale per vector (max(absmax, 1e-4) * fp32(1/448), rounded
+ * up to a power of two when round_scale).  out_fp8 device uint8 [batch, 128],
+ * out_scale device fp32 [batch]; only emitting rows are written.  The state
+ * update is identical to kvc_c128_online_decode. */
+int kvc_c128_online_decode_quant(float* state, int64_t num_slots, const float* kv_score_in,
+                                 uint8_t* out_fp8, float* out_scale, const float* ape,
+                                 const int32_t* indices, const int32_t* seq_lens, int64_t batch,
+                                 int round_scale, void* stream);
+
 /* Pool-128 online ragged prefill (c128_online.cuh page,
  * flash_c128_online_prefill and run_prefill).  Two launches in stream order:
  *   1. every compress plan: the segment's softmax state, merged with state
@@ -273,6 +299,19 @@ int kvc_c128_online_prefill(float* state, int64_t num_slots, const float* kv_sco
                             const int32_t* indices, const int32_t* load_indices, int64_t batch,
                             const kvc_online_plan* compress_plan, uint32_t n_compress,
                             const kvc_online_plan* write_plan, uint32_t n_write, void* stream);
+
+/* kvc_c128_online_prefill with the rotate/quantise epilogue (as in
+ * kvc_c128_online_decode_quant) on every chunk-closing vector: out_fp8
+ * device uint8 [num_tokens, 128] and out_scale device fp32 [num_tokens],
+ * written at row ragged_id of each compress plan.  State handling is
+ * identical to kvc_c128_online_prefill. */
+int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* kv_score_in,
+                                  uint8_t* out_fp8, float* out_scale, int64_t num_tokens,
+                                  const float* ape, const int32_t* indices,
+                                  const int32_t* load_indices, int64_t batch,
+                                  const kvc_online_plan* compress_plan, uint32_t n_compress,
+                                  const kvc_online_plan* write_plan, uint32_t n_write,
+                                  int round_scale, void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostics.

@@ -312,20 +312,86 @@ int kvc_seed_tail_ring(uint16_t* tail_ring, int64_t num_ring_blocks, const uint1
 }
 
 // --------------------------------------------------------------- pool-128
+namespace {
+
+int check_decode(const char* fn, float* state, int64_t num_slots, const float* kv_score_in,
+                 const float* ape, const int32_t* indices, const int32_t* seq_lens,
+                 int64_t batch) {
+  if (!state || !kv_score_in || !ape || !indices || !seq_lens)
+    return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (!aligned(state, 16) || !aligned(kv_score_in, 16) || !aligned(ape, 16))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  if (batch > kMaxI32 || num_slots > kMaxI32) return fail(KVC_ERR_SHAPE, "%s: sizes exceed 2^31-1", fn);
+  return KVC_OK;
+}
+
+int check_prefill(const char* fn, float* state, int64_t num_slots, const float* kv_score_in,
+                  int64_t num_tokens, const float* ape, const int32_t* indices, int64_t batch,
+                  const kvc_online_plan* compress_plan, uint32_t n_compress,
+                  const kvc_online_plan* write_plan, uint32_t n_write) {
+  if (!state || !kv_score_in || !ape || !indices || (n_compress && !compress_plan) ||
+      (n_write && !write_plan))
+    return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (!aligned(state, 16) || !aligned(kv_score_in, 16) || !aligned(ape, 16) ||
+      (compress_plan && !aligned(compress_plan, 16)) || (write_plan && !aligned(write_plan, 16)))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  if (num_tokens > (int64_t)0xfffffffeLL || num_slots > kMaxI32 || batch > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "%s: sizes out of range", fn);
+  return KVC_OK;
+}
+
+}  // namespace
+
 int kvc_c128_online_decode(float* state, int64_t num_slots, const float* kv_score_in, float* out,
                            const float* ape, const int32_t* indices, const int32_t* seq_lens,
                            int64_t batch, void* stream) {
-  if (batch < 0 || num_slots < 0) return fail(KVC_ERR_SHAPE, "kvc_c128_online_decode: negative size");
-  if (batch == 0) return ok();
-  if (!state || !kv_score_in || !out || !ape || !indices || !seq_lens)
-    return fail(KVC_ERR_NULL, "kvc_c128_online_decode: NULL pointer");
-  if (!aligned(state, 16) || !aligned(kv_score_in, 16) || !aligned(out, 16) || !aligned(ape, 16))
-    return fail(KVC_ERR_SHAPE, "kvc_c128_online_decode: misaligned pointer");
-  if (batch > kMaxI32 || num_slots > kMaxI32)
-    return fail(KVC_ERR_SHAPE, "kvc_c128_online_decode: sizes exceed 2^31-1");
-  return hip_status(kvc::launch_c128_decode(state, num_slots, kv_score_in, out, ape, indices,
-                                            seq_lens, batch, (hipStream_t)stream),
+  return kvc_c128_online_decode_layers(state, 0, num_slots, kv_score_in, 0, out, 0, ape, 0,
+                                       indices, seq_lens, batch, 1, stream);
+}
+
+int kvc_c128_online_decode_layers(float* state, int64_t state_layer_stride, int64_t num_slots,
+                                  const float* kv_score_in, int64_t in_layer_stride, float* out,
+                                  int64_t out_layer_stride, const float* ape,
+                                  int64_t ape_layer_stride, const int32_t* indices,
+                                  const int32_t* seq_lens, int64_t batch, int64_t num_layers,
+                                  void* stream) {
+  const char* fn = "kvc_c128_online_decode";
+  if (batch < 0 || num_slots < 0 || num_layers < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (batch == 0 || num_layers == 0) return ok();
+  int rc = check_decode(fn, state, num_slots, kv_score_in, ape, indices, seq_lens, batch);
+  if (rc != KVC_OK) return rc;
+  if (!out) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (!aligned(out, 16)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  if (num_layers > 65535) return fail(KVC_ERR_SHAPE, "%s: num_layers exceeds 65535", fn);
+  if (num_layers > 1 &&
+      (state_layer_stride < num_slots * 384 || in_layer_stride < batch * 256 ||
+       out_layer_stride < batch * 128 || ape_layer_stride < 128 * 128 ||
+       state_layer_stride % 4 || in_layer_stride % 4 || out_layer_stride % 4 ||
+       ape_layer_stride % 4))
+    return fail(KVC_ERR_SHAPE, "%s: layer strides must cover a layer and keep 16-byte rows", fn);
+  return hip_status(kvc::launch_c128_decode(state, state_layer_stride, num_slots, kv_score_in,
+                                            in_layer_stride, out, out_layer_stride, nullptr,
+                                            nullptr, false, ape, ape_layer_stride, indices,
+                                            seq_lens, batch, num_layers, (hipStream_t)stream),
                     "kvc_c128_online_decode launch");
+}
+
+int kvc_c128_online_decode_quant(float* state, int64_t num_slots, const float* kv_score_in,
+                                 uint8_t* out_fp8, float* out_scale, const float* ape,
+                                 const int32_t* indices, const int32_t* seq_lens, int64_t batch,
+                                 int round_scale, void* stream) {
+  const char* fn = "kvc_c128_online_decode_quant";
+  if (batch < 0 || num_slots < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (batch == 0) return ok();
+  int rc = check_decode(fn, state, num_slots, kv_score_in, ape, indices, seq_lens, batch);
+  if (rc != KVC_OK) return rc;
+  if (!out_fp8 || !out_scale) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (!aligned(out_fp8, 4) || !aligned(out_scale, 4))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  return hip_status(kvc::launch_c128_decode(state, 0, num_slots, kv_score_in, 0, nullptr, 0,
+                                            out_fp8, out_scale, round_scale != 0, ape, 0, indices,
+                                            seq_lens, batch, 1, (hipStream_t)stream),
+                    "kvc_c128_online_decode_quant launch");
 }
 
 int kvc_c128_online_prefill(float* state, int64_t num_slots, const float* kv_score_in, float* out,
@@ -333,23 +399,43 @@ int kvc_c128_online_prefill(float* state, int64_t num_slots, const float* kv_sco
                             const int32_t* load_indices, int64_t batch,
                             const kvc_online_plan* compress_plan, uint32_t n_compress,
                             const kvc_online_plan* write_plan, uint32_t n_write, void* stream) {
-  if (batch < 0 || num_slots < 0 || num_tokens < 0)
-    return fail(KVC_ERR_SHAPE, "kvc_c128_online_prefill: negative size");
+  const char* fn = "kvc_c128_online_prefill";
+  if (batch < 0 || num_slots < 0 || num_tokens < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
   if (n_compress == 0 && n_write == 0) return ok();
-  if (!state || !kv_score_in || !ape || !indices || (n_compress && (!compress_plan || !out)) ||
-      (n_write && !write_plan))
-    return fail(KVC_ERR_NULL, "kvc_c128_online_prefill: NULL pointer");
-  if (!aligned(state, 16) || !aligned(kv_score_in, 16) || !aligned(ape, 16) ||
-      (out && !aligned(out, 16)) || (compress_plan && !aligned(compress_plan, 16)) ||
-      (write_plan && !aligned(write_plan, 16)))
-    return fail(KVC_ERR_SHAPE, "kvc_c128_online_prefill: misaligned pointer");
-  if (num_tokens > (int64_t)0xfffffffeLL || num_slots > kMaxI32 || batch > kMaxI32)
-    return fail(KVC_ERR_SHAPE, "kvc_c128_online_prefill: sizes out of range");
-  return hip_status(kvc::launch_c128_prefill(state, num_slots, kv_score_in, out, num_tokens, ape,
+  int rc = check_prefill(fn, state, num_slots, kv_score_in, num_tokens, ape, indices, batch,
+                         compress_plan, n_compress, write_plan, n_write);
+  if (rc != KVC_OK) return rc;
+  if (n_compress && !out) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (out && !aligned(out, 16)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  return hip_status(kvc::launch_c128_prefill(state, num_slots, kv_score_in, out, nullptr, nullptr,
+                                             false, num_tokens, ape, indices, load_indices, batch,
+                                             compress_plan, n_compress, write_plan, n_write,
+                                             (hipStream_t)stream),
+                    "kvc_c128_online_prefill launch");
+}
+
+int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* kv_score_in,
+                                  uint8_t* out_fp8, float* out_scale, int64_t num_tokens,
+                                  const float* ape, const int32_t* indices,
+                                  const int32_t* load_indices, int64_t batch,
+                                  const kvc_online_plan* compress_plan, uint32_t n_compress,
+                                  const kvc_online_plan* write_plan, uint32_t n_write,
+                                  int round_scale, void* stream) {
+  const char* fn = "kvc_c128_online_prefill_quant";
+  if (batch < 0 || num_slots < 0 || num_tokens < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (n_compress == 0 && n_write == 0) return ok();
+  int rc = check_prefill(fn, state, num_slots, kv_score_in, num_tokens, ape, indices, batch,
+                         compress_plan, n_compress, write_plan, n_write);
+  if (rc != KVC_OK) return rc;
+  if (n_compress && (!out_fp8 || !out_scale)) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if ((out_fp8 && !aligned(out_fp8, 4)) || (out_scale && !aligned(out_scale, 4)))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  return hip_status(kvc::launch_c128_prefill(state, num_slots, kv_score_in, nullptr, out_fp8,
+                                             out_scale, round_scale != 0, num_tokens, ape,
                                              indices, load_indices, batch, compress_plan,
                                              n_compress, write_plan, n_write,
                                              (hipStream_t)stream),
-                    "kvc_c128_online_prefill launch");
+                    "kvc_c128_online_prefill_quant launch");
 }
 
 // --------------------------------------------------------------- diagnostics

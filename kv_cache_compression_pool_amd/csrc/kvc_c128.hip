@@ -31,22 +31,58 @@ namespace {
 // ------------------------------------------------------------------ decode
 constexpr int kDecodeReqPerBlock = 2;
 
+// Where emitted (chunk-closing) vectors go: fp32 rows, or e4m3 codes plus a
+// per-vector scale after the bf16 / rotation / quantisation epilogue.
+struct EmitSink {
+  float* out;            // fp32 [rows, 128] (fp32 mode)
+  uint8_t* codes;        // e4m3 [rows, 128] (quantised mode)
+  float* scales;         // fp32 [rows]      (quantised mode)
+  int64_t out_ls;        // per-layer strides (elements) of out / codes / scales
+  int64_t codes_ls;
+  int64_t scales_ls;
+  bool round_scale;
+};
+
+// Emit one 128-vector held by 32 lanes (lane q: channels 4q..4q+3).  In the
+// quantised mode the 32 lanes must all be active.
+template <bool kQuant>
+__device__ __forceinline__ void emit32(const EmitSink& o, int64_t layer, int64_t row, int q,
+                                       const float (&K)[4]) {
+  if constexpr (kQuant) {
+    // channel 4q + t: bits 0-1 in registers, bits 2-5 in the lane of the
+    // 16-lane row (q & 15), bit 6 in the row (q >> 4).
+    float v[4] = {K[0], K[1], K[2], K[3]};
+    float scale;
+    const uint32_t code = rotate_quantise32(v, q & 15, q >> 4, o.round_scale, scale);
+    reinterpret_cast<uint32_t*>(o.codes + layer * o.codes_ls + row * 128)[q] = code;
+    if (q == 0) o.scales[layer * o.scales_ls + row] = scale;
+  } else {
+    reinterpret_cast<float4*>(o.out + layer * o.out_ls + row * 128)[q] =
+        make_float4(K[0], K[1], K[2], K[3]);
+  }
+}
+
+// One request per 32 lanes; blockIdx.y selects the layer (state, input,
+// output and ape advance by their layer strides; indices and lengths are
+// shared by all layers).
+template <bool kQuant>
 __global__ __launch_bounds__(64) void c128_decode_kernel(
-    float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
-    float* __restrict__ out, const float* __restrict__ ape, const int32_t* __restrict__ indices,
-    const int32_t* __restrict__ seq_lens, int64_t batch) {
+    float* __restrict__ state, int64_t state_ls, int64_t num_slots, const float* __restrict__ in,
+    int64_t in_ls, EmitSink o, const float* __restrict__ ape, int64_t ape_ls,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ seq_lens, int64_t batch) {
+  const int64_t layer = blockIdx.y;
   const int64_t b = (int64_t)blockIdx.x * kDecodeReqPerBlock + (threadIdx.x >> 5);
   const int q = threadIdx.x & 31;                       // channels 4q..4q+3
   if (b >= batch) return;
   const int32_t idx = indices[b];
   const int32_t L = seq_lens[b];
-  const float4* row = reinterpret_cast<const float4*>(in + b * 256);
+  const float4* row = reinterpret_cast<const float4*>(in + layer * in_ls + b * 256);
   const float4 kv = row[q];
   const float4 sc = row[32 + q];
   if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
   const int c = (L - 1) & 127;
-  const float4 bias = reinterpret_cast<const float4*>(ape + c * 128)[q];
-  float4* st = reinterpret_cast<float4*>(state + (int64_t)idx * 384);
+  const float4 bias = reinterpret_cast<const float4*>(ape + layer * ape_ls + c * 128)[q];
+  float4* st = reinterpret_cast<float4*>(state + layer * state_ls + (int64_t)idx * 384);
 
   float s[4] = {sc.x + bias.x, sc.y + bias.y, sc.z + bias.z, sc.w + bias.w};
   float k[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -71,7 +107,7 @@ __global__ __launch_bounds__(64) void c128_decode_kernel(
     for (int i = 0; i < 4; ++i) { M[i] = s[i]; S[i] = 1.0f; K[i] = k[i]; }
   }
   if (c == 127) {
-    reinterpret_cast<float4*>(out + b * 128)[q] = make_float4(K[0], K[1], K[2], K[3]);
+    emit32<kQuant>(o, layer, b, q, K);
   } else {
     st[q] = make_float4(M[0], M[1], M[2], M[3]);
     st[32 + q] = make_float4(S[0], S[1], S[2], S[3]);
@@ -112,10 +148,10 @@ __device__ __forceinline__ float4 load_stream4(const float4* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-template <bool kWrite, int kWaves>
+template <bool kWrite, int kWaves, bool kQuant>
 __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
     float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
-    float* __restrict__ out, int64_t num_tokens, const float* __restrict__ ape,
+    EmitSink o, int64_t num_tokens, const float* __restrict__ ape,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ load_indices, int64_t batch,
     const kvc_online_plan* __restrict__ plans, uint32_t n_plans) {
   constexpr int kTokPerLane = 128 / (2 * kWaves);   // chunk positions per lane
@@ -256,43 +292,55 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
     st[32 + q] = make_float4(D[0], D[1], D[2], D[3]);
     st[64 + q] = make_float4(K[0], K[1], K[2], K[3]);
   } else {
-    reinterpret_cast<float4*>(out + (int64_t)p.ragged_id * 128)[q] =
-        make_float4(K[0], K[1], K[2], K[3]);
+    emit32<kQuant>(o, 0, (int64_t)p.ragged_id, q, K);
   }
 }
 
 }  // namespace
 
-hipError_t launch_c128_decode(float* state, int64_t num_slots, const float* in, float* out,
-                              const float* ape, const int32_t* indices, const int32_t* seq_lens,
-                              int64_t batch, hipStream_t stream) {
-  const dim3 grid((unsigned)((batch + kDecodeReqPerBlock - 1) / kDecodeReqPerBlock));
-  hipLaunchKernelGGL(c128_decode_kernel, grid, dim3(64), 0, stream, state, num_slots, in, out,
-                     ape, indices, seq_lens, batch);
+hipError_t launch_c128_decode(float* state, int64_t state_ls, int64_t num_slots, const float* in,
+                              int64_t in_ls, float* out, int64_t out_ls, uint8_t* codes,
+                              float* scales, bool round_scale, const float* ape, int64_t ape_ls,
+                              const int32_t* indices, const int32_t* seq_lens, int64_t batch,
+                              int64_t num_layers, hipStream_t stream) {
+  const dim3 grid((unsigned)((batch + kDecodeReqPerBlock - 1) / kDecodeReqPerBlock),
+                  (unsigned)num_layers);
+  const EmitSink o{out, codes, scales, out_ls, batch * 128, batch, round_scale};
+  if (codes)
+    hipLaunchKernelGGL((c128_decode_kernel<true>), grid, dim3(64), 0, stream, state, state_ls,
+                       num_slots, in, in_ls, o, ape, ape_ls, indices, seq_lens, batch);
+  else
+    hipLaunchKernelGGL((c128_decode_kernel<false>), grid, dim3(64), 0, stream, state, state_ls,
+                       num_slots, in, in_ls, o, ape, ape_ls, indices, seq_lens, batch);
   return hipGetLastError();
 }
 
 hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in, float* out,
+                               uint8_t* codes, float* scales, bool round_scale,
                                int64_t num_tokens, const float* ape, const int32_t* indices,
                                const int32_t* load_indices, int64_t batch,
                                const kvc_online_plan* cplan, uint32_t n_c,
                                const kvc_online_plan* wplan, uint32_t n_w, hipStream_t stream) {
   if (!load_indices) load_indices = indices;
+  const EmitSink o{out, codes, scales, 0, 0, 0, round_scale};
   // Pass 1 (compress plans) only reads the state; pass 2 (write plans) writes
   // it.  Stream order puts every pass-1 read before any pass-2 write.
   if (n_c) {
-    hipLaunchKernelGGL((c128_prefill_kernel<false, kCompressWaves>), dim3(n_c),
-                       dim3(64 * kCompressWaves), 0, stream,
-                       state, num_slots, in, out, num_tokens, ape, indices, load_indices, batch,
-                       cplan, n_c);
+    if (codes)
+      hipLaunchKernelGGL((c128_prefill_kernel<false, kCompressWaves, true>), dim3(n_c),
+                         dim3(64 * kCompressWaves), 0, stream, state, num_slots, in, o,
+                         num_tokens, ape, indices, load_indices, batch, cplan, n_c);
+    else
+      hipLaunchKernelGGL((c128_prefill_kernel<false, kCompressWaves, false>), dim3(n_c),
+                         dim3(64 * kCompressWaves), 0, stream, state, num_slots, in, o,
+                         num_tokens, ape, indices, load_indices, batch, cplan, n_c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (n_w) {
-    hipLaunchKernelGGL((c128_prefill_kernel<true, kWriteWaves>), dim3(n_w),
-                       dim3(64 * kWriteWaves), 0, stream,
-                       state, num_slots, in, out, num_tokens, ape, indices, load_indices, batch,
-                       wplan, n_w);
+    hipLaunchKernelGGL((c128_prefill_kernel<true, kWriteWaves, false>), dim3(n_w),
+                       dim3(64 * kWriteWaves), 0, stream, state, num_slots, in, o, num_tokens,
+                       ape, indices, load_indices, batch, wplan, n_w);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -141,4 +141,39 @@ __device__ __forceinline__ float fp8_scale(float absmax, bool round_scale) {
   return round_scale ? pow2_ceil(t) : t;
 }
 
+// ---- rotate + quantise one 128-vector held by 32 lanes --------------------
+// v[0..3]: fp32 values of 4 channels per lane, spread as wht128_split
+// expects (2 channel bits in registers, 4 in the row's lanes, 1 across the
+// two rows).  The Walsh-Hadamard matrix is a tensor product over the index
+// bits, so any such assignment of channel bits gives the same transform as
+// long as input and output use it.  Steps: bf16 round, rotate, scale by
+// 1/sqrt(128), bf16 round, per-vector scale, clamp, e4m3.  Returns the 4 codes
+// (little-endian) and the vector's scale (same in all 32 lanes).
+__device__ __forceinline__ uint32_t rotate_quantise32(float (&v)[4], int c, int h,
+                                                      bool round_scale, float& scale_out) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) v[t] = round_bf16(v[t]);
+  wht128_split(v, c, h);
+  float amax = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[t] = round_bf16(v[t] * kInvSqrt128);
+    amax = fmaxf(amax, fabsf(v[t]));
+  }
+  amax = row_max16(amax);
+  amax = fmaxf(amax, swap_rows16(amax));
+  const float scale = fp8_scale(amax, round_scale);
+  float q[4];
+  if (round_scale) {
+    const float inv = pow2_recip(scale);   // exact: scale is a power of two
+#pragma unroll
+    for (int t = 0; t < 4; ++t) q[t] = clamp_fp8(v[t] * inv);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) q[t] = clamp_fp8(v[t] / scale);   // IEEE division
+  }
+  scale_out = scale;
+  return pack_e4m3x4(q[0], q[1], q[2], q[3]);
+}
+
 }  // namespace kvc

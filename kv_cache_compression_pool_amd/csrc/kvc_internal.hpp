@@ -33,11 +33,19 @@ hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t
                               int64_t key_stride, const uint16_t* score, int64_t score_stride,
                               const int32_t* tslot, int64_t n_tokens, hipStream_t stream);
 
-hipError_t launch_c128_decode(float* state, int64_t num_slots, const float* in, float* out,
-                              const float* ape, const int32_t* indices, const int32_t* seq_lens,
-                              int64_t batch, hipStream_t stream);
+// Decode over num_layers layers (blockIdx.y); emitted vectors go to `out`
+// (fp32) or, when `codes` is non-null, through the rotate/quantise epilogue
+// to codes [layers][batch][128] and scales [layers][batch].
+hipError_t launch_c128_decode(float* state, int64_t state_ls, int64_t num_slots, const float* in,
+                              int64_t in_ls, float* out, int64_t out_ls, uint8_t* codes,
+                              float* scales, bool round_scale, const float* ape, int64_t ape_ls,
+                              const int32_t* indices, const int32_t* seq_lens, int64_t batch,
+                              int64_t num_layers, hipStream_t stream);
 
+// Prefill; chunk-closing vectors go to `out` (fp32 [num_tokens,128]) or,
+// when `codes` is non-null, to codes [num_tokens,128] + scales [num_tokens].
 hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in, float* out,
+                               uint8_t* codes, float* scales, bool round_scale,
                                int64_t num_tokens, const float* ape, const int32_t* indices,
                                const int32_t* load_indices, int64_t batch,
                                const kvc_online_plan* cplan, uint32_t n_c,

@@ -115,28 +115,8 @@ __device__ __forceinline__ uint32_t pool_epilogue(const float (&x)[8], int c, in
                                                   bool round_scale, float& scale_out) {
   float v[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) v[t] = round_bf16(h ? x[4 + t] : x[t]);
-  wht128_split(v, c, h);
-  float amax = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    v[t] = round_bf16(v[t] * kInvSqrt128);
-    amax = fmaxf(amax, fabsf(v[t]));
-  }
-  amax = row_max16(amax);
-  amax = fmaxf(amax, swap_rows16(amax));
-  const float scale = fp8_scale(amax, round_scale);
-  float q[4];
-  if (round_scale) {
-    const float inv = pow2_recip(scale);   // exact: scale is a power of two
-#pragma unroll
-    for (int t = 0; t < 4; ++t) q[t] = clamp_fp8(v[t] * inv);
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) q[t] = clamp_fp8(v[t] / scale);   // IEEE division
-  }
-  scale_out = scale;
-  return pack_e4m3x4(q[0], q[1], q[2], q[3]);
+  for (int t = 0; t < 4; ++t) v[t] = h ? x[4 + t] : x[t];
+  return rotate_quantise32(v, c, h, round_scale, scale_out);
 }
 
 // Where a compressed vector goes.  Packed: codes row `row` of a [n,128]

@@ -30,7 +30,9 @@ PLAN_SENTINEL = 0xFFFFFFFF
 EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_plan_prefill",
            "kvc_compress_prefill", "kvc_compress_prefill_paged", "kvc_compress_decode_ring",
            "kvc_compress_decode_ring_paged", "kvc_seed_tail_ring",
-           "kvc_c128_online_decode", "kvc_c128_online_prefill", "kvc_diag_convert")
+           "kvc_c128_online_decode", "kvc_c128_online_decode_layers",
+           "kvc_c128_online_decode_quant", "kvc_c128_online_prefill",
+           "kvc_c128_online_prefill_quant", "kvc_diag_convert")
 
 
 class KvcError(RuntimeError):
@@ -70,6 +72,12 @@ def lib() -> ctypes.CDLL:
         L.kvc_c128_online_decode.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]
         L.kvc_c128_online_prefill.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _p, _u32,
                                               _p, _u32, _p]
+        L.kvc_c128_online_decode_layers.argtypes = [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                                    _p, _p, _i64, _i64, _p]
+        L.kvc_c128_online_decode_quant.argtypes = [_p, _i64, _p, _p, _p, _p, _p, _p, _i64, _i32,
+                                                   _p]
+        L.kvc_c128_online_prefill_quant.argtypes = [_p, _i64, _p, _p, _p, _i64, _p, _p, _p,
+                                                    _i64, _p, _u32, _p, _u32, _i32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
@@ -309,6 +317,82 @@ def kvc_c128_online_decode(state, kv_score_in, out, ape, indices, seq_lens, stre
         _dptr(seq_lens, torch.int32, "seq_lens"), kv_score_in.shape[0], _stream(stream)))
 
 
+def kvc_c128_online_decode_layers(state, kv_score_in, out, ape, indices, seq_lens, stream=None):
+    """Multi-layer decode: state [L,S,384], kv_score_in [L,B,256], out
+    [L,B,128], ape [L,128,128] (contiguous); indices / seq_lens [B] shared."""
+    import torch
+    Lr, B = kv_score_in.shape[0], kv_score_in.shape[1]
+    _shape_ok(state, (Lr, None, 384), "state")
+    _shape_ok(kv_score_in, (Lr, B, 256), "kv_score_in")
+    _shape_ok(out, (Lr, B, 128), "out")
+    _shape_ok(ape, (Lr, 128, 128), "ape")
+    _shape_ok(indices, (B,), "indices")
+    _shape_ok(seq_lens, (B,), "seq_lens")
+    _check(lib().kvc_c128_online_decode_layers(
+        _dptr(state, torch.float32, "state"), state.stride(0), state.shape[1],
+        _dptr(kv_score_in, torch.float32, "kv_score_in"), kv_score_in.stride(0),
+        _dptr(out, torch.float32, "out"), out.stride(0), _dptr(ape, torch.float32, "ape"),
+        ape.stride(0), _dptr(indices, torch.int32, "indices"),
+        _dptr(seq_lens, torch.int32, "seq_lens"), B, Lr, _stream(stream)))
+
+
+def kvc_c128_online_decode_quant(state, kv_score_in, out_fp8, out_scale, ape, indices, seq_lens,
+                                 round_scale: bool, stream=None):
+    """Decode with the rotate / e4m3 epilogue on emitted vectors: out_fp8
+    uint8 [B,128], out_scale fp32 [B]."""
+    import torch
+    B = kv_score_in.shape[0]
+    _shape_ok(state, (None, 384), "state")
+    _shape_ok(kv_score_in, (B, 256), "kv_score_in")
+    _shape_ok(out_fp8, (B, 128), "out_fp8")
+    _shape_ok(out_scale, (B,), "out_scale")
+    _shape_ok(ape, (128, 128), "ape")
+    _shape_ok(indices, (B,), "indices")
+    _shape_ok(seq_lens, (B,), "seq_lens")
+    _check(lib().kvc_c128_online_decode_quant(
+        _dptr(state, torch.float32, "state"), state.shape[0],
+        _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out_fp8, torch.uint8, "out_fp8"),
+        _dptr(out_scale, torch.float32, "out_scale"), _dptr(ape, torch.float32, "ape"),
+        _dptr(indices, torch.int32, "indices"), _dptr(seq_lens, torch.int32, "seq_lens"), B,
+        int(round_scale), _stream(stream)))
+
+
+def kvc_c128_online_prefill_quant(state, kv_score_in, out_fp8, out_scale, ape, indices,
+                                  compress_plan, n_compress, write_plan, n_write,
+                                  round_scale: bool, load_indices=None, stream=None):
+    """Prefill with the rotate / e4m3 epilogue on chunk-closing vectors:
+    out_fp8 uint8 [N,128], out_scale fp32 [N]."""
+    import torch
+    N, B = kv_score_in.shape[0], indices.shape[0]
+    _shape_ok(state, (None, 384), "state")
+    _shape_ok(kv_score_in, (N, 256), "kv_score_in")
+    _shape_ok(out_fp8, (N, 128), "out_fp8")
+    _shape_ok(out_scale, (N,), "out_scale")
+    _shape_ok(ape, (128, 128), "ape")
+    _shape_ok(indices, (B,), "indices")
+    if load_indices is not None:
+        _shape_ok(load_indices, (B,), "load_indices")
+    _check_plans(compress_plan, n_compress, write_plan, n_write)
+    _check(lib().kvc_c128_online_prefill_quant(
+        _dptr(state, torch.float32, "state"), state.shape[0],
+        _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out_fp8, torch.uint8, "out_fp8"),
+        _dptr(out_scale, torch.float32, "out_scale"), N, _dptr(ape, torch.float32, "ape"),
+        _dptr(indices, torch.int32, "indices"),
+        _dptr(load_indices, torch.int32, "load_indices", optional=True), B,
+        None if compress_plan is None else compress_plan.data_ptr(), int(n_compress),
+        None if write_plan is None else write_plan.data_ptr(), int(n_write), int(round_scale),
+        _stream(stream)))
+
+
+def _check_plans(compress_plan, n_compress, write_plan, n_write):
+    for name, plan, n in (("compress_plan", compress_plan, n_compress),
+                          ("write_plan", write_plan, n_write)):
+        if int(n) > 0:
+            _need(plan is not None and plan.is_cuda and plan.is_contiguous()
+                  and plan.numel() * plan.element_size() >= 16 * int(n),
+                  f"{name} must be a contiguous device tensor of at least {int(n)} entries")
+
+
 def kvc_c128_online_prefill(state, kv_score_in, out, ape, indices, compress_plan, n_compress,
                             write_plan, n_write, load_indices=None, stream=None):
     """compress_plan / write_plan: device uint8 tensors of 16-byte entries (or
@@ -322,12 +406,7 @@ def kvc_c128_online_prefill(state, kv_score_in, out, ape, indices, compress_plan
     _shape_ok(indices, (B,), "indices")
     if load_indices is not None:
         _shape_ok(load_indices, (B,), "load_indices")
-    for name, plan, n in (("compress_plan", compress_plan, n_compress),
-                          ("write_plan", write_plan, n_write)):
-        if int(n) > 0:
-            _need(plan is not None and plan.is_cuda and plan.is_contiguous()
-                  and plan.numel() * plan.element_size() >= 16 * int(n),
-                  f"{name} must be a contiguous device tensor of at least {int(n)} entries")
+    _check_plans(compress_plan, n_compress, write_plan, n_write)
     cp = None if compress_plan is None else compress_plan.data_ptr()
     wp = None if write_plan is None else write_plan.data_ptr()
     _check(lib().kvc_c128_online_prefill(

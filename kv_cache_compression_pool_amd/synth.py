@@ -135,14 +135,19 @@ def _prior_tokens(g, counts):
 
 
 def c128_decode(seed: int = 0, batch: int = 1024, num_slots: int = 2048,
-                max_seq: int = 131072):
+                max_seq: int = 131072, emit_frac: float = 0.0, seq_lens=None):
     """Inputs for one decode step.  The state of request b must be built from
     ``prior_in`` rows (its first ``prior_counts[b]`` rows belong to b, in
     order) by folding them into an open chunk that ends at position
-    seq_lens[b]-2; slots whose chunk is empty are never read."""
+    seq_lens[b]-2; slots whose chunk is empty are never read.  ``emit_frac``
+    of the requests are moved to a chunk-closing length (a multiple of 128);
+    ``seq_lens`` overrides the drawn lengths."""
     g = rng(seed, "c128_decode")
     indices = g.permutation(num_slots)[:batch].astype(np.int32)
-    seq_lens = g.integers(1, max_seq, size=batch, endpoint=True).astype(np.int32)
+    drawn = g.integers(1, max_seq, size=batch, endpoint=True).astype(np.int32)
+    closing = g.random(batch) < emit_frac
+    drawn = np.where(closing, np.maximum(drawn // 128, 1) * 128, drawn).astype(np.int32)
+    seq_lens = drawn if seq_lens is None else np.asarray(seq_lens, np.int32)
     kv_score = g.standard_normal((batch, 2 * HEAD_DIM), dtype=np.float32)
     ape = (g.standard_normal((128, HEAD_DIM), dtype=np.float32) * np.float32(0.1))
     prior_counts = ((seq_lens.astype(np.int64) - 1) % 128)

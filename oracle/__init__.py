@@ -304,6 +304,36 @@ def c128_decode(state, kv_score_in, ape, indices, seq_lens, out=None):
     return out
 
 
+def c128_decode_quant(state, kv_score_in, ape, indices, seq_lens, round_scale: bool):
+    """Decode, then the pool-16 epilogue (bf16, rotation, bf16, e4m3) on every
+    emitted vector.  Returns (emitted row mask, codes [B,128], scales [B],
+    fp32 out [B,128]); non-emitted rows of codes / scales are zero."""
+    x = _c(kv_score_in, np.float32)
+    B = x.shape[0]
+    out = np.full((B, 128), np.nan, np.float32)
+    c128_decode(state, x, ape, indices, seq_lens, out=out)
+    emit = ~np.isnan(out[:, 0])
+    codes = np.zeros((B, 128), np.uint8)
+    scales = np.zeros(B, np.float32)
+    codes[emit], scales[emit] = pool_epilogue(out[emit], round_scale)
+    return emit, codes, scales, out
+
+
+def c128_prefill_quant(state, kv_score_in, ape, indices, cplan, wplan, round_scale: bool,
+                       load_indices=None):
+    """Prefill, then the pool-16 epilogue on every chunk-closing vector.
+    Returns (written row mask, codes [N,128], scales [N], fp32 out [N,128])."""
+    x = _c(kv_score_in, np.float32)
+    N = x.shape[0]
+    out = np.full((max(N, 1), 128), np.nan, np.float32)
+    c128_prefill(state, x, ape, indices, cplan, wplan, load_indices=load_indices, out=out)
+    rows = ~np.isnan(out[:, 0])
+    codes = np.zeros((out.shape[0], 128), np.uint8)
+    scales = np.zeros(out.shape[0], np.float32)
+    codes[rows], scales[rows] = pool_epilogue(out[rows], round_scale)
+    return rows, codes, scales, out
+
+
 def c128_plan(seq_lens, extend_lens, num_tokens: int, pad: bool = False):
     """Compress / write plan lists (structured arrays of PLAN_DTYPE)."""
     sl = _c(seq_lens, np.int64)

@@ -530,3 +530,96 @@ def test_paged_ring_decode_matches_packed():
     written = ref_s != 5.0
     exp = _paged_expect(gc, gsc, np.arange(d["num_out"]), written, d["num_out"], 0x5A)
     assert np.array_equal(cache.cpu().numpy(), exp)
+
+
+# ------------------------------------------------------------------ c128 layers / quantised epilogue
+def _layer_case(seq_lens, indices, seed, num_slots=2048):
+    from tests.helpers import seed_states
+    d = synth.c128_decode(seed=seed, batch=indices.size, num_slots=num_slots, seq_lens=seq_lens)
+    st = synth.nan_state(num_slots)
+    seed_states(st, indices, d["prior_counts"], d["prior_in"], seq_lens.astype(np.int64) - 1,
+                d["ape"])
+    return st, d["kv_score_in"], d["ape"]
+
+
+def test_c128_decode_layers_equal_separate_calls():
+    base = c128_decode_case(seed=3, batch=300, emit_frac=0.2)
+    idx, sl = base["indices"], base["seq_lens"]
+    layers = [(base["state"], base["kv_score_in"], base["ape"])]
+    layers += [_layer_case(sl, idx, seed=40 + l) for l in range(4)]
+    L = len(layers)
+    note(f"c128 decode {L} layers x 300")
+    st = np.stack([x[0] for x in layers])
+    xin = np.stack([x[1] for x in layers])
+    ape = np.stack([x[2] for x in layers])
+    gst, gout = dev(st), torch.full((L, 300, 128), float("nan"), device="cuda")
+    kvc.kvc_c128_online_decode_layers(gst, dev(xin), gout, dev(ape), dev(idx), dev(sl))
+    torch.cuda.synchronize()
+    gst, gout = gst.cpu().numpy(), gout.cpu().numpy()
+    for l in range(L):
+        rs = st[l].copy()
+        ro = np.full((300, 128), np.nan, np.float32)
+        oracle.c128_decode(rs, xin[l], ape[l], idx, sl, out=ro)
+        assert np.array_equal(np.isnan(gout[l]), np.isnan(ro))
+        e = ~np.isnan(ro[:, 0])
+        assert e.sum() > 20
+        assert rel_err_rows(gout[l][e], ro[e]).max() <= VEC_TOL
+        compare_state(gst[l], rs, f"layer {l} state")
+
+
+@pytest.mark.parametrize("round_scale", [True, False])
+def test_c128_decode_quant_epilogue(round_scale):
+    d = c128_decode_case(seed=5, batch=1024, emit_frac=0.5)
+    note(f"c128 decode quant round_scale={round_scale}")
+    B = 1024
+    rs = d["state"].copy()
+    emit, rc, rsc, ro = oracle.c128_decode_quant(rs, d["kv_score_in"], d["ape"], d["indices"],
+                                                 d["seq_lens"], round_scale)
+    args = (dev(d["kv_score_in"]),)
+    g1 = dev(d["state"])
+    gout = torch.full((B, 128), float("nan"), device="cuda")
+    kvc.kvc_c128_online_decode(g1, args[0], gout, dev(d["ape"]), dev(d["indices"]),
+                               dev(d["seq_lens"]))
+    g2 = dev(d["state"])
+    gcodes = torch.full((B, 128), 0x33, dtype=torch.uint8, device="cuda")
+    gscale = torch.full((B,), 5.0, device="cuda")
+    kvc.kvc_c128_online_decode_quant(g2, args[0], gcodes, gscale, dev(d["ape"]),
+                                     dev(d["indices"]), dev(d["seq_lens"]), round_scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(g1.cpu().numpy(), g2.cpu().numpy(), equal_nan=True)
+    gout, gc, gs = gout.cpu().numpy(), gcodes.cpu().numpy(), gscale.cpu().numpy()
+    assert np.array_equal(~np.isnan(gout[:, 0]), emit) and emit.sum() > 300
+    assert np.all(gc[~emit] == 0x33) and np.all(gs[~emit] == 5.0)
+    assert rel_err_rows(gout[emit], ro[emit]).max() <= VEC_TOL
+    ref_c, ref_s, flips = reference_for(gout[emit], ro[emit], rc[emit], rsc[emit], round_scale,
+                                        "c128 decode quant")
+    check_codes(gc[emit], ref_c, "c128 decode quant")
+    check_scales(gs[emit], ref_s, round_scale, "c128 decode quant")
+    note(f"c128 decode quant: {emit.sum()} vectors, bf16-boundary vectors {flips}")
+
+
+def test_c128_prefill_quant_epilogue():
+    d = c128_prefill_case(seed=0)
+    N = int(d["extend_lens"].sum())
+    note("c128 prefill quant 32 seqs")
+    rs = d["state"].copy()
+    rows, rc, rsc, ro = oracle.c128_prefill_quant(rs, d["kv_score_in"], d["ape"], d["indices"],
+                                                  d["cplan"], d["wplan"], True)
+    gst, gout, cp, wp = run_c128_prefill_gpu(d, d["state"])
+    g2 = dev(d["state"])
+    gcodes = torch.full((N, 128), 0x33, dtype=torch.uint8, device="cuda")
+    gscale = torch.full((N,), 5.0, device="cuda")
+    kvc.kvc_c128_online_prefill_quant(g2, dev(d["kv_score_in"]), gcodes, gscale, dev(d["ape"]),
+                                      dev(d["indices"]), kvc.plans_to_device(cp), cp.size,
+                                      kvc.plans_to_device(wp), wp.size, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(gst, g2.cpu().numpy(), equal_nan=True)
+    gc, gs = gcodes.cpu().numpy(), gscale.cpu().numpy()
+    assert np.array_equal(~np.isnan(gout[:, 0]), rows[:N])
+    assert np.all(gc[~rows[:N]] == 0x33)
+    r = rows[:N]
+    ref_c, ref_s, flips = reference_for(gout[r], ro[:N][r], rc[:N][r], rsc[:N][r], True,
+                                        "c128 prefill quant")
+    check_codes(gc[r], ref_c, "c128 prefill quant")
+    check_scales(gs[r], ref_s, True, "c128 prefill quant")
+    note(f"c128 prefill quant: {r.sum()} vectors, bf16-boundary vectors {flips}")
