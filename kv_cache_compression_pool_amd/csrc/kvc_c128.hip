@@ -10,11 +10,12 @@
 //            row); two requests per 64-thread workgroup so even a small batch
 //            spreads over many CUs.  Loads that do not depend on the slot
 //            index (input row, lengths) are issued before the state load.
-//   prefill  one 256-thread workgroup per plan.  Wave w covers chunk
-//            positions [32w, 32w+32); its two half-waves take even / odd
+//   prefill  one 512-thread workgroup per plan.  Wave w covers chunk
+//            positions [16w, 16w+16); its two half-waves take even / odd
 //            positions, 4 channels per lane, so every token row is read with
 //            128-bit loads and each lane keeps a private two-pass softmax over
-//            16 tokens in registers.  Partial (max, sum, weighted sum) states
+//            8 tokens in registers.  All row loads are issued branch-free
+//            right after the 16-byte plan load.  Partial (max, sum, weighted sum) states
 //            are merged across half-waves with a lane shuffle and across waves
 //            through LDS, then merged with the stored state when the segment
 //            starts mid-chunk.  Sums stay unnormalised until the end, so an
@@ -117,14 +118,14 @@ __global__ __launch_bounds__(64) void c128_decode_kernel(
 
 // ------------------------------------------------------------------ prefill
 #ifndef KVC_C128_COMPRESS_WAVES
-#define KVC_C128_COMPRESS_WAVES 4
+#define KVC_C128_COMPRESS_WAVES 8
 #endif
 #ifndef KVC_C128_WRITE_WAVES
 #define KVC_C128_WRITE_WAVES 8
 #endif
-// The compress pass has many plans and is bandwidth-bound: 4 waves per plan,
-// 16 chunk positions per lane.  The write pass has at most one plan per
-// request and is latency-bound: more waves per plan, fewer positions each.
+// 8 waves per plan (8 chunk positions per lane) keeps every lane's row loads
+// in flight at once within 128 VGPRs; measured best for both passes (the
+// compress pass is bandwidth-bound, the write pass latency-bound).
 constexpr int kCompressWaves = KVC_C128_COMPRESS_WAVES;
 constexpr int kWriteWaves = KVC_C128_WRITE_WAVES;
 
@@ -159,16 +160,17 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
 
   const uint32_t pid = blockIdx.x;
   if (pid >= n_plans) return;
-  const kvc_online_plan p = plans[pid];
-  if (p.ragged_id == 0xFFFFFFFFu) return;                       // padding entry
-  const uint32_t len = p.window_len;
-  const uint32_t pos127 = p.position & 127u;
-  if (len < 1u || len > pos127 + 1u || (int64_t)p.batch_id >= batch ||
-      (int64_t)p.ragged_id >= num_tokens || p.ragged_id + 1u < len)
+  // One 16-byte load for the whole plan entry.
+  const uint4 pv = reinterpret_cast<const uint4*>(plans)[pid];
+  const uint32_t ragged_id = pv.x, batch_id = pv.y, position = pv.z, len = pv.w;
+  if (ragged_id == 0xFFFFFFFFu) return;                         // padding entry
+  const uint32_t pos127 = position & 127u;
+  if (len < 1u || len > pos127 + 1u || (int64_t)batch_id >= batch ||
+      (int64_t)ragged_id >= num_tokens || ragged_id + 1u < len)
     return;                                                     // malformed: skip
   const uint32_t off = pos127 + 1u - len;                       // first chunk position
   const uint32_t end = pos127 + 1u;                             // one past the last
-  const int64_t seg0 = (int64_t)p.ragged_id - (int64_t)pos127;  // row of chunk position 0
+  const int64_t seg0 = (int64_t)ragged_id - (int64_t)pos127;    // row of chunk position 0
 
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -179,27 +181,25 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
 
   // Everything below depends only on the plan, so the token rows, the slot
   // indices and (for a segment that starts mid-chunk) the stored state are
-  // all requested before any of them is consumed.
-  float4 kv[kTokPerLane], u[kTokPerLane];
+  // all requested before any of them is consumed.  The row loads carry no
+  // branches: a position outside the segment re-reads the segment's last row
+  // (always in bounds) and is masked out afterwards.
+  float4 kv[kTokPerLane], sc[kTokPerLane], bi[kTokPerLane];
   bool valid[kTokPerLane];
 #pragma unroll
   for (int i = 0; i < kTokPerLane; ++i) {
     const uint32_t j = 2u * kTokPerLane * w + 2u * i + h;
     valid[i] = j >= off && j < end;
-    kv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    u[i] = make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
-    if (valid[i]) {
-      const int64_t r = seg0 + j;
-      kv[i] = load_stream4(in4 + r * 64 + q);
-      const float4 sc = load_stream4(in4 + r * 64 + 32 + q);
-      const float4 bi = ape4[j * 32 + q];
-      u[i] = make_float4(sc.x + bi.x, sc.y + bi.y, sc.z + bi.z, sc.w + bi.w);
-    }
+    const uint32_t jj = valid[i] ? j : pos127;
+    const int64_t r = seg0 + jj;
+    kv[i] = load_stream4(in4 + r * 64 + q);
+    sc[i] = load_stream4(in4 + r * 64 + 32 + q);
+    bi[i] = ape4[jj * 32 + q];
   }
   int32_t load_idx = -1;
-  if (off != 0u) load_idx = load_indices[p.batch_id];
+  if (off != 0u) load_idx = load_indices[batch_id];
   int32_t store_idx = -1;
-  if constexpr (kWrite) store_idx = indices[p.batch_id];
+  if constexpr (kWrite) store_idx = indices[batch_id];
   const bool lead = (w == 0 && h == 0);    // the 32 lanes that finish the plan
   const bool load_ok = load_idx >= 0 && (int64_t)load_idx < num_slots;
   float4 m1 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = m1, k1 = m1;
@@ -208,6 +208,14 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
     m1 = st[q];
     s1 = st[32 + q];
     k1 = st[64 + q];
+  }
+  float4 u[kTokPerLane];
+#pragma unroll
+  for (int i = 0; i < kTokPerLane; ++i) {
+    u[i] = valid[i] ? make_float4(sc[i].x + bi[i].x, sc[i].y + bi[i].y, sc[i].z + bi[i].z,
+                                  sc[i].w + bi[i].w)
+                    : make_float4(-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX);
+    if (!valid[i]) kv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
   float m[4] = {-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX};
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
     st[32 + q] = make_float4(D[0], D[1], D[2], D[3]);
     st[64 + q] = make_float4(K[0], K[1], K[2], K[3]);
   } else {
-    emit32<kQuant>(o, 0, (int64_t)p.ragged_id, q, K);
+    emit32<kQuant>(o, 0, (int64_t)ragged_id, q, K);
   }
 }
 

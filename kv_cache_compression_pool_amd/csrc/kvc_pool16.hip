@@ -20,7 +20,8 @@
 //     reduction plus one swizzle, and each lane stores 4 codes, so the 128-byte
 //     code vector leaves as one coalesced 32-lane store.
 //   * Slot rows are streamed with non-temporal loads; ape ([16,128] fp32) is
-//     staged once per workgroup in LDS after the row loads are in flight.
+//     staged once per workgroup in LDS (measured faster than per-lane reads
+//     of ape through the L1).
 //   * At most 128 VGPRs, so four waves per SIMD keep enough loads in flight.
 // The path is HBM-bound (about 8.3 KB read per 132 B written); there is no
 // dense contraction, so no MFMA.
@@ -56,6 +57,22 @@ __device__ __forceinline__ void widen8(uint4 w, float (&f)[8]) {
 __device__ __forceinline__ void stage_ape(float4* s_ape, const float* __restrict__ ape) {
   const float4* src = reinterpret_cast<const float4*>(ape);
   for (int i = threadIdx.x; i < kPool * 32; i += blockDim.x) s_ape[i] = src[i];
+  __syncthreads();
+}
+
+// The same in two steps for a block of kBlock threads (2 float4 each), so the
+// ape loads can be issued before the slot-row loads.
+struct ApeRegs {
+  float4 a, b;
+};
+__device__ __forceinline__ ApeRegs load_ape(const float* __restrict__ ape) {
+  static_assert(kPool * 32 == 2 * kBlock, "two float4 of ape per thread");
+  const float4* src = reinterpret_cast<const float4*>(ape);
+  return ApeRegs{src[threadIdx.x], src[threadIdx.x + kBlock]};
+}
+__device__ __forceinline__ void store_ape(float4* s_ape, const ApeRegs& r) {
+  s_ape[threadIdx.x] = r.a;
+  s_ape[threadIdx.x + kBlock] = r.b;
   __syncthreads();
 }
 
@@ -162,9 +179,13 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   // are always active.
   ok = ok && r0 >= 0 && r0 + kPool <= num_rows && dst >= 0 && dst < sink.rows;
 
+  // ape is requested first; the row loads are unconditional (a skipped pool
+  // reads rows 0..15, which exist: the launcher only runs with num_rows >=
+  // 16), so no branch forces the compiler to wait on them early.
+  const ApeRegs ape_regs = load_ape(ape);
   uint4 S[kHalf], K[kHalf];
-  if (ok) {
-    const int64_t row = r0 + kHalf * h;
+  {
+    const int64_t row = (ok ? r0 : 0) + kHalf * h;
     const uint4* sp = reinterpret_cast<const uint4*>(scores + row * score_stride) + c;
     const uint4* kp = reinterpret_cast<const uint4*>(keys + row * key_stride) + c;
     const int64_t ss = score_stride >> 3, ks = key_stride >> 3;
@@ -173,7 +194,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
 #pragma unroll
     for (int i = 0; i < kHalf; ++i) K[i] = load_stream(kp + i * ks);
   }
-  stage_ape(s_ape, ape);                         // overlaps the row loads
+  store_ape(s_ape, ape_regs);
   if (!ok) return;
 
   float x[8];
@@ -301,6 +322,7 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
                                  float* out_scale, int64_t out_rows, bool paged,
                                  const int64_t* loc, const uint8_t* write_mask, bool round_scale,
                                  float* dbg, hipStream_t stream) {
+  if (num_rows < kPool || n_pools <= 0) return hipSuccess;   // no pool can be complete
   const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
   const OutSink sink{out_fp8, out_scale, out_rows, paged};
