@@ -325,6 +325,15 @@ int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* 
 int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
                      void* stream);
 
+/* Streaming-read reference: reads `bytes` bytes at src (16-byte aligned,
+ * bytes a multiple of 16) with 128-bit non-temporal loads from 1024
+ * workgroups of 256 threads and writes one XOR word per thread to
+ * sink[0 .. 262143] (sink_words must be >= 262144).  It does no other work,
+ * so its time over a buffer is the practical HBM read rate the compression
+ * kernels are compared with. */
+int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

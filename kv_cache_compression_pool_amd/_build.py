@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkvc.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["kvc_api.cpp", "kvc_pool16.hip", "kvc_c128.hip"]
+SOURCES = ["kvc_api.cpp", "kvc_pool16.hip", "kvc_c128.hip", "kvc_diag.hip"]
 
 # Packed-fp32 instructions are disabled on purpose: plain fp32 VALU code only.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

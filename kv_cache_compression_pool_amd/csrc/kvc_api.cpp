@@ -448,4 +448,16 @@ int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int6
                     "kvc_diag_convert launch");
 }
 
+int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
+                         void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(KVC_ERR_SHAPE, "kvc_diag_stream_read: bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(KVC_ERR_NULL, "kvc_diag_stream_read: NULL pointer");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(KVC_ERR_SHAPE, "kvc_diag_stream_read: misaligned pointer");
+  if (sink_words < (int64_t)kvc::kStreamBlocks * 256)
+    return fail(KVC_ERR_SHAPE, "kvc_diag_stream_read: sink needs %d words", kvc::kStreamBlocks * 256);
+  return hip_status(kvc::launch_diag_stream_read(src, bytes, sink, (hipStream_t)stream),
+                    "kvc_diag_stream_read launch");
+}
+
 }  // extern "C"

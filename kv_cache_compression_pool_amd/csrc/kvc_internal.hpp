@@ -54,4 +54,8 @@ hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in,
 hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
                                hipStream_t stream);
 
+constexpr int kStreamBlocks = 1024;
+hipError_t launch_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                                   hipStream_t stream);
+
 }  // namespace kvc

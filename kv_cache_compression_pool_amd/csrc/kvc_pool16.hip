@@ -296,24 +296,6 @@ __global__ __launch_bounds__(256) void pool16_seed_kernel(uint16_t* __restrict__
   reinterpret_cast<uint4*>(rs)[c] = reinterpret_cast<const uint4*>(score + i * score_stride)[c];
 }
 
-__global__ __launch_bounds__(256) void diag_convert_kernel(const float* __restrict__ in,
-                                                           uint16_t* __restrict__ bf16_out,
-                                                           uint8_t* __restrict__ fp8_out,
-                                                           int64_t n) {
-  const int64_t i = 2 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
-  if (i >= n) return;
-  const float a = in[i], b = in[i + 1];
-  if (bf16_out) {
-    bf16_out[i] = bf16_bits(a);
-    bf16_out[i + 1] = bf16_bits(b);
-  }
-  if (fp8_out) {
-    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_fp8(a), clamp_fp8(b), 0, false);
-    fp8_out[i] = (uint8_t)(w & 0xff);
-    fp8_out[i + 1] = (uint8_t)((w >> 8) & 0xff);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const uint16_t* scores,
@@ -366,14 +348,6 @@ hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t
   const dim3 grid((unsigned)((n_tokens + 15) / 16));
   hipLaunchKernelGGL(pool16_seed_kernel, grid, dim3(256), 0, stream, ring, num_blocks, key,
                      key_stride, score, score_stride, tslot, n_tokens);
-  return hipGetLastError();
-}
-
-hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
-                               hipStream_t stream) {
-  const int64_t pairs = n / 2;
-  const dim3 grid((unsigned)((pairs + 255) / 256));
-  hipLaunchKernelGGL(diag_convert_kernel, grid, dim3(256), 0, stream, in, bf16_out, fp8_out, n);
   return hipGetLastError();
 }
 

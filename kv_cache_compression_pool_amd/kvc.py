@@ -32,7 +32,7 @@ EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_p
            "kvc_compress_decode_ring_paged", "kvc_seed_tail_ring",
            "kvc_c128_online_decode", "kvc_c128_online_decode_layers",
            "kvc_c128_online_decode_quant", "kvc_c128_online_prefill",
-           "kvc_c128_online_prefill_quant", "kvc_diag_convert")
+           "kvc_c128_online_prefill_quant", "kvc_diag_convert", "kvc_diag_stream_read")
 
 
 class KvcError(RuntimeError):
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.kvc_c128_online_prefill_quant.argtypes = [_p, _i64, _p, _p, _p, _i64, _p, _p, _p,
                                                     _i64, _p, _u32, _p, _u32, _i32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
+        L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
         _lib = L
@@ -423,6 +424,20 @@ def kvc_diag_convert(x, bf16_out=None, fp8_out=None, stream=None):
     _check(lib().kvc_diag_convert(
         _dptr(x, torch.float32, "x"), _dptr(bf16_out, torch.int16, "bf16_out", optional=True),
         _dptr(fp8_out, torch.uint8, "fp8_out", optional=True), x.numel(), _stream(stream)))
+
+
+STREAM_SINK_WORDS = 1024 * 256
+
+
+def kvc_diag_stream_read(src, sink, stream=None):
+    """Plain streaming read of a device tensor's bytes (see kvc.h); sink is a
+    device int32/uint32 tensor of at least STREAM_SINK_WORDS entries."""
+    nbytes = src.numel() * src.element_size()
+    _need(src.is_cuda and src.is_contiguous(), "src must be a contiguous device tensor")
+    _need(sink.is_cuda and sink.element_size() == 4 and sink.numel() >= STREAM_SINK_WORDS,
+          "sink must hold STREAM_SINK_WORDS 4-byte words")
+    _check(lib().kvc_diag_stream_read(src.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(),
+                                      sink.numel(), _stream(stream)))
 
 
 def plans_to_device(plan: np.ndarray, device="cuda"):

@@ -623,3 +623,21 @@ def test_c128_prefill_quant_epilogue():
     check_codes(gc[r], ref_c, "c128 prefill quant")
     check_scales(gs[r], ref_s, True, "c128 prefill quant")
     note(f"c128 prefill quant: {r.sum()} vectors, bf16-boundary vectors {flips}")
+
+
+def test_diag_stream_read_reads_every_word():
+    g = np.random.default_rng(30)
+    words = g.integers(0, 2**32, size=(3 * 1024 * 256 * 4 + 4 * 37), dtype=np.uint64).astype(np.uint32)
+    src = dev(words.view(np.int32))
+    sink = torch.zeros(kvc.kvc.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
+    kvc.kvc.kvc_diag_stream_read(src, sink)
+    torch.cuda.synchronize()
+    n16 = words.size // 4
+    quads = words.reshape(n16, 4)
+    x = np.bitwise_xor.reduce(quads, axis=1)
+    threads = kvc.kvc.STREAM_SINK_WORDS
+    exp = np.zeros(threads, np.uint32)
+    for t0 in range(0, n16, threads):
+        blk = x[t0:t0 + threads]
+        exp[:blk.size] ^= blk
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), exp)
