@@ -30,7 +30,10 @@ namespace kvc {
 namespace {
 
 // ------------------------------------------------------------------ decode
-constexpr int kDecodeReqPerBlock = 2;
+#ifndef KVC_C128_DECODE_REQ_PER_BLOCK
+#define KVC_C128_DECODE_REQ_PER_BLOCK 2
+#endif
+constexpr int kDecodeReqPerBlock = KVC_C128_DECODE_REQ_PER_BLOCK;
 
 // Where emitted (chunk-closing) vectors go: fp32 rows, or e4m3 codes plus a
 // per-vector scale after the bf16 / rotation / quantisation epilogue.
@@ -67,7 +70,7 @@ __device__ __forceinline__ void emit32(const EmitSink& o, int64_t layer, int64_t
 // output and ape advance by their layer strides; indices and lengths are
 // shared by all layers).
 template <bool kQuant>
-__global__ __launch_bounds__(64) void c128_decode_kernel(
+__global__ __launch_bounds__(32 * kDecodeReqPerBlock) void c128_decode_kernel(
     float* __restrict__ state, int64_t state_ls, int64_t num_slots, const float* __restrict__ in,
     int64_t in_ls, EmitSink o, const float* __restrict__ ape, int64_t ape_ls,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ seq_lens, int64_t batch) {
@@ -315,10 +318,10 @@ hipError_t launch_c128_decode(float* state, int64_t state_ls, int64_t num_slots,
                   (unsigned)num_layers);
   const EmitSink o{out, codes, scales, out_ls, batch * 128, batch, round_scale};
   if (codes)
-    hipLaunchKernelGGL((c128_decode_kernel<true>), grid, dim3(64), 0, stream, state, state_ls,
+    hipLaunchKernelGGL((c128_decode_kernel<true>), grid, dim3(32 * kDecodeReqPerBlock), 0, stream, state, state_ls,
                        num_slots, in, in_ls, o, ape, ape_ls, indices, seq_lens, batch);
   else
-    hipLaunchKernelGGL((c128_decode_kernel<false>), grid, dim3(64), 0, stream, state, state_ls,
+    hipLaunchKernelGGL((c128_decode_kernel<false>), grid, dim3(32 * kDecodeReqPerBlock), 0, stream, state, state_ls,
                        num_slots, in, in_ls, o, ape, ape_ls, indices, seq_lens, batch);
   return hipGetLastError();
 }

@@ -271,6 +271,125 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
   }
 }
 
+// Ring decode for short verify batches (next_n <= kMaxN).  Same result as
+// pool16_ring_kernel, organised for latency:
+//  * every token's maps and key / score rows are requested up front, in the
+//    same round trip as the ape table;
+//  * the loop runs over completions, not tokens.  Before completion t* reads
+//    its ring block, the stashes of tokens [done, t*) are stored from the
+//    lanes that read those slots back, which keeps the ordered semantics.
+//    Both 32-lane halves of a wave run the softmax / rotate / quantise body
+//    together even when they complete at different tokens.
+template <bool kRoundScale, int kMaxN>
+__global__ __launch_bounds__(kBlock) void pool16_ring_prefetch_kernel(
+    uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
+    const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
+    const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
+    const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
+    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink) {
+  static_assert(kMaxN <= 32, "completion mask is 32 bits");
+  __shared__ float4 s_ape[kPool * 32];
+  const int c = threadIdx.x & 15;
+  const int h = (threadIdx.x >> 4) & 1;
+  const int64_t r = (int64_t)blockIdx.x * kPoolsPerBlock + (threadIdx.x >> 5);
+  const int64_t rr = r < num_requests ? r : 0;   // rows past the batch read request 0, stop below
+
+  const ApeRegs ape_regs = load_ape(ape);
+  int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
+  uint4 kv[kMaxN], sv[kMaxN];
+#pragma unroll
+  for (int t = 0; t < kMaxN; ++t) {
+    const int tt = t < next_n ? t : next_n - 1;   // in bounds; entries t >= next_n are unused
+    const int64_t e = rr * next_n + tt;
+    loc[t] = slot_mapping[e];
+    pos[t] = positions[e];
+    ts[t] = tail_slot[e];
+    kv[t] = reinterpret_cast<const uint4*>(key + rr * key_sb + tt * key_st)[c];
+    sv[t] = reinterpret_cast<const uint4*>(score + rr * score_sb + tt * score_st)[c];
+  }
+  // Pin the token loads above the barrier: otherwise they are sunk below it
+  // and wait for the ape round trip instead of sharing it.
+#pragma unroll
+  for (int t = 0; t < kMaxN; ++t)
+    asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]), "v"(kv[t].x), "v"(kv[t].y),
+                 "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x), "v"(sv[t].y), "v"(sv[t].z),
+                 "v"(sv[t].w));
+  store_ape(s_ape, ape_regs);
+  if (r >= num_requests) return;
+
+  // Per-token decisions: ring block, completion and stash flags.
+  int32_t blk[kMaxN];
+  uint32_t completes = 0, stashes = 0;
+#pragma unroll
+  for (int t = 0; t < kMaxN; ++t) {
+    const int64_t b = (int64_t)(ts[t] > 0 ? ts[t] : 0) / kPool;
+    blk[t] = (int32_t)b;   // ts is int32, so the block index fits
+    if (t >= next_n || b >= num_blocks) continue;
+    if (loc[t] >= 0 && pos[t] >= 0 && (pos[t] & (kPool - 1)) == kPool - 1) completes |= 1u << t;
+    // A row stores the stashes of the slots it later reads (slots 8h..8h+7).
+    if (pos[t] >= 0 && ts[t] >= 0 && ((pos[t] & (kPool - 1)) >> 3) == h) stashes |= 1u << t;
+  }
+
+  auto stash_range = [&](uint32_t mask) {
+#pragma unroll
+    for (int t = 0; t < kMaxN; ++t) {
+      if (mask & (1u << t)) {
+        uint16_t* ring_k = ring + (int64_t)blk[t] * (2 * kPool * 128);
+        const int slot = pos[t] & (kPool - 1);
+        reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = kv[t];
+        reinterpret_cast<uint4*>(ring_k + kPool * 128 + slot * 128)[c] = sv[t];
+      }
+    }
+  };
+
+  uint32_t done = 0;   // tokens whose stash has been stored: bits below the cursor
+  while (completes) {
+    const int t1 = __builtin_ctz(completes);
+    completes &= completes - 1;
+    const uint32_t before = (1u << t1) - 1;
+    stash_range(stashes & before & ~done);
+    done = before;
+    int32_t b1 = 0, l1 = 0;
+    uint4 k1 = make_uint4(0, 0, 0, 0), s1 = k1;
+#pragma unroll
+    for (int t = 0; t < kMaxN; ++t) {
+      if (t == t1) {
+        b1 = blk[t];
+        l1 = loc[t];
+        k1 = kv[t];
+        s1 = sv[t];
+      }
+    }
+    const uint16_t* ring_k = ring + (int64_t)b1 * (2 * kPool * 128);
+    const uint16_t* ring_s = ring_k + kPool * 128;
+    uint4 S[kHalf], K[kHalf];
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) {
+      const int slot = kHalf * h + i;
+      S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
+      K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
+    }
+    // All 16 row loads in flight at once (the scheduler otherwise splits them
+    // into two round trips to save registers).
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i)
+      asm volatile("" ::"v"(S[i].x), "v"(S[i].y), "v"(S[i].z), "v"(S[i].w), "v"(K[i].x),
+                   "v"(K[i].y), "v"(K[i].z), "v"(K[i].w));
+    // Slot 15 is the completing token itself: row 1 replaces what it read
+    // there (a load kept unconditional so the row loads stay branch-free).
+    if (h) {
+      S[kHalf - 1] = s1;
+      K[kHalf - 1] = k1;
+    }
+    float x[8];
+    pool_mean(S, K, s_ape, c, h, x);
+    float scale;
+    const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
+    if (l1 < sink.rows) sink.store(l1, c, h, codes, scale);
+  }
+  stash_range(stashes & ~done);
+}
+
 // Tail-ring seeding: one 16-lane row per token copies its 256 B key and
 // score rows when it is among its request's last 16 tokens.
 __global__ __launch_bounds__(256) void pool16_seed_kernel(uint16_t* __restrict__ ring,
@@ -331,14 +450,21 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
   const dim3 grid((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
   const OutSink sink{out_fp8, out_scale, out_rows, paged};
-  if (round_scale)
-    hipLaunchKernelGGL((pool16_ring_kernel<true>), grid, block, 0, stream, ring, num_blocks,
-                       tail_slot, key, key_sb, key_st, score, score_sb, score_st, ape,
-                       slot_mapping, positions, num_requests, next_n, sink);
-  else
-    hipLaunchKernelGGL((pool16_ring_kernel<false>), grid, block, 0, stream, ring, num_blocks,
-                       tail_slot, key, key_sb, key_st, score, score_sb, score_st, ape,
-                       slot_mapping, positions, num_requests, next_n, sink);
+#define KVC_RING(KERNEL)                                                                      \
+  hipLaunchKernelGGL(KERNEL, grid, block, 0, stream, ring, num_blocks, tail_slot, key, key_sb, \
+                     key_st, score, score_sb, score_st, ape, slot_mapping, positions,           \
+                     num_requests, next_n, sink)
+  if (next_n <= 4) {
+    if (round_scale) KVC_RING((pool16_ring_prefetch_kernel<true, 4>));
+    else KVC_RING((pool16_ring_prefetch_kernel<false, 4>));
+  } else if (next_n <= 8) {
+    if (round_scale) KVC_RING((pool16_ring_prefetch_kernel<true, 8>));
+    else KVC_RING((pool16_ring_prefetch_kernel<false, 8>));
+  } else {
+    if (round_scale) KVC_RING((pool16_ring_kernel<true>));
+    else KVC_RING((pool16_ring_kernel<false>));
+  }
+#undef KVC_RING
   return hipGetLastError();
 }
 
