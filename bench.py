@@ -253,9 +253,23 @@ def bench_c128_prefill(args, torch, kvc, synth, stream):
 
     steps = max(args.steps // 2, 10)
     total_ms, ev_ms, host = timed(step, steps, max(args.warmup, 3), torch, stream)
+
+    # The same plans as single-launch work items.
+    items = kvc.kvc_c128_plan_prefill_fused(d["seq_lens"], d["extend_lens"], N)
+    items_t = kvc.items_to_device(items)
+    paired = int(sum(1 for it in items if it["compress"]["ragged_id"] != kvc.PLAN_SENTINEL
+                     and it["write"]["ragged_id"] != kvc.PLAN_SENTINEL))
+
+    def step_fused(i):
+        r = i % R
+        kvc.kvc_c128_online_prefill_fused(states[r], ins[r], ape, idx, items_t, items.size,
+                                          out=outs[r])
+
+    f_total, f_ev, _ = timed(step_fused, steps, max(args.warmup, 3), torch, stream)
     return dict(tokens=N, vectors=int(cp.size), write_plans=int(wp.size), replicas=R,
                 total_ms=total_ms, steps=steps, ev_ms=ev_ms, host_s=host,
-                alg_bytes=alg)
+                alg_bytes=alg, items=int(items.size), paired=paired, fused_total_ms=f_total,
+                fused_ev_ms=f_ev)
 
 
 # ------------------------------------------------------------------ pool-16 ring decode
@@ -414,6 +428,12 @@ def main():
             "call_us": round(c5["ev_ms"] * 1e3, 3), "bytes_per_call": c5["alg_bytes"],
             "hbm_gbs": round(g5, 1), "hbm_frac": round(g5 / PEAK_HBM_GBS, 4),
             "input_replicas": c5["replicas"]}
+        g5f = gbs(c5["alg_bytes"], c5["fused_ev_ms"])
+        line["c128_prefill"]["single_launch"] = {
+            "items": c5["items"], "paired_items": c5["paired"],
+            "vectors_per_s": round(c5["vectors"] * c5["steps"] / (c5["fused_total_ms"] * 1e-3), 1),
+            "call_us": round(c5["fused_ev_ms"] * 1e3, 3), "hbm_gbs": round(g5f, 1),
+            "hbm_frac": round(g5f / PEAK_HBM_GBS, 4)}
         log("pool-16 ring decode")
         c3 = bench_ring(args, torch, kvc, synth, stream)
         g3 = gbs(c3["alg_bytes"], c3["ev_ms"])

@@ -69,6 +69,16 @@ typedef struct kvc_online_plan {
     uint32_t window_len;
 } kvc_online_plan;
 
+/* Work item of the single-launch pool-128 prefill: the plans one workgroup
+ * runs, compress first.  Either plan may be padding (all fields 0xFFFFFFFF).
+ * Both are set only when they belong to one request whose first segment
+ * starts mid-chunk and closes it (reading the stored state) and whose
+ * trailing segment is a write plan (replacing that state). */
+typedef struct kvc_online_item {
+    kvc_online_plan compress;
+    kvc_online_plan write;
+} kvc_online_item;
+
 /* Library version (major*10000 + minor*100 + patch). */
 int kvc_version(void);
 
@@ -114,6 +124,23 @@ int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, i
                           int64_t num_tokens, kvc_online_plan* compress_plan,
                           kvc_online_plan* write_plan, int pad_to_capacity,
                           uint32_t* n_compress, uint32_t* n_write);
+
+/* The plans of kvc_c128_plan_prefill, arranged as work items for
+ * kvc_c128_online_prefill_fused.  Same segments, same plan entries; a
+ * request's first compress plan is paired with its write plan when the
+ * former starts mid-chunk (it reads the state row that the write plan
+ * replaces), every other plan gets an item of its own.  Order: paired items,
+ * then compress-only items, then write-only items, each in request order
+ * (the longest work first).
+ *   items            host [num_tokens] (capacity: each item covers at least
+ *                    one token)
+ *   pad_to_capacity  nonzero: fill with padding items up to num_tokens and
+ *                    report num_tokens.
+ *   n_items          host, out
+ * Errors: as kvc_c128_plan_prefill. */
+int kvc_c128_plan_prefill_fused(const int64_t* seq_lens, const int64_t* extend_lens,
+                                int64_t batch, int64_t num_tokens, kvc_online_item* items,
+                                int pad_to_capacity, uint32_t* n_items);
 
 /* ------------------------------------------------------------------------
  * Device entry points.
@@ -312,6 +339,33 @@ int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* 
                                   const kvc_online_plan* compress_plan, uint32_t n_compress,
                                   const kvc_online_plan* write_plan, uint32_t n_write,
                                   int round_scale, void* stream);
+
+/* Pool-128 online ragged prefill in ONE launch (c128_online.cuh page,
+ * flash_c128_online_prefill; same results as kvc_c128_online_prefill with
+ * load_indices = indices).  The page orders state reads before state writes
+ * with two launches; here each work item from kvc_c128_plan_prefill_fused
+ * carries the only read that can conflict with its write, so one workgroup
+ * does both in order and the second launch (latency-bound, a few
+ * microseconds) disappears.  Requires the state rows indices[b] of the
+ * requests in the call to be distinct (as the write pass of the two-launch
+ * form already does).
+ *   state, kv_score_in, num_tokens, ape, indices, batch: as
+ *                  kvc_c128_online_prefill (reads and writes use indices)
+ *   out            device fp32 [num_tokens, 128], or NULL when out_fp8 is
+ *                  given; chunk-closing rows only
+ *   out_fp8, out_scale  device uint8 [num_tokens, 128] and fp32
+ *                  [num_tokens] for the rotate/quantise epilogue (as
+ *                  kvc_c128_online_prefill_quant), or both NULL
+ *   round_scale    used with out_fp8
+ *   items          device [n_items], 16-byte aligned; padding items and
+ *                  malformed plans are skipped as in kvc_c128_online_prefill
+ * Exactly one of out and out_fp8 (with out_scale) must be given.
+ * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_HIP. */
+int kvc_c128_online_prefill_fused(float* state, int64_t num_slots, const float* kv_score_in,
+                                  float* out, uint8_t* out_fp8, float* out_scale,
+                                  int round_scale, int64_t num_tokens, const float* ape,
+                                  const int32_t* indices, int64_t batch,
+                                  const kvc_online_item* items, uint32_t n_items, void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostics.

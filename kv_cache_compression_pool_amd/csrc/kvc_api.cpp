@@ -81,29 +81,23 @@ int kvc_plan_pool_prefill(const int64_t* seq_lens, int64_t batch, int pool_size,
   return ok();
 }
 
-int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, int64_t batch,
-                          int64_t num_tokens, kvc_online_plan* compress_plan,
-                          kvc_online_plan* write_plan, int pad_to_capacity,
-                          uint32_t* n_compress, uint32_t* n_write) {
-  if (!n_compress || !n_write) return fail(KVC_ERR_NULL, "kvc_c128_plan_prefill: NULL count");
-  *n_compress = *n_write = 0;
-  if (batch < 0 || num_tokens < 0)
-    return fail(KVC_ERR_SHAPE, "kvc_c128_plan_prefill: negative size");
-  if (num_tokens > (int64_t)0xfffffffeLL)
-    return fail(KVC_ERR_SHAPE, "kvc_c128_plan_prefill: num_tokens exceeds 2^32-2");
-  if (batch > 0 && (!seq_lens || !extend_lens))
-    return fail(KVC_ERR_NULL, "kvc_c128_plan_prefill: NULL lengths");
-  if (num_tokens > 0 && (!compress_plan || !write_plan))
-    return fail(KVC_ERR_NULL, "kvc_c128_plan_prefill: NULL plan buffer");
+}  // extern "C"
+
+namespace {
+
+// Cuts every request's extend range at multiples of 128 and hands each
+// segment to emit(b, plan, closes_chunk, first_of_request) in request order.
+// Returns KVC_OK, the first error emit returns, or a planner error.
+template <class Emit>
+int walk_c128_segments(const char* fn, const int64_t* seq_lens, const int64_t* extend_lens,
+                       int64_t batch, int64_t num_tokens, Emit&& emit) {
   uint64_t row = 0;
-  uint32_t nc = 0, nw = 0;
   for (int64_t b = 0; b < batch; ++b) {
     const int64_t L = seq_lens[b], E = extend_lens[b];
     if (!(E > 0 && E <= L))
-      return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: request %lld extend %lld not in (0, %lld]",
+      return fail(KVC_ERR_PLAN, "%s: request %lld extend %lld not in (0, %lld]", fn,
                   (long long)b, (long long)E, (long long)L);
-    if (L > (int64_t)0xffffffffLL)
-      return fail(KVC_ERR_SHAPE, "kvc_c128_plan_prefill: seq_len exceeds 2^32-1");
+    if (L > (int64_t)0xffffffffLL) return fail(KVC_ERR_SHAPE, "%s: seq_len exceeds 2^32-1", fn);
     const int64_t prefix = L - E;
     int64_t pos = prefix;
     while (pos < L) {
@@ -114,30 +108,124 @@ int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, i
       p.batch_id = (uint32_t)b;
       p.position = (uint32_t)(seg_end - 1);
       p.window_len = (uint32_t)(seg_end - pos);
-      if (seg_end == chunk_end) {
-        if ((int64_t)nc >= num_tokens)
-          return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: compress plans exceed capacity");
-        compress_plan[nc++] = p;
-      } else {
-        if ((int64_t)nw >= num_tokens)
-          return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: write plans exceed capacity");
-        write_plan[nw++] = p;
-      }
+      const int rc = emit(b, p, seg_end == chunk_end, pos == prefix);
+      if (rc != KVC_OK) return rc;
       pos = seg_end;
     }
     row += (uint64_t)E;
   }
   if (row != (uint64_t)num_tokens)
-    return fail(KVC_ERR_PLAN, "kvc_c128_plan_prefill: extends sum to %llu, num_tokens %lld",
+    return fail(KVC_ERR_PLAN, "%s: extends sum to %llu, num_tokens %lld", fn,
                 (unsigned long long)row, (long long)num_tokens);
+  return KVC_OK;
+}
+
+int check_plan_args(const char* fn, const int64_t* seq_lens, const int64_t* extend_lens,
+                    int64_t batch, int64_t num_tokens) {
+  if (batch < 0 || num_tokens < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (num_tokens > (int64_t)0xfffffffeLL)
+    return fail(KVC_ERR_SHAPE, "%s: num_tokens exceeds 2^32-2", fn);
+  if (batch > 0 && (!seq_lens || !extend_lens)) return fail(KVC_ERR_NULL, "%s: NULL lengths", fn);
+  return KVC_OK;
+}
+
+constexpr kvc_online_plan kPadPlan = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+
+}  // namespace
+
+extern "C" {
+
+int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, int64_t batch,
+                          int64_t num_tokens, kvc_online_plan* compress_plan,
+                          kvc_online_plan* write_plan, int pad_to_capacity,
+                          uint32_t* n_compress, uint32_t* n_write) {
+  const char* fn = "kvc_c128_plan_prefill";
+  if (!n_compress || !n_write) return fail(KVC_ERR_NULL, "%s: NULL count", fn);
+  *n_compress = *n_write = 0;
+  int rc = check_plan_args(fn, seq_lens, extend_lens, batch, num_tokens);
+  if (rc != KVC_OK) return rc;
+  if (num_tokens > 0 && (!compress_plan || !write_plan))
+    return fail(KVC_ERR_NULL, "%s: NULL plan buffer", fn);
+  uint32_t nc = 0, nw = 0;
+  rc = walk_c128_segments(fn, seq_lens, extend_lens, batch, num_tokens,
+                          [&](int64_t, const kvc_online_plan& p, bool closes, bool) {
+                            uint32_t& n = closes ? nc : nw;
+                            if ((int64_t)n >= num_tokens)
+                              return fail(KVC_ERR_PLAN, "%s: %s plans exceed capacity", fn,
+                                          closes ? "compress" : "write");
+                            (closes ? compress_plan : write_plan)[n++] = p;
+                            return (int)KVC_OK;
+                          });
+  if (rc != KVC_OK) return rc;
   if (pad_to_capacity) {
-    const kvc_online_plan pad = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-    for (int64_t i = nc; i < num_tokens; ++i) compress_plan[i] = pad;
-    for (int64_t i = nw; i < num_tokens; ++i) write_plan[i] = pad;
+    for (int64_t i = nc; i < num_tokens; ++i) compress_plan[i] = kPadPlan;
+    for (int64_t i = nw; i < num_tokens; ++i) write_plan[i] = kPadPlan;
     nc = nw = (uint32_t)num_tokens;
   }
   *n_compress = nc;
   *n_write = nw;
+  return ok();
+}
+
+int kvc_c128_plan_prefill_fused(const int64_t* seq_lens, const int64_t* extend_lens,
+                                int64_t batch, int64_t num_tokens, kvc_online_item* items,
+                                int pad_to_capacity, uint32_t* n_items) {
+  const char* fn = "kvc_c128_plan_prefill_fused";
+  if (!n_items) return fail(KVC_ERR_NULL, "%s: NULL count", fn);
+  *n_items = 0;
+  int rc = check_plan_args(fn, seq_lens, extend_lens, batch, num_tokens);
+  if (rc != KVC_OK) return rc;
+  if (num_tokens > 0 && !items) return fail(KVC_ERR_NULL, "%s: NULL item buffer", fn);
+  // A request pairs its first compress plan with its write plan when the
+  // former starts mid-chunk; both conditions are fixed by its lengths.
+  auto paired = [&](int64_t b) {
+    const int64_t L = seq_lens[b], prefix = L - extend_lens[b];
+    return prefix % 128 != 0 && (prefix / 128 + 1) * 128 < L && L % 128 != 0;
+  };
+  // Pass 1: validate and count each kind of item.
+  uint64_t n_pair = 0, n_conly = 0, n_wonly = 0;
+  rc = walk_c128_segments(fn, seq_lens, extend_lens, batch, num_tokens,
+                          [&](int64_t b, const kvc_online_plan&, bool closes, bool first) {
+                            const bool pr = paired(b);
+                            if (closes && pr && first) ++n_pair;
+                            else if (closes) ++n_conly;
+                            else if (!pr) ++n_wonly;
+                            return (int)KVC_OK;
+                          });
+  if (rc != KVC_OK) return rc;
+  const uint64_t total = n_pair + n_conly + n_wonly;   // <= num_tokens: >= 1 token per item
+  if (total > (uint64_t)num_tokens) return fail(KVC_ERR_PLAN, "%s: items exceed capacity", fn);
+  // Pass 2: place the items.  The compress half of a paired item is written
+  // when its first segment is seen, the write half when the trailing one is.
+  uint64_t i_pair = 0, i_conly = n_pair, i_wonly = n_pair + n_conly;
+  int64_t cur_b = -1;
+  uint64_t cur_pair = 0;
+  rc = walk_c128_segments(fn, seq_lens, extend_lens, batch, num_tokens,
+                          [&](int64_t b, const kvc_online_plan& p, bool closes, bool first) {
+                            const bool pr = paired(b);
+                            if (closes && pr && first) {
+                              cur_b = b;
+                              cur_pair = i_pair++;
+                              items[cur_pair].compress = p;
+                              items[cur_pair].write = kPadPlan;
+                            } else if (closes) {
+                              items[i_conly].compress = p;
+                              items[i_conly++].write = kPadPlan;
+                            } else if (pr && cur_b == b) {
+                              items[cur_pair].write = p;
+                            } else {
+                              items[i_wonly].compress = kPadPlan;
+                              items[i_wonly++].write = p;
+                            }
+                            return (int)KVC_OK;
+                          });
+  if (rc != KVC_OK) return rc;
+  uint64_t n = total;
+  if (pad_to_capacity) {
+    for (int64_t i = (int64_t)total; i < num_tokens; ++i) items[i] = {kPadPlan, kPadPlan};
+    n = (uint64_t)num_tokens;
+  }
+  *n_items = (uint32_t)n;
   return ok();
 }
 
@@ -436,6 +524,32 @@ int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* 
                                              n_compress, write_plan, n_write,
                                              (hipStream_t)stream),
                     "kvc_c128_online_prefill_quant launch");
+}
+
+int kvc_c128_online_prefill_fused(float* state, int64_t num_slots, const float* kv_score_in,
+                                  float* out, uint8_t* out_fp8, float* out_scale,
+                                  int round_scale, int64_t num_tokens, const float* ape,
+                                  const int32_t* indices, int64_t batch,
+                                  const kvc_online_item* items, uint32_t n_items, void* stream) {
+  const char* fn = "kvc_c128_online_prefill_fused";
+  if (batch < 0 || num_slots < 0 || num_tokens < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (n_items == 0) return ok();
+  if (!items) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  int rc = check_prefill(fn, state, num_slots, kv_score_in, num_tokens, ape, indices, batch,
+                         nullptr, 0, nullptr, 0);
+  if (rc != KVC_OK) return rc;
+  if (!aligned(items, 16)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  const bool quant = out_fp8 != nullptr;
+  if (quant ? (out != nullptr || !out_scale) : (!out || out_scale != nullptr))
+    return fail(KVC_ERR_NULL, "%s: give either out or out_fp8 with out_scale", fn);
+  if ((out && !aligned(out, 16)) || (out_fp8 && !aligned(out_fp8, 4)) ||
+      (out_scale && !aligned(out_scale, 4)))
+    return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  return hip_status(kvc::launch_c128_prefill_fused(state, num_slots, kv_score_in, out, out_fp8,
+                                                   out_scale, round_scale != 0, num_tokens, ape,
+                                                   indices, batch, items, n_items,
+                                                   (hipStream_t)stream),
+                    "kvc_c128_online_prefill_fused launch");
 }
 
 // --------------------------------------------------------------- diagnostics

@@ -152,19 +152,24 @@ __device__ __forceinline__ float4 load_stream4(const float4* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-template <bool kWrite, int kWaves, bool kQuant>
-__global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
-    float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
-    EmitSink o, int64_t num_tokens, const float* __restrict__ ape,
-    const int32_t* __restrict__ indices, const int32_t* __restrict__ load_indices, int64_t batch,
-    const kvc_online_plan* __restrict__ plans, uint32_t n_plans) {
-  constexpr int kTokPerLane = 128 / (2 * kWaves);   // chunk positions per lane
-  __shared__ float s_m[kWaves][128], s_d[kWaves][128], s_a[kWaves][128];
+// LDS partials of one plan: (max, sum, weighted sum) per wave and channel.
+template <int kWaves>
+struct PlanLds {
+  float m[kWaves][128], d[kWaves][128], a[kWaves][128];
+};
 
-  const uint32_t pid = blockIdx.x;
-  if (pid >= n_plans) return;
-  // One 16-byte load for the whole plan entry.
-  const uint4 pv = reinterpret_cast<const uint4*>(plans)[pid];
+// One plan (16-byte entry pv) processed by the whole workgroup.  Returns
+// early for padding or malformed entries (uniformly, before the barrier) and
+// for the lanes that do not finish the plan (after it).  kWrite: store the
+// (max, sum, kv) state to indices[b]; otherwise emit the normalised vector to
+// row ragged_id.
+template <bool kWrite, int kWaves, bool kQuant>
+__device__ __forceinline__ void prefill_plan(
+    const uint4 pv, float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
+    const EmitSink& o, int64_t num_tokens, const float* __restrict__ ape,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ load_indices, int64_t batch,
+    PlanLds<kWaves>& lds) {
+  constexpr int kTokPerLane = 128 / (2 * kWaves);   // chunk positions per lane
   const uint32_t ragged_id = pv.x, batch_id = pv.y, position = pv.z, len = pv.w;
   if (ragged_id == 0xFFFFFFFFu) return;                         // padding entry
   const uint32_t pos127 = position & 127u;
@@ -253,9 +258,9 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
   if (h == 0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      s_m[w][4 * q + k] = m[k];
-      s_d[w][4 * q + k] = d[k];
-      s_a[w][4 * q + k] = a[k];
+      lds.m[w][4 * q + k] = m[k];
+      lds.d[w][4 * q + k] = d[k];
+      lds.a[w][4 * q + k] = a[k];
     }
   }
   __syncthreads();
@@ -268,13 +273,14 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
   float M[4], D[4], A[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    M[k] = s_m[0][4 * q + k]; D[k] = s_d[0][4 * q + k]; A[k] = s_a[0][4 * q + k];
+    M[k] = lds.m[0][4 * q + k]; D[k] = lds.d[0][4 * q + k]; A[k] = lds.a[0][4 * q + k];
   }
 #pragma unroll
   for (int ww = 1; ww < kWaves; ++ww)
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      merge_partial(M[k], D[k], A[k], s_m[ww][4 * q + k], s_d[ww][4 * q + k], s_a[ww][4 * q + k]);
+      merge_partial(M[k], D[k], A[k], lds.m[ww][4 * q + k], lds.d[ww][4 * q + k],
+                    lds.a[ww][4 * q + k]);
 
   float K[4];
   if (off != 0u) {
@@ -305,6 +311,46 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
   } else {
     emit32<kQuant>(o, 0, (int64_t)ragged_id, q, K);
   }
+}
+
+// One workgroup per plan of one list (compress or write pass).
+template <bool kWrite, int kWaves, bool kQuant>
+__global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
+    float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
+    EmitSink o, int64_t num_tokens, const float* __restrict__ ape,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ load_indices, int64_t batch,
+    const kvc_online_plan* __restrict__ plans, uint32_t n_plans) {
+  __shared__ PlanLds<kWaves> lds;
+  if (blockIdx.x >= n_plans) return;
+  // One 16-byte load for the whole plan entry.
+  const uint4 pv = reinterpret_cast<const uint4*>(plans)[blockIdx.x];
+  prefill_plan<kWrite, kWaves, kQuant>(pv, state, num_slots, in, o, num_tokens, ape, indices,
+                                       load_indices, batch, lds);
+}
+
+// Single-launch prefill over work items {compress plan, write plan}.  An item
+// that holds both belongs to one request whose first (mid-chunk) compress
+// segment reads the stored state that its write plan replaces: the workgroup
+// finishes the compress plan, whose state loads were consumed before the
+// barrier, and only then stores the new state.  No other item of the call
+// touches that request's state row, so no ordering between workgroups is
+// needed.
+template <bool kQuant>
+__global__ __launch_bounds__(64 * kCompressWaves) void c128_prefill_fused_kernel(
+    float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
+    EmitSink o, int64_t num_tokens, const float* __restrict__ ape,
+    const int32_t* __restrict__ indices, int64_t batch,
+    const kvc_online_item* __restrict__ items, uint32_t n_items) {
+  __shared__ PlanLds<kCompressWaves> lds;
+  if (blockIdx.x >= n_items) return;
+  const uint4* it = reinterpret_cast<const uint4*>(items) + 2 * (size_t)blockIdx.x;
+  const uint4 pc = it[0];
+  const uint4 pw = it[1];
+  prefill_plan<false, kCompressWaves, kQuant>(pc, state, num_slots, in, o, num_tokens, ape,
+                                              indices, indices, batch, lds);
+  __syncthreads();   // the LDS partials are reused by the write plan
+  prefill_plan<true, kCompressWaves, false>(pw, state, num_slots, in, o, num_tokens, ape, indices,
+                                            indices, batch, lds);
 }
 
 }  // namespace
@@ -355,6 +401,23 @@ hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in,
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+hipError_t launch_c128_prefill_fused(float* state, int64_t num_slots, const float* in, float* out,
+                                     uint8_t* codes, float* scales, bool round_scale,
+                                     int64_t num_tokens, const float* ape, const int32_t* indices,
+                                     int64_t batch, const kvc_online_item* items,
+                                     uint32_t n_items, hipStream_t stream) {
+  const EmitSink o{out, codes, scales, 0, 0, 0, round_scale};
+  if (codes)
+    hipLaunchKernelGGL((c128_prefill_fused_kernel<true>), dim3(n_items),
+                       dim3(64 * kCompressWaves), 0, stream, state, num_slots, in, o, num_tokens,
+                       ape, indices, batch, items, n_items);
+  else
+    hipLaunchKernelGGL((c128_prefill_fused_kernel<false>), dim3(n_items),
+                       dim3(64 * kCompressWaves), 0, stream, state, num_slots, in, o, num_tokens,
+                       ape, indices, batch, items, n_items);
+  return hipGetLastError();
 }
 
 }  // namespace kvc

@@ -26,13 +26,15 @@ KVC_ERR_HIP = -5
 PLAN_DTYPE = np.dtype([("ragged_id", "<u4"), ("batch_id", "<u4"), ("position", "<u4"),
                        ("window_len", "<u4")])
 PLAN_SENTINEL = 0xFFFFFFFF
+ITEM_DTYPE = np.dtype([("compress", PLAN_DTYPE), ("write", PLAN_DTYPE)])
 
 EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_plan_prefill",
            "kvc_compress_prefill", "kvc_compress_prefill_paged", "kvc_compress_decode_ring",
            "kvc_compress_decode_ring_paged", "kvc_seed_tail_ring",
            "kvc_c128_online_decode", "kvc_c128_online_decode_layers",
            "kvc_c128_online_decode_quant", "kvc_c128_online_prefill",
-           "kvc_c128_online_prefill_quant", "kvc_diag_convert", "kvc_diag_stream_read")
+           "kvc_c128_online_prefill_quant", "kvc_c128_plan_prefill_fused",
+           "kvc_c128_online_prefill_fused", "kvc_diag_convert", "kvc_diag_stream_read")
 
 
 class KvcError(RuntimeError):
@@ -78,6 +80,9 @@ def lib() -> ctypes.CDLL:
                                                    _p]
         L.kvc_c128_online_prefill_quant.argtypes = [_p, _i64, _p, _p, _p, _i64, _p, _p, _p,
                                                     _i64, _p, _u32, _p, _u32, _i32, _p]
+        L.kvc_c128_plan_prefill_fused.argtypes = [_p, _p, _i64, _i64, _p, _i32, _p]
+        L.kvc_c128_online_prefill_fused.argtypes = [_p, _i64, _p, _p, _p, _p, _i32, _i64, _p, _p,
+                                                    _i64, _p, _u32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
         L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _p]
         for name in EXPORTS[2:]:
@@ -155,6 +160,22 @@ def kvc_c128_plan_prefill(seq_lens, extend_lens, num_tokens: int, pad_to_capacit
                                        _np_ptr(cp), _np_ptr(wp), int(pad_to_capacity),
                                        ctypes.byref(nc), ctypes.byref(nw)))
     return cp[:nc.value].copy(), wp[:nw.value].copy()
+
+
+def kvc_c128_plan_prefill_fused(seq_lens, extend_lens, num_tokens: int,
+                                pad_to_capacity: bool = False):
+    """Work items for kvc_c128_online_prefill_fused: host array of ITEM_DTYPE
+    (fields compress / write, each a PLAN_DTYPE record; all-0xFFFFFFFF = none)."""
+    sl = np.ascontiguousarray(seq_lens, np.int64)
+    el = np.ascontiguousarray(extend_lens, np.int64)
+    if sl.size != el.size:
+        raise ValueError("seq_lens and extend_lens differ in length")
+    items = np.zeros(max(int(num_tokens), 1), ITEM_DTYPE)
+    n = ctypes.c_uint32()
+    _check(lib().kvc_c128_plan_prefill_fused(_np_ptr(sl), _np_ptr(el), sl.size, int(num_tokens),
+                                             _np_ptr(items), int(pad_to_capacity),
+                                             ctypes.byref(n)))
+    return items[:n.value].copy()
 
 
 # ------------------------------------------------------------------ device entry points
@@ -419,6 +440,38 @@ def kvc_c128_online_prefill(state, kv_score_in, out, ape, indices, compress_plan
         cp, int(n_compress), wp, int(n_write), _stream(stream)))
 
 
+def kvc_c128_online_prefill_fused(state, kv_score_in, ape, indices, items, n_items, out=None,
+                                  out_fp8=None, out_scale=None, round_scale: bool = True,
+                                  stream=None):
+    """Single-launch prefill over device work items (see items_to_device);
+    chunk-closing vectors go to out (fp32 [N,128]) or, with out_fp8 / out_scale,
+    through the rotate / e4m3 epilogue."""
+    import torch
+    N, B = kv_score_in.shape[0], indices.shape[0]
+    _shape_ok(state, (None, 384), "state")
+    _shape_ok(kv_score_in, (N, 256), "kv_score_in")
+    _shape_ok(ape, (128, 128), "ape")
+    _shape_ok(indices, (B,), "indices")
+    _need((out is None) != (out_fp8 is None), "give either out or out_fp8 / out_scale")
+    if out is not None:
+        _shape_ok(out, (N, 128), "out")
+    else:
+        _shape_ok(out_fp8, (N, 128), "out_fp8")
+        _shape_ok(out_scale, (N,), "out_scale")
+    if int(n_items) > 0:
+        _need(items is not None and items.is_cuda and items.is_contiguous()
+              and items.numel() * items.element_size() >= 32 * int(n_items),
+              f"items must be a contiguous device tensor of at least {int(n_items)} entries")
+    _check(lib().kvc_c128_online_prefill_fused(
+        _dptr(state, torch.float32, "state"), state.shape[0],
+        _dptr(kv_score_in, torch.float32, "kv_score_in"),
+        _dptr(out, torch.float32, "out", optional=True),
+        _dptr(out_fp8, torch.uint8, "out_fp8", optional=True),
+        _dptr(out_scale, torch.float32, "out_scale", optional=True), int(round_scale), N,
+        _dptr(ape, torch.float32, "ape"), _dptr(indices, torch.int32, "indices"), B,
+        None if items is None else items.data_ptr(), int(n_items), _stream(stream)))
+
+
 def kvc_diag_convert(x, bf16_out=None, fp8_out=None, stream=None):
     import torch
     _check(lib().kvc_diag_convert(
@@ -446,6 +499,15 @@ def plans_to_device(plan: np.ndarray, device="cuda"):
     raw = np.ascontiguousarray(plan, PLAN_DTYPE).view(np.uint8).reshape(-1, 16)
     if raw.shape[0] == 0:
         return torch.empty((1, 16), dtype=torch.uint8, device=device)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+def items_to_device(items: np.ndarray, device="cuda"):
+    """Host ITEM_DTYPE array -> device uint8 tensor [n, 32] (16-byte aligned)."""
+    import torch
+    raw = np.ascontiguousarray(items, ITEM_DTYPE).view(np.uint8).reshape(-1, 32)
+    if raw.shape[0] == 0:
+        return torch.empty((1, 32), dtype=torch.uint8, device=device)
     return torch.from_numpy(raw.copy()).to(device)
 
 

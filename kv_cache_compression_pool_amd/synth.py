@@ -157,12 +157,18 @@ def c128_decode(seed: int = 0, batch: int = 1024, num_slots: int = 2048,
 
 
 def c128_prefill(seed: int = 0, batch: int = 32, num_slots: int = 2048,
-                 max_prior: int = 32768, max_extend: int = 16384):
+                 max_prior: int = 32768, max_extend: int = 16384, seq_lens=None,
+                 extend_lens=None):
     """Inputs for one ragged prefill.  ``prior_counts[b] = prior % 128`` raw
-    tokens (rows of ``prior_in``) form the open chunk carried in the state."""
+    tokens (rows of ``prior_in``) form the open chunk carried in the state.
+    Explicit ``seq_lens`` / ``extend_lens`` replace the random lengths."""
     g = rng(seed, "c128_prefill")
     prior = g.integers(0, max_prior, size=batch, endpoint=True).astype(np.int64)
     extend = g.integers(1, max_extend, size=batch, endpoint=True).astype(np.int64)
+    if seq_lens is not None:
+        extend = np.asarray(extend_lens, np.int64)
+        prior = np.asarray(seq_lens, np.int64) - extend
+        batch = extend.size
     seq_lens = prior + extend
     N = int(extend.sum())
     indices = g.permutation(num_slots)[:batch].astype(np.int32)

@@ -51,6 +51,68 @@ def test_c128_planner_matches_oracle():
             assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def _is_pad(rec):
+    return int(rec["ragged_id"]) == kvc.PLAN_SENTINEL
+
+
+def test_c128_fused_planner_matches_oracle_plans():
+    """The fused work items hold exactly the oracle's plans, pair a request's
+    first compress plan with its write plan only when that compress plan
+    starts mid-chunk (the one state read a write can conflict with), and are
+    ordered paired / compress-only / write-only, each in request order."""
+    g = np.random.default_rng(3)
+    key = lambda r: tuple(int(r[f]) for f in ("ragged_id", "batch_id", "position", "window_len"))
+    for trial in range(300):
+        B = int(g.integers(1, 7))
+        el = g.integers(1, 700, B)
+        sl = el + g.integers(0, 700, B)
+        if trial % 3 == 0:                  # many chunk-aligned lengths
+            sl = np.maximum(sl - sl % 128, 128) + 128 * (g.random(B) < 0.5)
+            el = np.minimum(el, sl)
+        n = int(el.sum())
+        cp, wp = oracle.c128_plan(sl, el, n)
+        items = kvc.kvc_c128_plan_prefill_fused(sl, el, n)
+        assert items.size == cp.size + wp.size - sum(
+            1 for it in items if not _is_pad(it["compress"]) and not _is_pad(it["write"]))
+        got_c = [key(it["compress"]) for it in items if not _is_pad(it["compress"])]
+        got_w = [key(it["write"]) for it in items if not _is_pad(it["write"])]
+        assert sorted(got_c) == sorted(key(r) for r in cp)
+        assert sorted(got_w) == sorted(key(r) for r in wp)
+        kinds = []
+        for it in items:
+            c, w = it["compress"], it["write"]
+            assert not (_is_pad(c) and _is_pad(w))
+            if not _is_pad(c) and not _is_pad(w):
+                b = int(c["batch_id"])
+                assert int(w["batch_id"]) == b
+                prefix = int(sl[b] - el[b])
+                first_pos = int(c["position"]) - int(c["window_len"]) + 1
+                assert first_pos == prefix and prefix % 128 != 0
+                kinds.append(0)
+            elif not _is_pad(c):
+                b = int(c["batch_id"])
+                first_pos = int(c["position"]) - int(c["window_len"]) + 1
+                # a first, mid-chunk compress plan with a write plan must be paired
+                assert not (first_pos % 128 != 0 and sl[b] % 128 != 0)
+                kinds.append(1)
+            else:
+                b = int(w["batch_id"])
+                first_pos = int(w["position"]) - int(w["window_len"]) + 1
+                # an unpaired write plan: no compress plan of its request reads the state
+                assert first_pos == int(sl[b] - el[b]) or int(sl[b] - el[b]) % 128 == 0
+                kinds.append(2)
+        assert kinds == sorted(kinds)
+        for k in (0, 1, 2):
+            sel = [it for it, kk in zip(items, kinds) if kk == k]
+            half = "write" if k == 2 else "compress"
+            bids = [(int(it[half]["batch_id"]), int(it[half]["position"])) for it in sel]
+            assert bids == sorted(bids)
+        padded = kvc.kvc_c128_plan_prefill_fused(sl, el, n, pad_to_capacity=True)
+        assert padded.size == n
+        assert np.array_equal(padded[:items.size], items)
+        assert all(_is_pad(it["compress"]) and _is_pad(it["write"]) for it in padded[items.size:])
+
+
 def test_planner_errors():
     with pytest.raises(kvc.KvcError) as e:
         kvc.kvc_c128_plan_prefill([10], [11], 11)
@@ -106,10 +168,23 @@ def test_device_entry_points_validate_before_launch():
         == kvc.KVC_ERR_NULL
     assert L.kvc_c128_online_prefill(p, 4, p, p, 8, p, p, None, 1, ctypes.c_void_p(0x1008), 3,
                                      None, 0, None) == kvc.KVC_ERR_SHAPE
+    # fused prefill: nothing to do, missing items, both / neither output, misaligned items
+    f = L.kvc_c128_online_prefill_fused
+    assert f(p, 4, p, p, None, None, 1, 8, p, p, 1, None, 0, None) == kvc.KVC_OK
+    assert f(p, 4, p, p, None, None, 1, 8, p, p, 1, None, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, p, p, p, 1, 8, p, p, 1, p, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, None, None, None, 1, 8, p, p, 1, p, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, None, p, None, 1, 8, p, p, 1, p, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, p, None, None, 1, 8, p, p, 1, ctypes.c_void_p(0x1008), 2, None) \
+        == kvc.KVC_ERR_SHAPE
+    with pytest.raises(kvc.KvcError) as e:
+        kvc.kvc_c128_plan_prefill_fused([10], [11], 11)
+    assert e.value.code == kvc.KVC_ERR_PLAN
     assert L.kvc_diag_convert(p, None, None, 3, None) == kvc.KVC_ERR_SHAPE
     assert b"even" in L.kvc_last_error()
 
 
 def test_plan_struct_layout():
     assert kvc.PLAN_DTYPE.itemsize == 16
+    assert kvc.ITEM_DTYPE.itemsize == 32
     assert kvc.PLAN_DTYPE == oracle.PLAN_DTYPE

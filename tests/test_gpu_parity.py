@@ -411,6 +411,89 @@ def test_c128_prefill_distinct_load_indices():
     compare_state(gst, st, "c128 prefill load_indices")
 
 
+def run_c128_prefill_fused_gpu(d, state, pad=False, quant=False, round_scale=True):
+    n = int(d["extend_lens"].sum())
+    items = kvc.kvc_c128_plan_prefill_fused(d["seq_lens"], d["extend_lens"], n,
+                                            pad_to_capacity=pad)
+    gst = dev(state)
+    kw = {}
+    if quant:
+        kw["out_fp8"] = torch.full((n, 128), 0x33, dtype=torch.uint8, device="cuda")
+        kw["out_scale"] = torch.full((n,), 5.0, device="cuda")
+        kw["round_scale"] = round_scale
+    else:
+        kw["out"] = torch.full((n, 128), float("nan"), device="cuda")
+    kvc.kvc_c128_online_prefill_fused(gst, dev(d["kv_score_in"]), dev(d["ape"]),
+                                      dev(d["indices"]), kvc.items_to_device(items), items.size,
+                                      **kw)
+    torch.cuda.synchronize()
+    outs = [t.cpu().numpy() for k, t in kw.items() if k != "round_scale"]
+    return gst.cpu().numpy(), outs, items
+
+
+def compare_c128_prefill_fused(d, what, pad=False):
+    """Single-launch prefill: within tolerance of the oracle and identical to
+    the two-launch device path (same per-plan arithmetic)."""
+    note(what)
+    st = d["state"].copy()
+    ref = np.full((int(d["extend_lens"].sum()), 128), np.nan, np.float32)
+    oracle.c128_prefill(st, d["kv_score_in"], d["ape"], d["indices"], d["cplan"], d["wplan"],
+                        out=ref)
+    gst, (gout,), items = run_c128_prefill_fused_gpu(d, d["state"], pad=pad)
+    paired = int(sum(1 for it in items if it["compress"]["ragged_id"] != kvc.PLAN_SENTINEL
+                     and it["write"]["ragged_id"] != kvc.PLAN_SENTINEL))
+    assert np.array_equal(np.isnan(gout), np.isnan(ref))
+    rows = ~np.isnan(ref[:, 0])
+    e = rel_err_rows(gout[rows], ref[rows]).max(initial=0)
+    assert e <= VEC_TOL, f"{what}: out err {e:.3g}"
+    compare_state(gst, st, what + " state")
+    gst2, gout2, _, _ = run_c128_prefill_gpu(d, d["state"])
+    assert np.array_equal(gout, gout2, equal_nan=True), f"{what}: differs from two launches"
+    assert np.array_equal(gst, gst2, equal_nan=True), f"{what}: state differs from two launches"
+    note(f"{what}: {items.size} items ({paired} paired), {rows.sum()} vectors, out err {e:.3g}")
+    return paired
+
+
+def test_c128_prefill_fused_full_size_c5():
+    assert compare_c128_prefill_fused(c128_prefill_case(seed=0), "c128 fused prefill 32 seqs") > 0
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_c128_prefill_fused_small_and_padded(seed):
+    d = c128_prefill_case(seed=seed, batch=5, max_prior=700, max_extend=900)
+    compare_c128_prefill_fused(d, f"c128 fused prefill small seed {seed}")
+    compare_c128_prefill_fused(d, f"c128 fused prefill small seed {seed} padded", pad=True)
+
+
+def test_c128_prefill_fused_every_item_kind():
+    # prior mid-chunk + closing + trailing (paired); prior aligned (compress-only
+    # first segment); single mid-chunk segment (write-only); exact chunk ends.
+    seq = np.array([300, 512, 70, 256, 1000, 129, 131, 200], np.int64)
+    ext = np.array([250, 256, 10, 200, 990, 1, 130, 199], np.int64)
+    d = c128_prefill_case(seed=7, seq_lens=seq, extend_lens=ext)
+    assert compare_c128_prefill_fused(d, "c128 fused prefill item kinds") == 4
+
+
+def test_c128_prefill_fused_quant():
+    d = c128_prefill_case(seed=0)
+    note("c128 fused prefill quant 32 seqs")
+    N = int(d["extend_lens"].sum())
+    for rs in (True, False):
+        gst, (gc, gs), items = run_c128_prefill_fused_gpu(d, d["state"], quant=True,
+                                                          round_scale=rs)
+        cp, wp = kvc.kvc_c128_plan_prefill(d["seq_lens"], d["extend_lens"], N)
+        g2 = dev(d["state"])
+        c2 = torch.full((N, 128), 0x33, dtype=torch.uint8, device="cuda")
+        s2 = torch.full((N,), 5.0, device="cuda")
+        kvc.kvc_c128_online_prefill_quant(g2, dev(d["kv_score_in"]), c2, s2, dev(d["ape"]),
+                                          dev(d["indices"]), kvc.plans_to_device(cp), cp.size,
+                                          kvc.plans_to_device(wp), wp.size, rs)
+        torch.cuda.synchronize()
+        assert np.array_equal(gc, c2.cpu().numpy())
+        assert np.array_equal(gs, s2.cpu().numpy())
+        assert np.array_equal(gst, g2.cpu().numpy(), equal_nan=True)
+
+
 # ------------------------------------------------------------------ tail-ring seeding
 @pytest.mark.parametrize("num_seqs,max_len,pad,blocks", [(64, 8192, 0, None), (30, 40, 13, None),
                                                          (7, 5, 0, None), (12, 100, 3, 9)])
