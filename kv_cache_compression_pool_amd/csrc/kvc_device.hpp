@@ -69,17 +69,68 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
+// ---- exchanges between the four 16-lane rows of a wave -------------------
+// gfx950's v_permlane16_swap / v_permlane32_swap move whole rows between two
+// registers on the VALU (no LDS).  Called with (a, b) they return
+//   permlane16: d = (odd row)    ? b[l-16] : a[l],  s = (even row)   ? a[l+16] : b[l]
+//   permlane32: d = (upper half) ? b[l-32] : a[l],  s = (lower half) ? a[l+32] : b[l]
+struct LanePair {
+  float d, s;
+};
+__device__ __forceinline__ LanePair permlane16_swap(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair permlane32_swap(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Value of lane l ^ 16 (odd: this lane is in an odd row).
+__device__ __forceinline__ float xor_rows16(float v, bool odd) {
+  const LanePair p = permlane16_swap(v, v);
+  return odd ? p.d : p.s;
+}
+// Value of lane l ^ 32 (upper: this lane is in the upper half).
+__device__ __forceinline__ float xor_rows32(float v, bool upper) {
+  const LanePair p = permlane32_swap(v, v);
+  return upper ? p.d : p.s;
+}
+// Max with lane l ^ 16 / l ^ 32 (every lane receives it).
+__device__ __forceinline__ float max_rows16(float v) {
+  const LanePair p = permlane16_swap(v, v);
+  return fmaxf(p.d, p.s);
+}
+__device__ __forceinline__ float max_rows32(float v) {
+  const LanePair p = permlane32_swap(v, v);
+  return fmaxf(p.d, p.s);
+}
+// Reduce-scatter of two values with lane l ^ 16: even rows receive
+// a[l] + a[l ^ 16], odd rows b[l] + b[l ^ 16].
+__device__ __forceinline__ float sum_scatter16(float a, float b) {
+  const LanePair p = permlane16_swap(a, b);
+  return p.d + p.s;
+}
+// The same with lane l ^ 32: the lower half receives the a sums, the upper
+// half the b sums.
+__device__ __forceinline__ float sum_scatter32(float a, float b) {
+  const LanePair p = permlane32_swap(a, b);
+  return p.d + p.s;
+}
+
 // ---- Walsh-Hadamard over a 32-lane-distributed 128-vector ----------------
 // A 128-vector is spread over two 16-lane rows: lane c of row h holds the
 // channels 8c + 4h + t, t = 0..3, in v[0..3].  Channel index bits 0-1 live in
 // the register index, bit 2 in the row index, bits 3-6 in the lane index.
 // Every stage maps the pair (a, b) at channel indices (i, i + 2^k) to
 // (a + b, a - b), giving the unnormalised Sylvester-ordered transform H v.
-template <int kMask>
-__device__ __forceinline__ void wht_lane_stage(float (&v)[4], int c) {
+template <int kMask, int N>
+__device__ __forceinline__ void wht_lane_stage(float (&v)[N], int c) {
   const float sgn = (c & kMask) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < N; ++t) {
     const float p = row_xor<kMask>(v[t]);
     v[t] = __builtin_fmaf(v[t], sgn, p);   // lane bit clear: v + p; set: p - v
   }
@@ -174,6 +225,54 @@ __device__ __forceinline__ uint32_t rotate_quantise32(float (&v)[4], int c, int 
   }
   scale_out = scale;
   return pack_e4m3x4(q[0], q[1], q[2], q[3]);
+}
+
+// ---- rotate + quantise one 128-vector held by a whole wave -----------------
+// Lane l = 16q + c holds channels 8c + 2q + t, t = 0..1, in v[0..1]: channel
+// bit 0 in the register index, bit 1 in the row parity (q & 1), bit 2 in the
+// wave half (q >> 1), bits 3-6 in the lane of the row.  Same steps and result
+// as rotate_quantise32.  Returns the 2 codes in the low 16 bits and the
+// vector's scale (same in all 64 lanes).
+__device__ __forceinline__ uint32_t rotate_quantise64(float (&v)[2], int c, int q,
+                                                      bool round_scale, float& scale_out) {
+  const bool odd = q & 1, upper = q >> 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) v[t] = round_bf16(v[t]);
+  {
+    const float a = v[0], b = v[1];
+    v[0] = a + b;
+    v[1] = a - b;
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) v[t] = __builtin_fmaf(v[t], odd ? -1.0f : 1.0f, xor_rows16(v[t], odd));
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    v[t] = __builtin_fmaf(v[t], upper ? -1.0f : 1.0f, xor_rows32(v[t], upper));
+  wht_lane_stage<1>(v, c);
+  wht_lane_stage<2>(v, c);
+  wht_lane_stage<4>(v, c);
+  wht_lane_stage<8>(v, c);
+  float amax = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    v[t] = round_bf16(v[t] * kInvSqrt128);
+    amax = fmaxf(amax, fabsf(v[t]));
+  }
+  amax = row_max16(amax);
+  amax = max_rows16(amax);
+  amax = max_rows32(amax);
+  const float scale = fp8_scale(amax, round_scale);
+  float qv[2];
+  if (round_scale) {
+    const float inv = pow2_recip(scale);   // exact: scale is a power of two
+#pragma unroll
+    for (int t = 0; t < 2; ++t) qv[t] = clamp_fp8(v[t] * inv);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) qv[t] = clamp_fp8(v[t] / scale);   // IEEE division
+  }
+  scale_out = scale;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false) & 0xffffu;
 }
 
 }  // namespace kvc

@@ -23,6 +23,10 @@
 //     staged once per workgroup in LDS (measured faster than per-lane reads
 //     of ape through the L1).
 //   * At most 128 VGPRs, so four waves per SIMD keep enough loads in flight.
+//   * Ring decode of short verify batches is latency-bound, not bandwidth-
+//     bound: there one request takes a whole wave (row q of the wave owns
+//     slots 4q..4q+3) so each lane's share of the dependent arithmetic is
+//     halved; rows exchange through gfx950's permlane swaps.
 // The path is HBM-bound (about 8.3 KB read per 132 B written); there is no
 // dense contraction, so no MFMA.
 #include "kvc_device.hpp"
@@ -125,6 +129,67 @@ __device__ __forceinline__ void pool_mean(const uint4 (&S)[kHalf], const uint4 (
   }
 }
 
+// Softmax-weighted mean of one pool, whole-wave layout (one pool per wave,
+// for latency-bound calls).  Lane 16q + c holds the gate scores S[i] and keys
+// K[i] of slot 4q + i, channels 8c..8c+7.  Returns x[t] = the mean of channel
+// 8c + 2q + t, t = 0..1: the max is all-reduced over the four rows, the sums
+// are reduce-scattered (first across the wave halves, then across row pairs),
+// so each lane finishes only the two channels it rotates afterwards.
+__device__ __forceinline__ void pool_mean_wave(const uint4 (&S)[4], const uint4 (&K)[4],
+                                               const float4* __restrict__ s_ape, int c, int q,
+                                               float (&x)[2]) {
+  const float4* ap = s_ape + (4 * q) * 32 + 2 * c;
+  float u[4][8], m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m[j] = -__builtin_huge_valf();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s[8];
+    widen8(S[i], s);
+    const float4 a0 = ap[i * 32], a1 = ap[i * 32 + 1];
+    const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u[i][j] = s[j] + a[j];
+      m[j] = fmaxf(m[j], u[i][j]);
+    }
+  }
+  float ml[8], den[8], acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    m[j] = max_rows32(max_rows16(m[j]));          // max over all 16 slots
+    ml[j] = m[j] * kLog2e;
+    den[j] = 0.0f;
+    acc[j] = 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float k[8];
+    widen8(K[i], k);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = exp2_hw(__builtin_fmaf(u[i][j], kLog2e, -ml[j]));
+      den[j] += p;
+      acc[j] = __builtin_fmaf(k[j], p, acc[j]);
+    }
+  }
+  // Lower half keeps channels j = 0..3, upper half j = 4..7 (channel bit 2 =
+  // q >> 1); then even rows keep j' = 0, 1 and odd rows j' = 2, 3 of those
+  // (channel bit 1 = q & 1).
+  float d4[4], a4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    d4[j] = sum_scatter32(den[j], den[j + 4]);
+    a4[j] = sum_scatter32(acc[j], acc[j + 4]);
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float d = sum_scatter16(d4[t], d4[t + 2]);
+    const float a = sum_scatter16(a4[t], a4[t + 2]);
+    x[t] = a * __builtin_amdgcn_rcpf(d);
+  }
+}
+
 // bf16 round -> rotate -> bf16 round -> scale -> e4m3 for the pool's two
 // rows.  Row h handles channels 8c + 4h + t; returns their 4 codes packed
 // little-endian and the pool's scale.
@@ -153,6 +218,17 @@ struct OutSink {
     } else {
       reinterpret_cast<uint32_t*>(codes + row * 128)[2 * c + h] = code4;
       if (c == 0 && h == 0) scales[row] = scale;
+    }
+  }
+  // Whole-wave layout: lane 16q + c stores the codes of channels 8c + 2q and
+  // 8c + 2q + 1 (low 16 bits of code2).
+  __device__ __forceinline__ void store2(int64_t row, int c, int q, uint32_t code2,
+                                         float scale) const {
+    uint8_t* base = codes + row * (paged ? kPagedBytes : 128);
+    reinterpret_cast<uint16_t*>(base)[4 * c + q] = (uint16_t)code2;
+    if (c == 0 && q == 0) {
+      if (paged) *reinterpret_cast<float*>(base + 128) = scale;
+      else scales[row] = scale;
     }
   }
 };
@@ -271,28 +347,32 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
   }
 }
 
-// Ring decode for short verify batches (next_n <= kMaxN).  Same result as
-// pool16_ring_kernel, organised for latency:
+// Ring decode for short verify batches (next_n <= kMaxN) with one request per
+// wave.  The same ordered semantics as pool16_ring_kernel:
 //  * every token's maps and key / score rows are requested up front, in the
 //    same round trip as the ape table;
 //  * the loop runs over completions, not tokens.  Before completion t* reads
 //    its ring block, the stashes of tokens [done, t*) are stored from the
-//    lanes that read those slots back, which keeps the ordered semantics.
-//    Both 32-lane halves of a wave run the softmax / rotate / quantise body
-//    together even when they complete at different tokens.
+//    lanes that read those slots back: row q of the wave stashes and reads
+//    slots 4q..4q+3, so same-lane program order orders them;
+//  * a whole wave per request halves each lane's share of the softmax and
+//    rotation (4 slots x 8 channels, then 2 channels) compared with the
+//    32-lane layout: in this latency-bound call the dependent arithmetic of
+//    one completion, not bandwidth, sets the time.
 template <bool kRoundScale, int kMaxN>
-__global__ __launch_bounds__(kBlock) void pool16_ring_prefetch_kernel(
+__global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
     const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
     const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
     const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
     const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink) {
   static_assert(kMaxN <= 32, "completion mask is 32 bits");
+  constexpr int kReqPerBlock = kBlock / 64;
   __shared__ float4 s_ape[kPool * 32];
   const int c = threadIdx.x & 15;
-  const int h = (threadIdx.x >> 4) & 1;
-  const int64_t r = (int64_t)blockIdx.x * kPoolsPerBlock + (threadIdx.x >> 5);
-  const int64_t rr = r < num_requests ? r : 0;   // rows past the batch read request 0, stop below
+  const int q = (threadIdx.x >> 4) & 3;
+  const int64_t r = (int64_t)blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
+  const int64_t rr = r < num_requests ? r : 0;   // waves past the batch read request 0, stop below
 
   const ApeRegs ape_regs = load_ape(ape);
   int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
@@ -315,9 +395,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_prefetch_kernel(
                  "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x), "v"(sv[t].y), "v"(sv[t].z),
                  "v"(sv[t].w));
   store_ape(s_ape, ape_regs);
-  if (r >= num_requests) return;
+  if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
 
-  // Per-token decisions: ring block, completion and stash flags.
   int32_t blk[kMaxN];
   uint32_t completes = 0, stashes = 0;
 #pragma unroll
@@ -326,8 +405,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_prefetch_kernel(
     blk[t] = (int32_t)b;   // ts is int32, so the block index fits
     if (t >= next_n || b >= num_blocks) continue;
     if (loc[t] >= 0 && pos[t] >= 0 && (pos[t] & (kPool - 1)) == kPool - 1) completes |= 1u << t;
-    // A row stores the stashes of the slots it later reads (slots 8h..8h+7).
-    if (pos[t] >= 0 && ts[t] >= 0 && ((pos[t] & (kPool - 1)) >> 3) == h) stashes |= 1u << t;
+    if (pos[t] >= 0 && ts[t] >= 0 && ((pos[t] & (kPool - 1)) >> 2) == q) stashes |= 1u << t;
   }
 
   auto stash_range = [&](uint32_t mask) {
@@ -343,7 +421,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_prefetch_kernel(
   };
 
   uint32_t done = 0;   // tokens whose stash has been stored: bits below the cursor
-  while (completes) {
+  while (completes) {  // uniform over the wave: one request per wave
     const int t1 = __builtin_ctz(completes);
     completes &= completes - 1;
     const uint32_t before = (1u << t1) - 1;
@@ -362,30 +440,28 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_prefetch_kernel(
     }
     const uint16_t* ring_k = ring + (int64_t)b1 * (2 * kPool * 128);
     const uint16_t* ring_s = ring_k + kPool * 128;
-    uint4 S[kHalf], K[kHalf];
+    uint4 S[4], K[4];
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) {
-      const int slot = kHalf * h + i;
+    for (int i = 0; i < 4; ++i) {
+      const int slot = 4 * q + i;
       S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
       K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
     }
-    // All 16 row loads in flight at once (the scheduler otherwise splits them
-    // into two round trips to save registers).
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i)
+    for (int i = 0; i < 4; ++i)
       asm volatile("" ::"v"(S[i].x), "v"(S[i].y), "v"(S[i].z), "v"(S[i].w), "v"(K[i].x),
                    "v"(K[i].y), "v"(K[i].z), "v"(K[i].w));
-    // Slot 15 is the completing token itself: row 1 replaces what it read
+    // Slot 15 is the completing token itself: row 3 replaces what it read
     // there (a load kept unconditional so the row loads stay branch-free).
-    if (h) {
-      S[kHalf - 1] = s1;
-      K[kHalf - 1] = k1;
+    if (q == 3) {
+      S[3] = s1;
+      K[3] = k1;
     }
-    float x[8];
-    pool_mean(S, K, s_ape, c, h, x);
+    float x[2];
+    pool_mean_wave(S, K, s_ape, c, q, x);
     float scale;
-    const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
-    if (l1 < sink.rows) sink.store(l1, c, h, codes, scale);
+    const uint32_t codes = rotate_quantise64(x, c, q, kRoundScale, scale);
+    if (l1 < sink.rows) sink.store2(l1, c, q, codes, scale);
   }
   stash_range(stashes & ~done);
 }
@@ -447,20 +523,22 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                               const int32_t* positions, int64_t num_requests, int next_n,
                               uint8_t* out_fp8, float* out_scale, int64_t out_rows, bool paged,
                               bool round_scale, hipStream_t stream) {
-  const dim3 grid((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
   const OutSink sink{out_fp8, out_scale, out_rows, paged};
+  constexpr int kWaveReq = kBlock / 64;
+  dim3 grid((unsigned)((num_requests + kWaveReq - 1) / kWaveReq));
 #define KVC_RING(KERNEL)                                                                      \
   hipLaunchKernelGGL(KERNEL, grid, block, 0, stream, ring, num_blocks, tail_slot, key, key_sb, \
                      key_st, score, score_sb, score_st, ape, slot_mapping, positions,           \
                      num_requests, next_n, sink)
   if (next_n <= 4) {
-    if (round_scale) KVC_RING((pool16_ring_prefetch_kernel<true, 4>));
-    else KVC_RING((pool16_ring_prefetch_kernel<false, 4>));
+    if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 4>));
+    else KVC_RING((pool16_ring_wave_kernel<false, 4>));
   } else if (next_n <= 8) {
-    if (round_scale) KVC_RING((pool16_ring_prefetch_kernel<true, 8>));
-    else KVC_RING((pool16_ring_prefetch_kernel<false, 8>));
+    if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 8>));
+    else KVC_RING((pool16_ring_wave_kernel<false, 8>));
   } else {
+    grid = dim3((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock));
     if (round_scale) KVC_RING((pool16_ring_kernel<true>));
     else KVC_RING((pool16_ring_kernel<false>));
   }

@@ -133,3 +133,62 @@ def test_graph_replay_matches_eager():
                 f"replay {rep} (plans {plan}): output {i} differs from eager"
         _ = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
         torch.cuda.synchronize()
+
+
+def test_graph_replay_single_launch_prefill():
+    """The single-launch c128 prefill captured once with capacity-padded work
+    items; two item lists of the same capacity swapped between replays."""
+    sl_a, el_a = np.array([700, 300, 129, 50]), np.array([600, 300, 2, 50])
+    sl_b, el_b = np.array([900, 130, 377, 20]), np.array([500, 130, 302, 20])
+    N = int(el_a.sum())
+    st_np, x_np, a_np, i_np = _c128_prefill_inputs(26, sl_a, el_a)
+    st0, x, a, idx = dev(st_np), dev(x_np), dev(a_np), dev(i_np)
+    st = st0.clone()
+    lists = {}
+    for name, sl, el in (("a", sl_a, el_a), ("b", sl_b, el_b)):
+        items = kvc.kvc_c128_plan_prefill_fused(sl, el, N, pad_to_capacity=True)
+        assert items.size == N
+        lists[name] = kvc.items_to_device(items)
+    items_t = torch.empty_like(lists["a"])
+    out = torch.empty((N, 128), device="cuda")
+
+    def step():
+        kvc.kvc_c128_online_prefill_fused(st, x, a, idx, items_t, N, out=out)
+
+    def reset(name):
+        st.copy_(st0)
+        items_t.copy_(lists[name])
+        out.fill_(7.0)
+
+    eager = {}
+    for name in ("a", "b"):
+        reset(name)
+        step()
+        torch.cuda.synchronize()
+        eager[name] = (st.cpu().clone(), out.cpu().clone())
+    assert not torch.equal(eager["a"][1], eager["b"][1])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    reset("a")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    reset("a")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep, name in enumerate(("a", "b", "b", "a")):
+        reset(name)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (g_, e_) in enumerate(zip((st.cpu(), out.cpu()), eager[name])):
+            assert torch.equal(g_.view(torch.uint8), e_.view(torch.uint8)), \
+                f"replay {rep} (items {name}): output {i} differs from eager"
+        _ = torch.randn(256, 256, device="cuda") @ torch.randn(256, 256, device="cuda")
+        torch.cuda.synchronize()
