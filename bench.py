@@ -120,7 +120,7 @@ def to_dev(torch, a):
 
 # ------------------------------------------------------------------ pool-16 prefill
 def bench_pool16_prefill(args, torch, kvc, synth, stream):
-    d = synth.pool16_ragged(seed=0)
+    d = synth.pool16_ragged(seed=0, num_seqs=args.prefill_seqs)
     rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
     n = int(rows.size)
     T = d["keys"].shape[0]
@@ -382,6 +382,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-layers", type=int, default=64,
                     help="layers in the multi-layer c128 decode measurement (0: skip)")
+    ap.add_argument("--prefill-seqs", type=int, default=64,
+                    help="sequences in the pool-16 prefill batch (64 is the configured "
+                         "workload; other sizes show how the rate depends on batch size)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -422,7 +425,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "pool16_ragged_prefill", "num_seqs": 64, "len_range": [1, 8192],
+        "config": {"workload": "pool16_ragged_prefill", "num_seqs": args.prefill_seqs,
+                   "len_range": [1, 8192],
                    "tokens": p["tokens"], "pools": p["n"], "pool": 16, "head_dim": 128,
                    "round_scale": True, "io": "bf16 in, e4m3 + fp32 scale out",
                    "input_replicas": p["replicas"]},
@@ -430,7 +434,7 @@ def main():
         "hbm_frac": round(achieved / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic() if args.prefill_seqs == 64 else None,
                      "kernel": "pool16_prefill_kernel",
                      "bytes_per_launch": p["alg_bytes"],
                      "bytes_per_vector": p["bytes_per_vec"],
