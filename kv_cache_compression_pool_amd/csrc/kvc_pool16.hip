@@ -136,9 +136,7 @@ __device__ __forceinline__ void pool_mean(const uint4 (&S)[kHalf], const uint4 (
 // are reduce-scattered (first across the wave halves, then across row pairs),
 // so each lane finishes only the two channels it rotates afterwards.
 __device__ __forceinline__ void pool_mean_wave(const uint4 (&S)[4], const uint4 (&K)[4],
-                                               const float4* __restrict__ s_ape, int c, int q,
-                                               float (&x)[2]) {
-  const float4* ap = s_ape + (4 * q) * 32 + 2 * c;
+                                               const float4 (&A)[4][2], float (&x)[2]) {
   float u[4][8], m[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) m[j] = -__builtin_huge_valf();
@@ -146,7 +144,7 @@ __device__ __forceinline__ void pool_mean_wave(const uint4 (&S)[4], const uint4 
   for (int i = 0; i < 4; ++i) {
     float s[8];
     widen8(S[i], s);
-    const float4 a0 = ap[i * 32], a1 = ap[i * 32 + 1];
+    const float4 a0 = A[i][0], a1 = A[i][1];
     const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -368,13 +366,20 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink) {
   static_assert(kMaxN <= 32, "completion mask is 32 bits");
   constexpr int kReqPerBlock = kBlock / 64;
-  __shared__ float4 s_ape[kPool * 32];
   const int c = threadIdx.x & 15;
   const int q = (threadIdx.x >> 4) & 3;
   const int64_t r = (int64_t)blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
   const int64_t rr = r < num_requests ? r : 0;   // waves past the batch read request 0, stop below
 
-  const ApeRegs ape_regs = load_ape(ape);
+  // Each lane keeps the ape values of its 4 slots x 8 channels in registers
+  // (L2-resident 8 KB table): no LDS staging, so no barrier in the chain.
+  float4 A[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4* ap = reinterpret_cast<const float4*>(ape) + (4 * q + i) * 32 + 2 * c;
+    A[i][0] = ap[0];
+    A[i][1] = ap[1];
+  }
   int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
   uint4 kv[kMaxN], sv[kMaxN];
 #pragma unroll
@@ -387,14 +392,6 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     kv[t] = reinterpret_cast<const uint4*>(key + rr * key_sb + tt * key_st)[c];
     sv[t] = reinterpret_cast<const uint4*>(score + rr * score_sb + tt * score_st)[c];
   }
-  // Pin the token loads above the barrier: otherwise they are sunk below it
-  // and wait for the ape round trip instead of sharing it.
-#pragma unroll
-  for (int t = 0; t < kMaxN; ++t)
-    asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]), "v"(kv[t].x), "v"(kv[t].y),
-                 "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x), "v"(sv[t].y), "v"(sv[t].z),
-                 "v"(sv[t].w));
-  store_ape(s_ape, ape_regs);
   if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
 
   int32_t blk[kMaxN];
@@ -458,7 +455,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
       K[3] = k1;
     }
     float x[2];
-    pool_mean_wave(S, K, s_ape, c, q, x);
+    pool_mean_wave(S, K, A, x);
     float scale;
     const uint32_t codes = rotate_quantise64(x, c, q, kRoundScale, scale);
     if (l1 < sink.rows) sink.store2(l1, c, q, codes, scale);
