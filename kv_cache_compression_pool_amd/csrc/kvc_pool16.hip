@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
 // Ring decode for short verify batches (next_n <= kMaxN) with one request per
 // wave.  The same ordered semantics as pool16_ring_kernel:
 //  * every token's maps and key / score rows are requested up front, in the
-//    same round trip as the ape table;
+//    same round trip as the lane's ape values (kept in registers, so there is
+//    no LDS staging and no barrier);
 //  * the loop runs over completions, not tokens.  Before completion t* reads
 //    its ring block, the stashes of tokens [done, t*) are stored from the
 //    lanes that read those slots back: row q of the wave stashes and reads
