@@ -211,6 +211,9 @@ int kvc_compress_prefill_paged(const uint16_t* keys, int64_t key_row_stride,
  *   tail_slot_mapping, slot_mapping, positions  device int32 [num_requests,
  *                    next_n], contiguous; -1 marks padding.
  *   out_fp8, out_scale  device [num_out, 128] uint8 / [num_out] fp32.
+ *   dbg_pooled       device fp32 [num_out, 128] (16-byte aligned) or NULL:
+ *                    row slot_mapping[e] of every completion receives the fp32
+ *                    weighted mean before any rounding (for parity checks).
  * Errors: as kvc_compress_prefill. */
 int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                              const int32_t* tail_slot_mapping,
@@ -220,7 +223,7 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                              const int32_t* slot_mapping, const int32_t* positions,
                              int64_t num_requests, int next_n, int pool_size,
                              uint8_t* out_fp8, float* out_scale, int64_t num_out,
-                             int round_scale, void* stream);
+                             int round_scale, float* dbg_pooled, void* stream);
 
 /* kvc_compress_decode_ring writing completions into a page-size-1 paged cache
  * instead of packed arrays (the page's cache-write path): slot_mapping[e] is

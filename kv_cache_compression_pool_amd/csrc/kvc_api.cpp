@@ -325,7 +325,8 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                              int64_t score_stride_b, int64_t score_stride_t, const float* ape,
                              const int32_t* slot_mapping, const int32_t* positions,
                              int64_t num_requests, int next_n, int pool_size, uint8_t* out_fp8,
-                             float* out_scale, int64_t num_out, int round_scale, void* stream) {
+                             float* out_scale, int64_t num_out, int round_scale,
+                             float* dbg_pooled, void* stream) {
   const char* fn = "kvc_compress_decode_ring";
   if (pool_size != kPool) return fail(KVC_ERR_UNSUPPORTED, "%s: pool_size %d (only 16)", fn, pool_size);
   if (num_requests < 0 || next_n < 0 || num_ring_blocks < 0 || num_out < 0)
@@ -339,11 +340,13 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
   if (num_out > 0 && (!aligned(out_fp8, 8) || !aligned(out_scale, 4)))
     return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
   if (num_out > kMaxI32) return fail(KVC_ERR_SHAPE, "%s: num_out exceeds 2^31-1", fn);
+  if (dbg_pooled && !aligned(dbg_pooled, 16)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
   return hip_status(kvc::launch_pool16_ring(tail_ring, num_ring_blocks, tail_slot_mapping, key,
                                             key_stride_b, key_stride_t, score, score_stride_b,
                                             score_stride_t, ape, slot_mapping, positions,
                                             num_requests, next_n, out_fp8, out_scale, num_out,
-                                            false, round_scale != 0, (hipStream_t)stream),
+                                            false, round_scale != 0, dbg_pooled,
+                                            (hipStream_t)stream),
                     "kvc_compress_decode_ring launch");
 }
 
@@ -373,7 +376,8 @@ int kvc_compress_decode_ring_paged(uint16_t* tail_ring, int64_t num_ring_blocks,
                                             key_stride_b, key_stride_t, score, score_stride_b,
                                             score_stride_t, ape, slot_mapping, positions,
                                             num_requests, next_n, kv_cache, nullptr, num_pages,
-                                            true, round_scale != 0, (hipStream_t)stream),
+                                            true, round_scale != 0, nullptr,
+                                            (hipStream_t)stream),
                     "kvc_compress_decode_ring_paged launch");
 }
 

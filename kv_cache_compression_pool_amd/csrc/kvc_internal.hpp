@@ -27,7 +27,7 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                               const float* ape, const int32_t* slot_mapping,
                               const int32_t* positions, int64_t num_requests, int next_n,
                               uint8_t* out_fp8, float* out_scale, int64_t out_rows, bool paged,
-                              bool round_scale, hipStream_t stream);
+                              bool round_scale, float* dbg, hipStream_t stream);
 
 hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t* key,
                               int64_t key_stride, const uint16_t* score, int64_t score_stride,

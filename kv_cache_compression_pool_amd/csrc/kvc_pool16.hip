@@ -207,6 +207,7 @@ struct OutSink {
   float* scales;       // packed scales (unused when paged)
   int64_t rows;        // rows / pages available
   bool paged;
+  float* dbg;          // ring decode: fp32 [rows, 128] pre-rounding means, or null
   __device__ __forceinline__ void store(int64_t row, int c, int h, uint32_t code4,
                                         float scale) const {
     if (paged) {
@@ -333,6 +334,9 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
       }
       float x[8];
       pool_mean(S, K, s_ape, c, h, x);
+      if (sink.dbg && loc < sink.rows)
+        reinterpret_cast<float4*>(sink.dbg + (int64_t)loc * 128 + 8 * c)[h] =
+            h ? make_float4(x[4], x[5], x[6], x[7]) : make_float4(x[0], x[1], x[2], x[3]);
       float scale;
       const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
       if (loc < sink.rows) sink.store(loc, c, h, codes, scale);
@@ -457,6 +461,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     }
     float x[2];
     pool_mean_wave(S, K, A, x);
+    if (sink.dbg && l1 < sink.rows)   // channels 8c + 2q + t
+      reinterpret_cast<float2*>(sink.dbg + (int64_t)l1 * 128)[4 * c + q] = make_float2(x[0], x[1]);
     float scale;
     const uint32_t codes = rotate_quantise64(x, c, q, kRoundScale, scale);
     if (l1 < sink.rows) sink.store2(l1, c, q, codes, scale);
@@ -500,7 +506,7 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
   if (num_rows < kPool || n_pools <= 0) return hipSuccess;   // no pool can be complete
   const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
-  const OutSink sink{out_fp8, out_scale, out_rows, paged};
+  const OutSink sink{out_fp8, out_scale, out_rows, paged, nullptr};
 #define KVC_LAUNCH(RS, DBG)                                                                   \
   hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG>), grid, block, 0, stream, keys,          \
                      key_stride, scores, score_stride, num_rows, ape, src_rows, n_pools,     \
@@ -520,9 +526,9 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                               const float* ape, const int32_t* slot_mapping,
                               const int32_t* positions, int64_t num_requests, int next_n,
                               uint8_t* out_fp8, float* out_scale, int64_t out_rows, bool paged,
-                              bool round_scale, hipStream_t stream) {
+                              bool round_scale, float* dbg, hipStream_t stream) {
   const dim3 block(kBlock);
-  const OutSink sink{out_fp8, out_scale, out_rows, paged};
+  const OutSink sink{out_fp8, out_scale, out_rows, paged, dbg};
   constexpr int kWaveReq = kBlock / 64;
   dim3 grid((unsigned)((num_requests + kWaveReq - 1) / kWaveReq));
 #define KVC_RING(KERNEL)                                                                      \

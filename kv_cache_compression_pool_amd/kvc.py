@@ -64,7 +64,8 @@ def lib() -> ctypes.CDLL:
         L.kvc_compress_prefill.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i32, _p, _i64, _p, _p,
                                            _i32, _p, _p]
         L.kvc_compress_decode_ring.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p,
-                                               _p, _p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p]
+                                               _p, _p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p,
+                                               _p]
         L.kvc_compress_prefill_paged.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i32, _p, _i64,
                                                  _p, _i64, _i32, _p, _p, _i32, _p]
         L.kvc_compress_decode_ring_paged.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64,
@@ -274,9 +275,10 @@ def kvc_compress_decode_ring_paged(tail_ring, tail_slot_mapping, key, score, ape
 
 def kvc_compress_decode_ring(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,
                              positions, out_fp8, out_scale, round_scale: bool,
-                             pool_size: int = 16, stream=None):
+                             pool_size: int = 16, stream=None, dbg_pooled=None):
     """tail_ring bf16 [nb,2,16,128] (updated); key/score bf16 [R,next_n,128];
-    maps int32 [R,next_n]; out_fp8 uint8 [num_out,128]; out_scale fp32 [num_out]."""
+    maps int32 [R,next_n]; out_fp8 uint8 [num_out,128]; out_scale fp32 [num_out];
+    dbg_pooled fp32 [num_out,128] or None (pre-rounding means of completions)."""
     import torch
     ring = _bf16_view(tail_ring, "tail_ring", min_last=None)
     k = _bf16_view(key, "key", min_last=None)
@@ -295,13 +297,18 @@ def kvc_compress_decode_ring(tail_ring, tail_slot_mapping, key, score, ape, slot
           "out_fp8 must be a contiguous [num_out, 128] tensor")
     _need(out_scale.dim() == 1 and out_scale.shape[0] >= out_fp8.shape[0],
           "out_scale must hold num_out entries")
+    if dbg_pooled is not None:
+        _need(dbg_pooled.dim() == 2 and dbg_pooled.shape[0] >= out_fp8.shape[0]
+              and dbg_pooled.shape[1] == 128 and dbg_pooled.is_contiguous(),
+              "dbg_pooled must be a contiguous [num_out, 128] tensor")
     _check(lib().kvc_compress_decode_ring(
         ring.data_ptr(), ring.shape[0], _dptr(tail_slot_mapping, torch.int32, "tail_slot_mapping"),
         k.data_ptr(), k.stride(0), k.stride(1), s.data_ptr(), s.stride(0), s.stride(1),
         _dptr(ape, torch.float32, "ape"), _dptr(slot_mapping, torch.int32, "slot_mapping"),
         _dptr(positions, torch.int32, "positions"), R, N, pool_size,
         _dptr(out_fp8, torch.uint8, "out_fp8"), _dptr(out_scale, torch.float32, "out_scale"),
-        out_fp8.shape[0], int(round_scale), _stream(stream)))
+        out_fp8.shape[0], int(round_scale),
+        _dptr(dbg_pooled, torch.float32, "dbg_pooled", optional=True), _stream(stream)))
 
 
 def kvc_seed_tail_ring(tail_ring, key, score, tslot, pool_size: int = 16, stream=None):

@@ -153,11 +153,13 @@ def test_device_entry_points_validate_before_launch():
     assert L.kvc_compress_prefill(None, 0, None, 0, 0, None, 16, None, 0, None, None, 1, None,
                                   None) == kvc.KVC_OK
     assert L.kvc_compress_decode_ring(None, 0, None, None, 0, 0, None, 0, 0, None, None, None, 0,
-                                      4, 16, None, None, 0, 1, None) == kvc.KVC_OK
+                                      4, 16, None, None, 0, 1, None, None) == kvc.KVC_OK
     assert L.kvc_compress_decode_ring(p, 4, p, p, 512, 128, p, 512, 128, p, p, p, 4, 4, 12, p, p,
-                                      4, 1, None) == kvc.KVC_ERR_UNSUPPORTED
+                                      4, 1, None, None) == kvc.KVC_ERR_UNSUPPORTED
     assert L.kvc_compress_decode_ring(p, 4, p, p, 500, 128, p, 512, 128, p, p, p, 4, 4, 16, p, p,
-                                      4, 1, None) == kvc.KVC_ERR_SHAPE
+                                      4, 1, None, None) == kvc.KVC_ERR_SHAPE
+    assert L.kvc_compress_decode_ring(p, 4, p, p, 512, 128, p, 512, 128, p, p, p, 4, 4, 16, p, p,
+                                      4, 1, ctypes.c_void_p(0x1008), None) == kvc.KVC_ERR_SHAPE
     assert L.kvc_c128_online_decode(None, 0, None, None, None, None, None, 0, None) == kvc.KVC_OK
     assert L.kvc_c128_online_decode(p, 4, None, p, p, p, p, 2, None) == kvc.KVC_ERR_NULL
     assert L.kvc_c128_online_decode(p, 4, ctypes.c_void_p(0x1004), p, p, p, p, 2, None) \

@@ -71,12 +71,22 @@ def reference_for(gx, rx, rc, rs, round_scale, what):
     n = rx.shape[0]
     gb = oracle.bf16_rne(gx.ravel()).reshape(n, 128)
     rb = oracle.bf16_rne(rx.ravel()).reshape(n, 128)
-    flip = (gb != rb).any(axis=1)
+    ch = gb != rb
+    flip = ch.any(axis=1)
     ref_c, ref_s = rc.copy(), rs.copy()
     if flip.any():
+        # Every channel that rounds differently must be explained by fp32
+        # accumulation error, which is absolute on the vector's scale (so
+        # channels near zero flip most): the two means of that channel differ
+        # by at most 64 fp32 ulps of the vector's max-abs value.
+        vmax = np.abs(rx).max(axis=1, keepdims=True)
+        near = np.abs(gx.astype(np.float64) - rx) <= 64 * 2.0**-23 * vmax
+        assert np.all(near[ch]), f"{what}: a channel rounds differently beyond fp32 error"
         ref_c[flip], ref_s[flip] = oracle.pool_epilogue(gx[flip], round_scale)
-    assert flip.sum() <= max(2, 0.02 * n), f"{what}: {flip.sum()} of {n} pools round differently"
+    # A rounding-mode error would flip about half of all channels.
+    assert flip.sum() <= max(8, 0.05 * n), f"{what}: {flip.sum()} of {n} pools round differently"
     return ref_c, ref_s, int(flip.sum())
+
 
 
 # ------------------------------------------------------------------ pool-16 prefill
@@ -219,7 +229,9 @@ def test_device_bf16_rounding_matches_oracle():
 # ------------------------------------------------------------------ pool-16 ring decode
 def run_ring(d):
     """Run ring decode on both sides; return GPU ring / codes / scales and the
-    reference ring / codes / scales (bf16-boundary aware, see reference_for)."""
+    reference ring / codes / scales (bf16-boundary aware, see reference_for:
+    the ring kernel's own fp32 means, from its dbg_pooled output, decide which
+    pools round differently)."""
     ring = d["ring"].copy()
     n_out = d["num_out"]
     rc = np.full((n_out, 128), 0x33, np.uint8)
@@ -232,26 +244,23 @@ def run_ring(d):
     gring = dev(d["ring"], torch.int16)
     go = torch.full((n_out, 128), 0x33, dtype=torch.uint8, device="cuda")
     gs = torch.full((n_out,), 5.0, device="cuda")
+    gx = torch.full((n_out, 128), float("nan"), device="cuda")
     kvc.kvc_compress_decode_ring(gring, dev(d["tail_slot_mapping"]), dev(d["key"], torch.int16),
                                  dev(d["score"], torch.int16), dev(d["ape"]),
                                  dev(d["slot_mapping"]), dev(d["positions"]), go, gs,
-                                 d["round_scale"])
+                                 d["round_scale"], dbg_pooled=gx)
     torch.cuda.synchronize()
-    gc, gsc = go.cpu().numpy(), gs.cpu().numpy()
-    # Pooled means of the completed pools, from the same device code (the
-    # prefill kernel with its diagnostic output) on the gathered pools.
+    gc, gsc, gx = go.cpu().numpy(), gs.cpu().numpy(), gx.cpu().numpy()
     done = np.nonzero(rs != 5.0)[0]
+    assert np.array_equal(np.nonzero(~np.isnan(gx[:, 0]))[0], done), "completed rows differ"
     ref_c, ref_s = rc.copy(), rs.copy()
     if done.size:
-        keys = pk[done].reshape(-1, 128)
-        scores = ps[done].reshape(-1, 128)
-        pc, pscale, px = run_prefill_gpu(keys, scores, d["ape"], None, done.size,
-                                         d["round_scale"])
-        assert np.array_equal(pc[:done.size], gc[done]), "ring and prefill kernels disagree"
-        assert np.array_equal(pscale[:done.size], gsc[done])
-        _, _, ox = oracle.compress_prefill(keys, scores, d["ape"], None, d["round_scale"])
-        assert rel_err_rows(px[:done.size], ox).max() <= VEC_TOL
-        c2, s2, flips = reference_for(px[:done.size], ox, rc[done], rs[done], d["round_scale"],
+        # the oracle's pooled means of the same 16-slot pools
+        _, _, ox = oracle.compress_prefill(pk[done].reshape(-1, 128), ps[done].reshape(-1, 128),
+                                           d["ape"], None, d["round_scale"])
+        e = rel_err_rows(gx[done], ox).max()
+        assert e <= VEC_TOL, f"ring decode: fp32 mean rel err {e:.3g}"
+        c2, s2, flips = reference_for(gx[done], ox, rc[done], rs[done], d["round_scale"],
                                       "ring decode")
         ref_c[done], ref_s[done] = c2, s2
     return gring.cpu().numpy().view(np.uint16), gc, gsc, ring, ref_c, ref_s
