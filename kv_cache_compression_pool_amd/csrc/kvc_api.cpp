@@ -45,7 +45,7 @@ constexpr int64_t kMaxI32 = 0x7fffffffLL;
 
 extern "C" {
 
-int kvc_version(void) { return 100; }
+int kvc_version(void) { return 200; }
 
 const char* kvc_last_error(void) { return g_last_error.c_str(); }
 
