@@ -313,8 +313,35 @@ def bench_ring(args, torch, kvc, synth, stream):
 
     steps = max(args.steps, 50)
     total_ms, ev_ms, host = timed(step, steps, max(args.warmup, 5), torch, stream)
-    return dict(requests=R_req, next_n=N, completions=comps, total_ms=total_ms, steps=steps,
-                ev_ms=ev_ms, host_s=host, alg_bytes=alg)
+    res = dict(requests=R_req, next_n=N, completions=comps, total_ms=total_ms, steps=steps,
+               ev_ms=ev_ms, host_s=host, alg_bytes=alg)
+
+    # Multi-layer form: the same requests and tokens in each of `layers`
+    # layers (own ring, keys, scores and ape per layer) in one launch; the
+    # maps are shared, so their bytes count once.
+    layers = args.decode_layers
+    if layers:
+        per_layer = alg - int(valid.sum()) * 12
+        alg_l = per_layer * layers + int(valid.sum()) * 12
+        per_rep = layers * (ring.numel() + key.numel() + score.numel()) * 2
+        RL = max(2, -(-(2 * MALL_BYTES) // per_rep))
+        rings = [ring.unsqueeze(0).repeat(layers, 1, 1, 1, 1) for _ in range(RL)]
+        keys = [key.unsqueeze(0).repeat(layers, 1, 1, 1) for _ in range(RL)]
+        scores = [score.unsqueeze(0).repeat(layers, 1, 1, 1) for _ in range(RL)]
+        ape_l = ape.unsqueeze(0).repeat(layers, 1, 1).contiguous()
+        out_l = torch.empty((layers, d["num_out"], 128), dtype=torch.uint8, device="cuda")
+        scl_l = torch.empty((layers, d["num_out"]), device="cuda")
+
+        def step_l(i):
+            r = i % RL
+            kvc.kvc_compress_decode_ring_layers(rings[r], ts, keys[r], scores[r], ape_l, sm, pos,
+                                                out_l, scl_l, True)
+
+        n_l = max(args.steps // 4, 20)
+        tl, evl, _ = timed(step_l, n_l, 3, torch, stream)
+        res["layers"] = dict(layers=layers, total_ms=tl, ev_ms=evl, steps=n_l, alg_bytes=alg_l,
+                             replicas=RL)
+    return res
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -381,7 +408,7 @@ def main():
                     help="prefill: the headline kernel only (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-layers", type=int, default=64,
-                    help="layers in the multi-layer c128 decode measurement (0: skip)")
+                    help="layers in the multi-layer decode measurements (0: skip)")
     ap.add_argument("--prefill-seqs", type=int, default=64,
                     help="sequences in the pool-16 prefill batch (64 is the configured "
                          "workload; other sizes show how the rate depends on batch size)")
@@ -491,6 +518,15 @@ def main():
             "tokens_per_s": round(c3["requests"] * c3["next_n"] * c3["steps"] / (c3["total_ms"] * 1e-3), 1),
             "launch_us": round(c3["ev_ms"] * 1e3, 3), "bytes_per_launch": c3["alg_bytes"],
             "hbm_gbs": round(g3, 1), "hbm_frac": round(g3 / PEAK_HBM_GBS, 4)}
+        if "layers" in c3:
+            cl = c3["layers"]
+            gl = gbs(cl["alg_bytes"], cl["ev_ms"])
+            line["ring_decode"]["multi_layer"] = {
+                "layers": cl["layers"], "launch_us": round(cl["ev_ms"] * 1e3, 3),
+                "tokens_per_s": round(c3["requests"] * c3["next_n"] * cl["layers"]
+                                      / (cl["ev_ms"] * 1e-3), 1),
+                "bytes_per_launch": cl["alg_bytes"], "hbm_gbs": round(gl, 1),
+                "hbm_frac": round(gl / PEAK_HBM_GBS, 4), "replicas": cl["replicas"]}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(p)

@@ -225,6 +225,31 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
                              uint8_t* out_fp8, float* out_scale, int64_t num_out,
                              int round_scale, float* dbg_pooled, void* stream);
 
+/* Multi-layer form of kvc_compress_decode_ring: the same requests and tokens
+ * (tail_slot_mapping, slot_mapping, positions are shared) in each of
+ * num_layers layers, in one launch.  Layer l uses tail_ring +
+ * l*ring_layer_stride, key + l*key_layer_stride, score + l*score_layer_stride
+ * (bf16 elements, multiples of 8), ape + l*ape_layer_stride (floats,
+ * multiple of 4), and writes out_fp8 rows / out_scale entries
+ * l*num_out .. l*num_out + num_out - 1 (out_fp8 [num_layers, num_out, 128],
+ * out_scale [num_layers, num_out]).  Each layer behaves exactly as a
+ * separate kvc_compress_decode_ring call.  For callers that run the ring
+ * decode of every layer of a model at once: one launch instead of
+ * num_layers latency-bound ones.
+ * Errors: as kvc_compress_decode_ring; KVC_ERR_SHAPE for num_layers > 65535
+ *         or layer strides that do not step over a whole layer. */
+int kvc_compress_decode_ring_layers(uint16_t* tail_ring, int64_t ring_layer_stride,
+                                    int64_t num_ring_blocks, const int32_t* tail_slot_mapping,
+                                    const uint16_t* key, int64_t key_layer_stride,
+                                    int64_t key_stride_b, int64_t key_stride_t,
+                                    const uint16_t* score, int64_t score_layer_stride,
+                                    int64_t score_stride_b, int64_t score_stride_t,
+                                    const float* ape, int64_t ape_layer_stride,
+                                    const int32_t* slot_mapping, const int32_t* positions,
+                                    int64_t num_requests, int next_n, int pool_size,
+                                    uint8_t* out_fp8, float* out_scale, int64_t num_out,
+                                    int64_t num_layers, int round_scale, void* stream);
+
 /* kvc_compress_decode_ring writing completions into a page-size-1 paged cache
  * instead of packed arrays (the page's cache-write path): slot_mapping[e] is
  * the page; pages outside [0, num_pages) are skipped.  kv_cache as in

@@ -319,19 +319,25 @@ int kvc_compress_prefill_paged(const uint16_t* keys, int64_t key_row_stride,
                     "kvc_compress_prefill_paged launch");
 }
 
-int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
-                             const int32_t* tail_slot_mapping, const uint16_t* key,
-                             int64_t key_stride_b, int64_t key_stride_t, const uint16_t* score,
-                             int64_t score_stride_b, int64_t score_stride_t, const float* ape,
-                             const int32_t* slot_mapping, const int32_t* positions,
-                             int64_t num_requests, int next_n, int pool_size, uint8_t* out_fp8,
-                             float* out_scale, int64_t num_out, int round_scale,
-                             float* dbg_pooled, void* stream) {
-  const char* fn = "kvc_compress_decode_ring";
+}  // extern "C"
+
+namespace {
+
+// Packed-output ring decode over num_layers layers (layer strides in
+// elements; ignored for one layer).
+int ring_decode_packed(const char* fn, uint16_t* tail_ring, int64_t ring_ls,
+                       int64_t num_ring_blocks, const int32_t* tail_slot_mapping,
+                       const uint16_t* key, int64_t key_ls, int64_t key_stride_b,
+                       int64_t key_stride_t, const uint16_t* score, int64_t score_ls,
+                       int64_t score_stride_b, int64_t score_stride_t, const float* ape,
+                       int64_t ape_ls, const int32_t* slot_mapping, const int32_t* positions,
+                       int64_t num_requests, int next_n, int pool_size, uint8_t* out_fp8,
+                       float* out_scale, int64_t num_out, int64_t num_layers, int round_scale,
+                       float* dbg_pooled, void* stream) {
   if (pool_size != kPool) return fail(KVC_ERR_UNSUPPORTED, "%s: pool_size %d (only 16)", fn, pool_size);
-  if (num_requests < 0 || next_n < 0 || num_ring_blocks < 0 || num_out < 0)
+  if (num_requests < 0 || next_n < 0 || num_ring_blocks < 0 || num_out < 0 || num_layers < 0)
     return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
-  if (num_requests == 0 || next_n == 0) return ok();
+  if (num_requests == 0 || next_n == 0 || num_layers == 0) return ok();
   int rc = check_ring_inputs(fn, tail_ring, tail_slot_mapping, key, key_stride_b, key_stride_t,
                              score, score_stride_b, score_stride_t, ape, slot_mapping, positions,
                              num_requests, next_n);
@@ -341,13 +347,65 @@ int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
     return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
   if (num_out > kMaxI32) return fail(KVC_ERR_SHAPE, "%s: num_out exceeds 2^31-1", fn);
   if (dbg_pooled && !aligned(dbg_pooled, 16)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  if (num_layers > 65535) return fail(KVC_ERR_SHAPE, "%s: num_layers exceeds 65535", fn);
+  if (num_layers > 1) {
+    // Each layer stride must step over a whole layer of its buffer.
+    const int64_t key_extent = (num_requests - 1) * key_stride_b + (next_n - 1) * key_stride_t + 128;
+    const int64_t score_extent =
+        (num_requests - 1) * score_stride_b + (next_n - 1) * score_stride_t + 128;
+    if (ring_ls < num_ring_blocks * 2 * kPool * kHeadDim || ring_ls % 8 || key_ls < key_extent ||
+        key_ls % 8 || score_ls < score_extent || score_ls % 8 || ape_ls < kPool * kHeadDim ||
+        ape_ls % 4)
+      return fail(KVC_ERR_SHAPE, "%s: layer strides overlap layers or break alignment", fn);
+  } else {
+    ring_ls = key_ls = score_ls = ape_ls = 0;
+  }
   return hip_status(kvc::launch_pool16_ring(tail_ring, num_ring_blocks, tail_slot_mapping, key,
                                             key_stride_b, key_stride_t, score, score_stride_b,
                                             score_stride_t, ape, slot_mapping, positions,
                                             num_requests, next_n, out_fp8, out_scale, num_out,
-                                            false, round_scale != 0, dbg_pooled,
+                                            false, round_scale != 0, dbg_pooled, num_layers,
+                                            ring_ls, key_ls, score_ls, ape_ls,
                                             (hipStream_t)stream),
-                    "kvc_compress_decode_ring launch");
+                    fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_compress_decode_ring(uint16_t* tail_ring, int64_t num_ring_blocks,
+                             const int32_t* tail_slot_mapping, const uint16_t* key,
+                             int64_t key_stride_b, int64_t key_stride_t, const uint16_t* score,
+                             int64_t score_stride_b, int64_t score_stride_t, const float* ape,
+                             const int32_t* slot_mapping, const int32_t* positions,
+                             int64_t num_requests, int next_n, int pool_size, uint8_t* out_fp8,
+                             float* out_scale, int64_t num_out, int round_scale,
+                             float* dbg_pooled, void* stream) {
+  return ring_decode_packed("kvc_compress_decode_ring", tail_ring, 0, num_ring_blocks,
+                            tail_slot_mapping, key, 0, key_stride_b, key_stride_t, score, 0,
+                            score_stride_b, score_stride_t, ape, 0, slot_mapping, positions,
+                            num_requests, next_n, pool_size, out_fp8, out_scale, num_out, 1,
+                            round_scale, dbg_pooled, stream);
+}
+
+int kvc_compress_decode_ring_layers(uint16_t* tail_ring, int64_t ring_layer_stride,
+                                    int64_t num_ring_blocks, const int32_t* tail_slot_mapping,
+                                    const uint16_t* key, int64_t key_layer_stride,
+                                    int64_t key_stride_b, int64_t key_stride_t,
+                                    const uint16_t* score, int64_t score_layer_stride,
+                                    int64_t score_stride_b, int64_t score_stride_t,
+                                    const float* ape, int64_t ape_layer_stride,
+                                    const int32_t* slot_mapping, const int32_t* positions,
+                                    int64_t num_requests, int next_n, int pool_size,
+                                    uint8_t* out_fp8, float* out_scale, int64_t num_out,
+                                    int64_t num_layers, int round_scale, void* stream) {
+  return ring_decode_packed("kvc_compress_decode_ring_layers", tail_ring, ring_layer_stride,
+                            num_ring_blocks, tail_slot_mapping, key, key_layer_stride,
+                            key_stride_b, key_stride_t, score, score_layer_stride,
+                            score_stride_b, score_stride_t, ape, ape_layer_stride, slot_mapping,
+                            positions, num_requests, next_n, pool_size, out_fp8, out_scale,
+                            num_out, num_layers, round_scale, nullptr, stream);
 }
 
 int kvc_compress_decode_ring_paged(uint16_t* tail_ring, int64_t num_ring_blocks,
@@ -376,7 +434,7 @@ int kvc_compress_decode_ring_paged(uint16_t* tail_ring, int64_t num_ring_blocks,
                                             key_stride_b, key_stride_t, score, score_stride_b,
                                             score_stride_t, ape, slot_mapping, positions,
                                             num_requests, next_n, kv_cache, nullptr, num_pages,
-                                            true, round_scale != 0, nullptr,
+                                            true, round_scale != 0, nullptr, 1, 0, 0, 0, 0,
                                             (hipStream_t)stream),
                     "kvc_compress_decode_ring_paged launch");
 }

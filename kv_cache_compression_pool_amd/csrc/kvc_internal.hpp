@@ -21,13 +21,18 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
                                  const int64_t* loc, const uint8_t* write_mask, bool round_scale,
                                  float* dbg, hipStream_t stream);
 
+// Ring decode over num_layers layers (blockIdx.y): layer l reads ring / key /
+// score / ape at the given layer strides (elements; 0 for one layer) and
+// writes output rows l*out_rows .. l*out_rows + out_rows - 1 of the sink.
 hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t* tail_slot,
                               const uint16_t* key, int64_t key_sb, int64_t key_st,
                               const uint16_t* score, int64_t score_sb, int64_t score_st,
                               const float* ape, const int32_t* slot_mapping,
                               const int32_t* positions, int64_t num_requests, int next_n,
                               uint8_t* out_fp8, float* out_scale, int64_t out_rows, bool paged,
-                              bool round_scale, float* dbg, hipStream_t stream);
+                              bool round_scale, float* dbg, int64_t num_layers,
+                              int64_t ring_ls, int64_t key_ls, int64_t score_ls, int64_t ape_ls,
+                              hipStream_t stream);
 
 hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t* key,
                               int64_t key_stride, const uint16_t* score, int64_t score_stride,

@@ -219,6 +219,14 @@ struct OutSink {
       if (c == 0 && h == 0) scales[row] = scale;
     }
   }
+  // The same sink advanced by `rows` rows (the next layer's outputs).
+  __device__ __forceinline__ OutSink advanced(int64_t rows_by) const {
+    OutSink o = *this;
+    o.codes += rows_by * (paged ? kPagedBytes : 128);
+    if (!paged) o.scales += rows_by;
+    if (dbg) o.dbg += rows_by * 128;
+    return o;
+  }
   // Whole-wave layout: lane 16q + c stores the codes of channels 8c + 2q and
   // 8c + 2q + 1 (low 16 bits of code2).
   __device__ __forceinline__ void store2(int64_t row, int c, int q, uint32_t code2,
@@ -283,6 +291,13 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   sink.store(dst, c, h, codes, scale);
 }
 
+// Per-layer strides of a multi-layer ring decode (blockIdx.y = layer): ring,
+// key and score in bf16 elements, ape in floats, outputs in rows.  All zero
+// for a single layer.
+struct RingLayers {
+  int64_t ring, key, score, ape, out_rows;
+};
+
 // Tail-ring decode: 32 lanes per request (row h owns ring slots 8h..8h+7),
 // tokens strictly in order.  A token's key / score row is stashed by the row
 // that later reads that slot in a completion, so every ring read sees the
@@ -293,7 +308,16 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
     const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
     const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
     const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
-    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink) {
+    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink,
+    RingLayers ls) {
+  {
+    const int64_t layer = blockIdx.y;
+    ring += layer * ls.ring;
+    key += layer * ls.key;
+    score += layer * ls.score;
+    ape += layer * ls.ape;
+    sink = sink.advanced(layer * ls.out_rows);
+  }
   __shared__ float4 s_ape[kPool * 32];
   stage_ape(s_ape, ape);
 
@@ -352,8 +376,10 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
 // Ring decode for short verify batches (next_n <= kMaxN) with one request per
 // wave.  The same ordered semantics as pool16_ring_kernel:
 //  * every token's maps and key / score rows are requested up front, in the
-//    same round trip as the lane's ape values (kept in registers, so there is
-//    no LDS staging and no barrier);
+//    same round trip as the ape table (staged in LDS; keeping each lane's
+//    ape values in registers instead measured no faster for one call and
+//    20% slower for multi-layer launches, whose occupancy the extra 24 VGPRs
+//    cut from 3 to 2 waves per SIMD);
 //  * the loop runs over completions, not tokens.  Before completion t* reads
 //    its ring block, the stashes of tokens [done, t*) are stored from the
 //    lanes that read those slots back: row q of the wave stashes and reads
@@ -368,7 +394,16 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
     const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
     const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
-    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink) {
+    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink,
+    RingLayers ls) {
+  {
+    const int64_t layer = blockIdx.y;
+    ring += layer * ls.ring;
+    key += layer * ls.key;
+    score += layer * ls.score;
+    ape += layer * ls.ape;
+    sink = sink.advanced(layer * ls.out_rows);
+  }
   static_assert(kMaxN <= 32, "completion mask is 32 bits");
   constexpr int kReqPerBlock = kBlock / 64;
   const int c = threadIdx.x & 15;
@@ -376,15 +411,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   const int64_t r = (int64_t)blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
   const int64_t rr = r < num_requests ? r : 0;   // waves past the batch read request 0, stop below
 
-  // Each lane keeps the ape values of its 4 slots x 8 channels in registers
-  // (L2-resident 8 KB table): no LDS staging, so no barrier in the chain.
-  float4 A[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4* ap = reinterpret_cast<const float4*>(ape) + (4 * q + i) * 32 + 2 * c;
-    A[i][0] = ap[0];
-    A[i][1] = ap[1];
-  }
+  __shared__ float4 s_ape[kPool * 32];
+  const ApeRegs ape_regs = load_ape(ape);
   int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
   uint4 kv[kMaxN], sv[kMaxN];
 #pragma unroll
@@ -397,6 +425,14 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     kv[t] = reinterpret_cast<const uint4*>(key + rr * key_sb + tt * key_st)[c];
     sv[t] = reinterpret_cast<const uint4*>(score + rr * score_sb + tt * score_st)[c];
   }
+  // Pin the token loads above the barrier: otherwise they are sunk below it
+  // and wait for the ape round trip instead of sharing it.
+#pragma unroll
+  for (int t = 0; t < kMaxN; ++t)
+    asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]), "v"(kv[t].x), "v"(kv[t].y),
+                 "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x), "v"(sv[t].y), "v"(sv[t].z),
+                 "v"(sv[t].w));
+  store_ape(s_ape, ape_regs);
   if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
 
   int32_t blk[kMaxN];
@@ -460,6 +496,12 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
       K[3] = k1;
     }
     float x[2];
+    float4 A[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      A[i][0] = s_ape[(4 * q + i) * 32 + 2 * c];
+      A[i][1] = s_ape[(4 * q + i) * 32 + 2 * c + 1];
+    }
     pool_mean_wave(S, K, A, x);
     if (sink.dbg && l1 < sink.rows)   // channels 8c + 2q + t
       reinterpret_cast<float2*>(sink.dbg + (int64_t)l1 * 128)[4 * c + q] = make_float2(x[0], x[1]);
@@ -526,15 +568,18 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                               const float* ape, const int32_t* slot_mapping,
                               const int32_t* positions, int64_t num_requests, int next_n,
                               uint8_t* out_fp8, float* out_scale, int64_t out_rows, bool paged,
-                              bool round_scale, float* dbg, hipStream_t stream) {
+                              bool round_scale, float* dbg, int64_t num_layers,
+                              int64_t ring_ls, int64_t key_ls, int64_t score_ls, int64_t ape_ls,
+                              hipStream_t stream) {
   const dim3 block(kBlock);
   const OutSink sink{out_fp8, out_scale, out_rows, paged, dbg};
+  const RingLayers ls{ring_ls, key_ls, score_ls, ape_ls, out_rows};
   constexpr int kWaveReq = kBlock / 64;
-  dim3 grid((unsigned)((num_requests + kWaveReq - 1) / kWaveReq));
+  dim3 grid((unsigned)((num_requests + kWaveReq - 1) / kWaveReq), (unsigned)num_layers);
 #define KVC_RING(KERNEL)                                                                      \
   hipLaunchKernelGGL(KERNEL, grid, block, 0, stream, ring, num_blocks, tail_slot, key, key_sb, \
                      key_st, score, score_sb, score_st, ape, slot_mapping, positions,           \
-                     num_requests, next_n, sink)
+                     num_requests, next_n, sink, ls)
   if (next_n <= 4) {
     if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 4>));
     else KVC_RING((pool16_ring_wave_kernel<false, 4>));
@@ -542,7 +587,8 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
     if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 8>));
     else KVC_RING((pool16_ring_wave_kernel<false, 8>));
   } else {
-    grid = dim3((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock));
+    grid = dim3((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock),
+                (unsigned)num_layers);
     if (round_scale) KVC_RING((pool16_ring_kernel<true>));
     else KVC_RING((pool16_ring_kernel<false>));
   }

@@ -30,7 +30,8 @@ ITEM_DTYPE = np.dtype([("compress", PLAN_DTYPE), ("write", PLAN_DTYPE)])
 
 EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_plan_prefill",
            "kvc_compress_prefill", "kvc_compress_prefill_paged", "kvc_compress_decode_ring",
-           "kvc_compress_decode_ring_paged", "kvc_seed_tail_ring",
+           "kvc_compress_decode_ring_paged", "kvc_compress_decode_ring_layers",
+           "kvc_seed_tail_ring",
            "kvc_c128_online_decode", "kvc_c128_online_decode_layers",
            "kvc_c128_online_decode_quant", "kvc_c128_online_prefill",
            "kvc_c128_online_prefill_quant", "kvc_c128_plan_prefill_fused",
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.kvc_compress_decode_ring.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64, _p,
                                                _p, _p, _i64, _i32, _i32, _p, _p, _i64, _i32, _p,
                                                _p]
+        L.kvc_compress_decode_ring_layers.argtypes = [_p, _i64, _i64, _p, _p, _i64, _i64, _i64,
+                                                      _p, _i64, _i64, _i64, _p, _i64, _p, _p,
+                                                      _i64, _i32, _i32, _p, _p, _i64, _i64, _i32,
+                                                      _p]
         L.kvc_compress_prefill_paged.argtypes = [_p, _i64, _p, _i64, _i64, _p, _i32, _p, _i64,
                                                  _p, _i64, _i32, _p, _p, _i32, _p]
         L.kvc_compress_decode_ring_paged.argtypes = [_p, _i64, _p, _p, _i64, _i64, _p, _i64, _i64,
@@ -242,6 +247,46 @@ def kvc_compress_prefill_paged(keys, scores, ape, pool_src_row, n_pools: int, kv
         _dptr(pool_src_row, torch.int32, "pool_src_row", optional=True), n_pools,
         _dptr(kv_cache, torch.uint8, "kv_cache"), kv_cache.numel() // 132, 1,
         _dptr(loc, torch.int64, "loc"), wm, int(round_scale), _stream(stream)))
+
+
+def kvc_compress_decode_ring_layers(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,
+                                    positions, out_fp8, out_scale, round_scale: bool,
+                                    pool_size: int = 16, stream=None):
+    """Multi-layer ring decode: tail_ring bf16 [L,nb,2,16,128]; key/score bf16
+    [L,R,next_n,128] (per-layer views with a common layer stride); ape fp32
+    [L,16,128]; maps int32 [R,next_n] shared by all layers; out_fp8 uint8
+    [L,num_out,128]; out_scale fp32 [L,num_out]."""
+    import torch
+    ring = _bf16_view(tail_ring, "tail_ring", min_last=None)
+    k = _bf16_view(key, "key", min_last=None)
+    s = _bf16_view(score, "score", min_last=None)
+    _need(ring.dim() == 5 and ring.is_contiguous() and tuple(ring.shape[2:]) == (2, pool_size, 128),
+          f"tail_ring must be a contiguous [L, nb, 2, {pool_size}, 128] tensor")
+    L = ring.shape[0]
+    _need(k.dim() == 4 and k.shape[0] == L and k.shape[3] == 128 and tuple(s.shape) == tuple(k.shape),
+          "key and score must be [L, R, next_n, 128]")
+    R, N = k.shape[1], k.shape[2]
+    for name, t in (("tail_slot_mapping", tail_slot_mapping), ("slot_mapping", slot_mapping),
+                    ("positions", positions)):
+        if tuple(t.shape) != (R, N) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{R}, {N}] tensor")
+    _need(ape.dim() == 3 and tuple(ape.shape) == (L, pool_size, 128) and ape.is_contiguous(),
+          f"ape must be a contiguous [L, {pool_size}, 128] tensor")
+    _need(out_fp8.dim() == 3 and out_fp8.shape[0] == L and out_fp8.shape[2] == 128
+          and out_fp8.is_contiguous(), "out_fp8 must be a contiguous [L, num_out, 128] tensor")
+    num_out = out_fp8.shape[1]
+    _need(tuple(out_scale.shape) == (L, num_out) and out_scale.is_contiguous(),
+          "out_scale must be a contiguous [L, num_out] tensor")
+    _check(lib().kvc_compress_decode_ring_layers(
+        ring.data_ptr(), ring.stride(0), ring.shape[1],
+        _dptr(tail_slot_mapping, torch.int32, "tail_slot_mapping"),
+        k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
+        s.data_ptr(), s.stride(0), s.stride(1), s.stride(2),
+        _dptr(ape, torch.float32, "ape"), ape.stride(0),
+        _dptr(slot_mapping, torch.int32, "slot_mapping"), _dptr(positions, torch.int32, "positions"),
+        R, N, pool_size, _dptr(out_fp8, torch.uint8, "out_fp8"),
+        _dptr(out_scale, torch.float32, "out_scale"), num_out, L, int(round_scale),
+        _stream(stream)))
 
 
 def kvc_compress_decode_ring_paged(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,

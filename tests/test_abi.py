@@ -170,6 +170,18 @@ def test_device_entry_points_validate_before_launch():
         == kvc.KVC_ERR_NULL
     assert L.kvc_c128_online_prefill(p, 4, p, p, 8, p, p, None, 1, ctypes.c_void_p(0x1008), 3,
                                      None, 0, None) == kvc.KVC_ERR_SHAPE
+    # multi-layer ring decode: too many layers, layer strides that overlap layers
+    r = L.kvc_compress_decode_ring_layers
+    assert r(p, 4 * 4096, 4, p, p, 4 * 512, 512, 128, p, 4 * 512, 512, 128, p, 2048, p, p, 4, 4,
+             16, p, p, 4, 70000, 1, None) == kvc.KVC_ERR_SHAPE
+    assert r(p, 4 * 4096 - 8, 4, p, p, 4 * 512, 512, 128, p, 4 * 512, 512, 128, p, 2048, p, p, 4,
+             4, 16, p, p, 4, 3, 1, None) == kvc.KVC_ERR_SHAPE
+    assert r(p, 4 * 4096, 4, p, p, 4 * 512 - 8, 512, 128, p, 4 * 512, 512, 128, p, 2048, p, p, 4,
+             4, 16, p, p, 4, 3, 1, None) == kvc.KVC_ERR_SHAPE
+    assert r(p, 4 * 4096, 4, p, p, 4 * 512, 512, 128, p, 4 * 512, 512, 128, p, 2044, p, p, 4, 4,
+             16, p, p, 4, 3, 1, None) == kvc.KVC_ERR_SHAPE
+    assert r(p, 0, 4, p, p, 0, 512, 128, p, 0, 512, 128, p, 0, p, p, 4, 4, 16, p, p, 4, 0, 1,
+             None) == kvc.KVC_OK
     # fused prefill: nothing to do, missing items, both / neither output, misaligned items
     f = L.kvc_c128_online_prefill_fused
     assert f(p, 4, p, p, None, None, 1, 8, p, p, 1, None, 0, None) == kvc.KVC_OK

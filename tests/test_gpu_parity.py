@@ -626,6 +626,51 @@ def test_paged_ring_decode_matches_packed():
     assert np.array_equal(cache.cpu().numpy(), exp)
 
 
+@pytest.mark.parametrize("next_n", [4, 9])
+def test_ring_decode_layers_equal_separate_calls(next_n):
+    """One launch over 5 layers (own ring, keys, scores and ape per layer,
+    shared maps) equals 5 single-layer calls, each checked against the oracle."""
+    L, R = 5, 37
+    base = synth.pool16_ring(seed=40 + next_n, num_requests=R, next_n=next_n, pad_frac=0.1)
+    pad = base["positions"] < 0
+    g = np.random.default_rng(41)
+    layers = []
+    for l in range(L):
+        d = dict(base)
+        if l:
+            d["ring"] = synth.bf16_normal(g, base["ring"].shape)
+            d["key"] = synth.bf16_normal(g, base["key"].shape)
+            d["score"] = synth.bf16_normal(g, base["score"].shape)
+            d["key"][pad] = synth.BF16_NAN
+            d["score"][pad] = synth.BF16_NAN
+            d["ape"] = synth.ape_pool16(g)
+        layers.append(d)
+    note(f"ring decode layers {L}x{R}x{next_n}")
+    singles = []
+    for l, d in enumerate(layers):
+        gring, gc, gsc, ring, ref_c, ref_s = run_ring(d)
+        assert np.array_equal(gring, ring)
+        check_codes(gc, ref_c, f"ring layer {l} codes")
+        check_scales(gsc, ref_s, True, f"ring layer {l} scales")
+        singles.append((gring, gc, gsc))
+    n_out = base["num_out"]
+    mring = dev(np.stack([d["ring"] for d in layers]), torch.int16)
+    mkey = dev(np.stack([d["key"] for d in layers]), torch.int16)
+    mscore = dev(np.stack([d["score"] for d in layers]), torch.int16)
+    mape = dev(np.stack([d["ape"] for d in layers]))
+    mo = torch.full((L, n_out, 128), 0x33, dtype=torch.uint8, device="cuda")
+    ms = torch.full((L, n_out), 5.0, device="cuda")
+    kvc.kvc_compress_decode_ring_layers(mring, dev(base["tail_slot_mapping"]), mkey, mscore, mape,
+                                        dev(base["slot_mapping"]), dev(base["positions"]), mo, ms,
+                                        True)
+    torch.cuda.synchronize()
+    mring, mo, ms = mring.cpu().numpy().view(np.uint16), mo.cpu().numpy(), ms.cpu().numpy()
+    for l, (gring, gc, gsc) in enumerate(singles):
+        assert np.array_equal(mring[l], gring), f"layer {l}: ring differs"
+        assert np.array_equal(mo[l], gc), f"layer {l}: codes differ"
+        assert np.array_equal(ms[l].view(np.uint32), gsc.view(np.uint32)), f"layer {l}: scales"
+
+
 # ------------------------------------------------------------------ c128 layers / quantised epilogue
 def _layer_case(seq_lens, indices, seed, num_slots=2048):
     from tests.helpers import seed_states
