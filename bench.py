@@ -344,6 +344,117 @@ def bench_ring(args, torch, kvc, synth, stream):
     return res
 
 
+# ------------------------------------------------------------------ next rows
+def bench_next_rows(args, torch, kvc, synth, stream):
+    """The extensions beyond the core path, each on the configured workload it
+    applies to: tail-ring seeding from the 64-sequence prefill batch, the
+    paged (page size 1) cache write of the prefill, the rotate / e4m3
+    epilogue of the pool-128 paths, and the pool-128 prefill with its work
+    items padded to capacity (as a captured graph replays it)."""
+    import numpy as np
+    out = {}
+    steps = max(args.steps // 2, 20)
+
+    # tail-ring seeding: every token's slot map is read, the last 16 tokens of
+    # each request are copied (key + score rows in, ring rows out)
+    d = synth.pool16_seed(seed=0)
+    T = d["tslot"].size
+    ring = to_dev(torch, d["ring"])
+    key, score, tsl = to_dev(torch, d["key"]), to_dev(torch, d["score"]), to_dev(torch, d["tslot"])
+    seeded = int(np.minimum(d["seq_lens"], 16).sum())
+    alg = T * 4 + seeded * 1024
+    _, ev, _ = timed(lambda i: kvc.kvc_seed_tail_ring(ring, key, score, tsl), steps, 3, torch,
+                     stream)
+    out["seed_tail_ring"] = {"workload": "pool16_seed_64seq", "tokens": T, "seeded_tokens": seeded,
+                             "launch_us": round(ev * 1e3, 3), "bytes_per_launch": alg,
+                             "hbm_gbs": round(gbs(alg, ev), 1)}
+    del ring, key, score, tsl
+
+    # paged prefill write (page size 1): same kernel and bytes as the packed form
+    d = synth.pool16_ragged(seed=0)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    n = int(rows.size)
+    per_rep = 2 * d["keys"].shape[0] * 256
+    R = max(2, -(-(2 * MALL_BYTES) // per_rep))
+    kv = [torch.stack([to_dev(torch, d["keys"]), to_dev(torch, d["scores"])]) for _ in range(R)]
+    ape, rows_t = to_dev(torch, d["ape"]), to_dev(torch, rows)
+    cache = torch.empty((n, 132), dtype=torch.uint8, device="cuda")
+    loc = torch.arange(n, dtype=torch.int64, device="cuda")
+
+    def paged(i):
+        r = kv[i % R]
+        kvc.kvc_compress_prefill_paged(r[0], r[1], ape, rows_t, n, cache, loc, True)
+
+    _, ev, _ = timed(paged, args.steps, 5, torch, stream)
+    alg = n * (16 * 256 * 2 + 132 + 4 + 8)      # rows, page, plan entry, loc
+    out["paged_prefill"] = {"workload": "pool16_ragged_prefill_paged", "pools": n,
+                            "launch_us": round(ev * 1e3, 3), "bytes_per_launch": alg,
+                            "hbm_gbs": round(gbs(alg, ev), 1),
+                            "hbm_frac": round(gbs(alg, ev) / PEAK_HBM_GBS, 4)}
+    del kv, cache
+
+    # pool-128 prefill, single launch: fp32 out vs rotate / e4m3 epilogue, and
+    # with the work items padded to capacity (num_tokens items)
+    d = synth.c128_prefill(seed=0)
+    N = int(d["extend_lens"].sum())
+    S = d["num_slots"]
+    ape = to_dev(torch, d["ape"])
+    idx = to_dev(torch, d["indices"])
+    state = torch.zeros((S, 384), device="cuda")
+    state[:, 128:256] = 1.0
+    ins = [to_dev(torch, d["kv_score_in"]) for _ in range(max(2, -(-(2 * MALL_BYTES) // (N * 1024))))]
+    RI = len(ins)
+    items = kvc.kvc_c128_plan_prefill_fused(d["seq_lens"], d["extend_lens"], N)
+    # capacity for any batch of up to 32 requests over these N tokens, and the
+    # pages' own choice (one entry per token)
+    items_pad = kvc.kvc_c128_plan_prefill_fused(d["seq_lens"], d["extend_lens"], N,
+                                                pad_to_capacity=True)
+    items_tok = kvc.kvc_c128_plan_prefill_fused(d["seq_lens"], d["extend_lens"], N,
+                                                pad_to_capacity=True, capacity=N)
+    it, itp = kvc.items_to_device(items), kvc.items_to_device(items_pad)
+    itt = kvc.items_to_device(items_tok)
+    o32 = torch.empty((N, 128), device="cuda")
+    codes = torch.empty((N, 128), dtype=torch.uint8, device="cuda")
+    scl = torch.empty((N,), device="cuda")
+    cs = max(args.steps // 4, 10)
+    _, ev32, _ = timed(lambda i: kvc.kvc_c128_online_prefill_fused(
+        state, ins[i % RI], ape, idx, it, items.size, out=o32), cs, 3, torch, stream)
+    _, evq, _ = timed(lambda i: kvc.kvc_c128_online_prefill_fused(
+        state, ins[i % RI], ape, idx, it, items.size, out_fp8=codes, out_scale=scl,
+        round_scale=True), cs, 3, torch, stream)
+    _, evp, _ = timed(lambda i: kvc.kvc_c128_online_prefill_fused(
+        state, ins[i % RI], ape, idx, itp, items_pad.size, out=o32), cs, 3, torch, stream)
+    _, evt, _ = timed(lambda i: kvc.kvc_c128_online_prefill_fused(
+        state, ins[i % RI], ape, idx, itt, items_tok.size, out=o32), cs, 3, torch, stream)
+    out["c128_prefill_single_launch"] = {
+        "workload": "c128_online_prefill_32seq", "items": int(items.size),
+        "fp32_out_us": round(ev32 * 1e3, 3), "quant_out_us": round(evq * 1e3, 3),
+        "padded_items": int(items_pad.size), "padded_fp32_out_us": round(evp * 1e3, 3),
+        "padded_per_token_items": int(items_tok.size),
+        "padded_per_token_fp32_out_us": round(evt * 1e3, 3)}
+    del ins
+
+    # pool-128 decode: fp32 out vs rotate / e4m3 epilogue (single call)
+    d = synth.c128_decode(seed=0)
+    B, S = d["indices"].size, d["num_slots"]
+    st = torch.zeros((S, 384), device="cuda")
+    st[:, 128:256] = 1.0
+    x, ape = to_dev(torch, d["kv_score_in"]), to_dev(torch, d["ape"])
+    idx, sl = to_dev(torch, d["indices"]), to_dev(torch, d["seq_lens"])
+    o = torch.empty((B, 128), device="cuda")
+    oc = torch.empty((B, 128), dtype=torch.uint8, device="cuda")
+    os_ = torch.empty((B,), device="cuda")
+    ds = max(args.steps, 50)
+    _, evd, _ = timed(lambda i: kvc.kvc_c128_online_decode(st, x, o, ape, idx, sl), ds, 5, torch,
+                      stream)
+    _, evdq, _ = timed(lambda i: kvc.kvc_c128_online_decode_quant(st, x, oc, os_, ape, idx, sl,
+                                                                   True), ds, 5, torch, stream)
+    out["c128_decode_epilogue"] = {"workload": "c128_online_decode_1024",
+                                   "fp32_out_us": round(evd * 1e3, 3),
+                                   "quant_out_us": round(evdq * 1e3, 3)}
+    return out
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_model() -> str:
     try:
@@ -527,6 +638,8 @@ def main():
                                       / (cl["ev_ms"] * 1e-3), 1),
                 "bytes_per_launch": cl["alg_bytes"], "hbm_gbs": round(gl, 1),
                 "hbm_frac": round(gl / PEAK_HBM_GBS, 4), "replicas": cl["replicas"]}
+        log("next rows (seeding, paged write, epilogues, padding)")
+        line["next_rows"] = bench_next_rows(args, torch, kvc, synth, stream)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(p)

@@ -132,15 +132,29 @@ int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, i
  * replaces), every other plan gets an item of its own.  Order: paired items,
  * then compress-only items, then write-only items, each in request order
  * (the longest work first).
- *   items            host [num_tokens] (capacity: each item covers at least
- *                    one token)
- *   pad_to_capacity  nonzero: fill with padding items up to num_tokens and
- *                    report num_tokens.
+ *   items            host [capacity]
+ *   capacity         entries available in items; at least the number of
+ *                    items, which never exceeds
+ *                    kvc_c128_fused_capacity(num_tokens, batch)
+ *   pad_to_capacity  nonzero: fill with padding items up to capacity and
+ *                    report capacity, so a captured launch always sees the
+ *                    same grid.  Every padding item costs an empty
+ *                    workgroup, so capacity should come from
+ *                    kvc_c128_fused_capacity for the largest batch the
+ *                    capture serves, not from num_tokens.
  *   n_items          host, out
- * Errors: as kvc_c128_plan_prefill. */
+ * Errors: as kvc_c128_plan_prefill (KVC_ERR_PLAN when the items exceed
+ *         capacity). */
 int kvc_c128_plan_prefill_fused(const int64_t* seq_lens, const int64_t* extend_lens,
                                 int64_t batch, int64_t num_tokens, kvc_online_item* items,
-                                int pad_to_capacity, uint32_t* n_items);
+                                int64_t capacity, int pad_to_capacity, uint32_t* n_items);
+
+/* Upper bound on the work items of any batch of at most max_batch requests
+ * extending num_tokens tokens in total: a request extending E tokens touches
+ * at most floor((E-1)/128) + 2 chunks, one segment each, so the items number
+ * at most floor(num_tokens/128) + 2*max_batch (and never more than
+ * num_tokens).  Returns 0 for negative arguments. */
+int64_t kvc_c128_fused_capacity(int64_t num_tokens, int64_t max_batch);
 
 /* ------------------------------------------------------------------------
  * Device entry points.

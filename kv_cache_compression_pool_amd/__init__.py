@@ -8,7 +8,7 @@ from .kvc import (ITEM_DTYPE, KvcError, PLAN_DTYPE, PLAN_SENTINEL, items_to_devi
                   kvc_c128_online_decode_layers, kvc_c128_online_decode_quant,
                   kvc_c128_online_prefill, kvc_c128_online_prefill_fused,
                   kvc_c128_online_prefill_quant, kvc_c128_plan_prefill,
-                  kvc_c128_plan_prefill_fused, kvc_compress_decode_ring,
+                  kvc_c128_fused_capacity, kvc_c128_plan_prefill_fused, kvc_compress_decode_ring,
                   kvc_compress_decode_ring_layers, kvc_compress_decode_ring_paged, kvc_compress_prefill,
                   kvc_compress_prefill_paged,
                   kvc_diag_convert, kvc_plan_pool_prefill, kvc_seed_tail_ring,
@@ -18,7 +18,7 @@ __all__ = ["ITEM_DTYPE", "KvcError", "PLAN_DTYPE", "PLAN_SENTINEL", "items_to_de
            "kvc_c128_online_decode_layers", "kvc_c128_online_decode_quant",
            "kvc_c128_online_prefill", "kvc_c128_online_prefill_fused",
            "kvc_c128_online_prefill_quant", "kvc_c128_plan_prefill",
-           "kvc_c128_plan_prefill_fused", "kvc_compress_decode_ring", "kvc_compress_decode_ring_layers",
+           "kvc_c128_fused_capacity", "kvc_c128_plan_prefill_fused", "kvc_compress_decode_ring", "kvc_compress_decode_ring_layers",
            "kvc_compress_decode_ring_paged",
            "kvc_compress_prefill", "kvc_compress_prefill_paged",
            "kvc_diag_convert", "kvc_plan_pool_prefill", "kvc_seed_tail_ring",

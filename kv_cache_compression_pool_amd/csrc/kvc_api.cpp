@@ -167,15 +167,23 @@ int kvc_c128_plan_prefill(const int64_t* seq_lens, const int64_t* extend_lens, i
   return ok();
 }
 
+int64_t kvc_c128_fused_capacity(int64_t num_tokens, int64_t max_batch) {
+  if (num_tokens < 0 || max_batch < 0) return 0;
+  const int64_t bound = num_tokens / 128 + 2 * max_batch;
+  return bound < num_tokens ? bound : num_tokens;
+}
+
 int kvc_c128_plan_prefill_fused(const int64_t* seq_lens, const int64_t* extend_lens,
                                 int64_t batch, int64_t num_tokens, kvc_online_item* items,
-                                int pad_to_capacity, uint32_t* n_items) {
+                                int64_t capacity, int pad_to_capacity, uint32_t* n_items) {
   const char* fn = "kvc_c128_plan_prefill_fused";
   if (!n_items) return fail(KVC_ERR_NULL, "%s: NULL count", fn);
   *n_items = 0;
   int rc = check_plan_args(fn, seq_lens, extend_lens, batch, num_tokens);
   if (rc != KVC_OK) return rc;
-  if (num_tokens > 0 && !items) return fail(KVC_ERR_NULL, "%s: NULL item buffer", fn);
+  if (capacity < 0 || capacity > (int64_t)0xffffffffLL)
+    return fail(KVC_ERR_SHAPE, "%s: capacity out of range", fn);
+  if (capacity > 0 && !items) return fail(KVC_ERR_NULL, "%s: NULL item buffer", fn);
   // A request pairs its first compress plan with its write plan when the
   // former starts mid-chunk; both conditions are fixed by its lengths.
   auto paired = [&](int64_t b) {
@@ -193,8 +201,10 @@ int kvc_c128_plan_prefill_fused(const int64_t* seq_lens, const int64_t* extend_l
                             return (int)KVC_OK;
                           });
   if (rc != KVC_OK) return rc;
-  const uint64_t total = n_pair + n_conly + n_wonly;   // <= num_tokens: >= 1 token per item
-  if (total > (uint64_t)num_tokens) return fail(KVC_ERR_PLAN, "%s: items exceed capacity", fn);
+  const uint64_t total = n_pair + n_conly + n_wonly;
+  if (total > (uint64_t)capacity)
+    return fail(KVC_ERR_PLAN, "%s: %llu items exceed capacity %lld", fn,
+                (unsigned long long)total, (long long)capacity);
   // Pass 2: place the items.  The compress half of a paired item is written
   // when its first segment is seen, the write half when the trailing one is.
   uint64_t i_pair = 0, i_conly = n_pair, i_wonly = n_pair + n_conly;
@@ -222,8 +232,8 @@ int kvc_c128_plan_prefill_fused(const int64_t* seq_lens, const int64_t* extend_l
   if (rc != KVC_OK) return rc;
   uint64_t n = total;
   if (pad_to_capacity) {
-    for (int64_t i = (int64_t)total; i < num_tokens; ++i) items[i] = {kPadPlan, kPadPlan};
-    n = (uint64_t)num_tokens;
+    for (int64_t i = (int64_t)total; i < capacity; ++i) items[i] = {kPadPlan, kPadPlan};
+    n = (uint64_t)capacity;
   }
   *n_items = (uint32_t)n;
   return ok();

@@ -35,6 +35,7 @@ EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_p
            "kvc_c128_online_decode", "kvc_c128_online_decode_layers",
            "kvc_c128_online_decode_quant", "kvc_c128_online_prefill",
            "kvc_c128_online_prefill_quant", "kvc_c128_plan_prefill_fused",
+           "kvc_c128_fused_capacity",
            "kvc_c128_online_prefill_fused", "kvc_diag_convert", "kvc_diag_stream_read")
 
 
@@ -86,13 +87,15 @@ def lib() -> ctypes.CDLL:
                                                    _p]
         L.kvc_c128_online_prefill_quant.argtypes = [_p, _i64, _p, _p, _p, _i64, _p, _p, _p,
                                                     _i64, _p, _u32, _p, _u32, _i32, _p]
-        L.kvc_c128_plan_prefill_fused.argtypes = [_p, _p, _i64, _i64, _p, _i32, _p]
+        L.kvc_c128_plan_prefill_fused.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _p]
+        L.kvc_c128_fused_capacity.argtypes = [_i64, _i64]
         L.kvc_c128_online_prefill_fused.argtypes = [_p, _i64, _p, _p, _p, _p, _i32, _i64, _p, _p,
                                                     _i64, _p, _u32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
         L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
+        L.kvc_c128_fused_capacity.restype = _i64
         _lib = L
     return _lib
 
@@ -168,18 +171,27 @@ def kvc_c128_plan_prefill(seq_lens, extend_lens, num_tokens: int, pad_to_capacit
     return cp[:nc.value].copy(), wp[:nw.value].copy()
 
 
+def kvc_c128_fused_capacity(num_tokens: int, max_batch: int) -> int:
+    """Upper bound on the single-launch work items of any batch of at most
+    max_batch requests extending num_tokens tokens."""
+    return int(lib().kvc_c128_fused_capacity(int(num_tokens), int(max_batch)))
+
+
 def kvc_c128_plan_prefill_fused(seq_lens, extend_lens, num_tokens: int,
-                                pad_to_capacity: bool = False):
+                                pad_to_capacity: bool = False, capacity=None):
     """Work items for kvc_c128_online_prefill_fused: host array of ITEM_DTYPE
-    (fields compress / write, each a PLAN_DTYPE record; all-0xFFFFFFFF = none)."""
+    (fields compress / write, each a PLAN_DTYPE record; all-0xFFFFFFFF = none).
+    capacity defaults to kvc_c128_fused_capacity(num_tokens, len(seq_lens))."""
     sl = np.ascontiguousarray(seq_lens, np.int64)
     el = np.ascontiguousarray(extend_lens, np.int64)
     if sl.size != el.size:
         raise ValueError("seq_lens and extend_lens differ in length")
-    items = np.zeros(max(int(num_tokens), 1), ITEM_DTYPE)
+    if capacity is None:
+        capacity = kvc_c128_fused_capacity(num_tokens, sl.size)
+    items = np.zeros(max(int(capacity), 1), ITEM_DTYPE)
     n = ctypes.c_uint32()
     _check(lib().kvc_c128_plan_prefill_fused(_np_ptr(sl), _np_ptr(el), sl.size, int(num_tokens),
-                                             _np_ptr(items), int(pad_to_capacity),
+                                             _np_ptr(items), int(capacity), int(pad_to_capacity),
                                              ctypes.byref(n)))
     return items[:n.value].copy()
 

@@ -107,10 +107,18 @@ def test_c128_fused_planner_matches_oracle_plans():
             half = "write" if k == 2 else "compress"
             bids = [(int(it[half]["batch_id"]), int(it[half]["position"])) for it in sel]
             assert bids == sorted(bids)
+        cap = kvc.kvc_c128_fused_capacity(n, B)
+        assert items.size <= cap <= n                       # the documented bound holds
         padded = kvc.kvc_c128_plan_prefill_fused(sl, el, n, pad_to_capacity=True)
-        assert padded.size == n
+        assert padded.size == cap
         assert np.array_equal(padded[:items.size], items)
         assert all(_is_pad(it["compress"]) and _is_pad(it["write"]) for it in padded[items.size:])
+        wide = kvc.kvc_c128_plan_prefill_fused(sl, el, n, pad_to_capacity=True, capacity=n)
+        assert wide.size == n and np.array_equal(wide[:items.size], items)
+        if items.size > 1:
+            with pytest.raises(kvc.KvcError) as e:
+                kvc.kvc_c128_plan_prefill_fused(sl, el, n, capacity=items.size - 1)
+            assert e.value.code == kvc.KVC_ERR_PLAN
 
 
 def test_planner_errors():
@@ -194,6 +202,10 @@ def test_device_entry_points_validate_before_launch():
     with pytest.raises(kvc.KvcError) as e:
         kvc.kvc_c128_plan_prefill_fused([10], [11], 11)
     assert e.value.code == kvc.KVC_ERR_PLAN
+    assert kvc.kvc_c128_fused_capacity(-1, 4) == 0
+    assert kvc.kvc_c128_fused_capacity(1000, 4) == 1000 // 128 + 8
+    assert kvc.kvc_c128_fused_capacity(10, 4) == 8
+    assert kvc.kvc_c128_fused_capacity(5, 4) == 5
     assert L.kvc_diag_convert(p, None, None, 3, None) == kvc.KVC_ERR_SHAPE
     assert b"even" in L.kvc_last_error()
 

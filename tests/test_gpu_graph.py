@@ -145,15 +145,16 @@ def test_graph_replay_single_launch_prefill():
     st0, x, a, idx = dev(st_np), dev(x_np), dev(a_np), dev(i_np)
     st = st0.clone()
     lists = {}
+    cap = kvc.kvc_c128_fused_capacity(N, 4)        # the capture serves batches of up to 4
     for name, sl, el in (("a", sl_a, el_a), ("b", sl_b, el_b)):
-        items = kvc.kvc_c128_plan_prefill_fused(sl, el, N, pad_to_capacity=True)
-        assert items.size == N
+        items = kvc.kvc_c128_plan_prefill_fused(sl, el, N, pad_to_capacity=True, capacity=cap)
+        assert items.size == cap
         lists[name] = kvc.items_to_device(items)
     items_t = torch.empty_like(lists["a"])
     out = torch.empty((N, 128), device="cuda")
 
     def step():
-        kvc.kvc_c128_online_prefill_fused(st, x, a, idx, items_t, N, out=out)
+        kvc.kvc_c128_online_prefill_fused(st, x, a, idx, items_t, cap, out=out)
 
     def reset(name):
         st.copy_(st0)
