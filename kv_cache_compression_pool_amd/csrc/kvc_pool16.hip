@@ -512,8 +512,11 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   stash_range(stashes & ~done);
 }
 
-// Tail-ring seeding: one 16-lane row per token copies its 256 B key and
-// score rows when it is among its request's last 16 tokens.
+// Tail-ring seeding.  Each lane decides for one token whether it is among its
+// request's last 16 (no token 16 positions later maps to the same ring
+// block); the wave then copies its few seeded tokens together, two per step,
+// one 16-lane row per 256 B key or score row.  Seeded tokens are rare (at
+// most 16 per request), so a wave mostly just reads 64 slot-map entries.
 __global__ __launch_bounds__(256) void pool16_seed_kernel(uint16_t* __restrict__ ring,
                                                           int64_t num_blocks,
                                                           const uint16_t* __restrict__ key,
@@ -522,19 +525,38 @@ __global__ __launch_bounds__(256) void pool16_seed_kernel(uint16_t* __restrict__
                                                           int64_t score_stride,
                                                           const int32_t* __restrict__ tslot,
                                                           int64_t n_tokens) {
-  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  if (i >= n_tokens) return;
-  const int64_t t = tslot[i];
-  if (t < 0) return;
-  const int64_t blk = t / kPool;
-  const int64_t ahead = (i + kPool < n_tokens) ? (int64_t)tslot[i + kPool] : -1;
-  if (ahead >= 0 && ahead / kPool == blk) return;     // a later token owns this slot
-  if (blk >= num_blocks) return;
-  uint16_t* rk = ring + blk * (2 * kPool * 128) + (t % kPool) * 128;
-  uint16_t* rs = rk + kPool * 128;
-  reinterpret_cast<uint4*>(rk)[c] = reinterpret_cast<const uint4*>(key + i * key_stride)[c];
-  reinterpret_cast<uint4*>(rs)[c] = reinterpret_cast<const uint4*>(score + i * score_stride)[c];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  int32_t t = -1;
+  bool seed = false;
+  if (i < n_tokens) {
+    t = tslot[i];
+    const int32_t ahead = (i + kPool < n_tokens) ? tslot[i + kPool] : -1;
+    seed = t >= 0 && (int64_t)(t / kPool) < num_blocks && !(ahead >= 0 && ahead / kPool == t / kPool);
+  }
+  uint64_t mask = __ballot(seed);
+  const int64_t wave_base = i - lane;
+  const int half = lane >> 5;                 // which of the step's two tokens
+  const int which = (lane >> 4) & 1;          // 0: key row, 1: score row
+  const int c = lane & 15;                    // 16-byte chunk of the row
+  while (mask) {                              // uniform over the wave
+    const int j0 = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    int j1 = -1;
+    if (mask) {
+      j1 = __builtin_ctzll(mask);
+      mask &= mask - 1;
+    }
+    const int j = half ? j1 : j0;
+    const int32_t tj = __shfl(t, j >= 0 ? j : j0);
+    if (j >= 0) {
+      const int64_t tok = wave_base + j;
+      const uint16_t* src = which ? score + tok * score_stride : key + tok * key_stride;
+      uint16_t* dst = ring + (int64_t)(tj / kPool) * (2 * kPool * 128) +
+                      (which * kPool + tj % kPool) * 128;
+      reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(src)[c];
+    }
+  }
 }
 
 }  // namespace
@@ -599,7 +621,7 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
 hipError_t launch_pool16_seed(uint16_t* ring, int64_t num_blocks, const uint16_t* key,
                               int64_t key_stride, const uint16_t* score, int64_t score_stride,
                               const int32_t* tslot, int64_t n_tokens, hipStream_t stream) {
-  const dim3 grid((unsigned)((n_tokens + 15) / 16));
+  const dim3 grid((unsigned)((n_tokens + 255) / 256));
   hipLaunchKernelGGL(pool16_seed_kernel, grid, dim3(256), 0, stream, ring, num_blocks, key,
                      key_stride, score, score_stride, tslot, n_tokens);
   return hipGetLastError();
