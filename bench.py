@@ -34,8 +34,9 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0                 # MI355X HBM3E peak, GB/s
 MALL_BYTES = 256 << 20                # Infinity Cache capacity
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pool16_prefill_ragged64_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "kv_cache_compression_pool_amd", "csrc", f)
-                  for f in ("kvc_pool16.hip", "kvc_device.hpp")]
+C128_PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "c128_prefill_32seq_single_launch_traffic.json")
+C128_DECODE_TRAFFIC = os.path.join(ROOT, "profiles", "c128_decode_64layers_traffic.json")
+KERNEL_SOURCES = ("kvc_pool16.hip", "kvc_device.hpp")
 METRIC = ("compressed vectors/s + achieved HBM GB/s (% of peak), "
           "pool-16 prefill & c128 decode")
 
@@ -44,23 +45,23 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(files=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in files:
+        with open(os.path.join(ROOT, "kv_cache_compression_pool_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, or None when
-    the kernel sources changed since the counters were taken."""
+def measured_traffic(path=TRAFFIC_FILE):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    kernel sources it names changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha") != kernel_source_sha():
+    if t.get("kernel_sha") != kernel_source_sha(tuple(t.get("kernel_sources", KERNEL_SOURCES))):
         return None
     return t.get("bytes_per_launch")
 
@@ -515,8 +516,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--replicas", type=int, default=None)
-    ap.add_argument("--only", choices=["prefill", "all"], default="all",
-                    help="prefill: the headline kernel only (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "c128", "all"], default="all",
+                    help="prefill: the headline kernel only; c128: the pool-128 prefill and "
+                         "decode legs only (both for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-layers", type=int, default=64,
                     help="layers in the multi-layer decode measurements (0: skip)")
@@ -540,14 +542,37 @@ def main():
     kvc.kvc.lib()
     stream = torch.cuda.current_stream()
 
+    def calibration_copy():
+        if args.calib_copy_mib:
+            a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            log(f"calibration copy of {args.calib_copy_mib} MiB done")
+
+    if args.only == "c128":
+        # profiling run: the pool-128 legs only, printed as their own line
+        calibration_copy()
+        log("pool-128 online prefill")
+        c5 = bench_c128_prefill(args, torch, kvc, synth, stream)
+        log("pool-128 online decode")
+        c4 = bench_c128_decode(args, torch, kvc, synth, stream)
+        prof = {"profiling": "c128",
+                "c128_prefill": {"bytes_per_call": c5["alg_bytes"],
+                                 "two_launch_us": round(c5["ev_ms"] * 1e3, 3),
+                                 "single_launch_us": round(c5["fused_ev_ms"] * 1e3, 3)},
+                "c128_decode": {"bytes_per_launch": c4["alg_bytes"],
+                                "launch_us": round(c4["ev_ms"] * 1e3, 3)}}
+        if "layers" in c4:
+            prof["c128_decode"]["multi_layer"] = {
+                "layers": c4["layers"]["layers"], "bytes_per_launch": c4["layers"]["alg_bytes"],
+                "launch_us": round(c4["layers"]["ev_ms"] * 1e3, 3)}
+        print(json.dumps(prof), flush=True)
+        return
+
     log("pool-16 ragged prefill")
     p = bench_pool16_prefill(args, torch, kvc, synth, stream)
-    if args.calib_copy_mib:
-        a = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"calibration copy of {args.calib_copy_mib} MiB done")
+    calibration_copy()
     achieved = gbs(p["alg_bytes"], p["ev_ms"])
     line = {
         "metric": METRIC,
@@ -604,7 +629,8 @@ def main():
                 "layers": cl["layers"], "launch_us": round(cl["ev_ms"] * 1e3, 3),
                 "token_updates_per_s": round(c4["batch"] * cl["layers"] / (cl["ev_ms"] * 1e-3), 1),
                 "bytes_per_launch": cl["alg_bytes"], "hbm_gbs": round(gl, 1),
-                "hbm_frac": round(gl / PEAK_HBM_GBS, 4)}
+                "hbm_frac": round(gl / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(C128_DECODE_TRAFFIC) if cl["layers"] == 64 else None}
         log("pool-128 online prefill")
         c5 = bench_c128_prefill(args, torch, kvc, synth, stream)
         g5 = gbs(c5["alg_bytes"], c5["ev_ms"])
@@ -620,7 +646,8 @@ def main():
             "items": c5["items"], "paired_items": c5["paired"],
             "vectors_per_s": round(c5["vectors"] * c5["steps"] / (c5["fused_total_ms"] * 1e-3), 1),
             "call_us": round(c5["fused_ev_ms"] * 1e3, 3), "hbm_gbs": round(g5f, 1),
-            "hbm_frac": round(g5f / PEAK_HBM_GBS, 4)}
+            "hbm_frac": round(g5f / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(C128_PREFILL_TRAFFIC)}
         log("pool-16 ring decode")
         c3 = bench_ring(args, torch, kvc, synth, stream)
         g3 = gbs(c3["alg_bytes"], c3["ev_ms"])
