@@ -106,10 +106,14 @@ def _check(rc: int) -> None:
 
 
 def _stream(stream) -> int | None:
-    if stream is not None:
-        return int(stream)
-    import torch
-    return torch.cuda.current_stream().cuda_stream
+    """hipStream_t handle: None = torch's current stream; a torch.cuda.Stream
+    or a raw integer handle is used as given."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return int(stream.cuda_stream)
+    return int(stream)
 
 
 def _dptr(t, dtype, name, optional=False):
