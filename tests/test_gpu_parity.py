@@ -780,3 +780,24 @@ def test_diag_stream_read_reads_every_word():
         blk = x[t0:t0 + threads]
         exp[:blk.size] ^= blk
     assert np.array_equal(sink.cpu().numpy().view(np.uint32), exp)
+
+
+def test_explicit_stream_argument():
+    """Work is enqueued on the stream passed in (a torch.cuda.Stream or its raw
+    handle), not on the current stream."""
+    d = synth.pool16_single(seed=0)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    n = rows.size
+    k, s, a, r = dev(d["keys"], torch.int16), dev(d["scores"], torch.int16), dev(d["ape"]), dev(rows)
+    ref_c = torch.zeros((n, 128), dtype=torch.uint8, device="cuda")
+    ref_s = torch.zeros((n,), device="cuda")
+    kvc.kvc_compress_prefill(k, s, a, r, n, ref_c, ref_s, False)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for handle in (side, side.cuda_stream):
+        c = torch.zeros((n, 128), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros((n,), device="cuda")
+        torch.cuda.synchronize()
+        kvc.kvc_compress_prefill(k, s, a, r, n, c, sc, False, stream=handle)
+        side.synchronize()
+        assert torch.equal(c, ref_c) and torch.equal(sc, ref_s)
