@@ -383,16 +383,16 @@ int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* 
                                   int round_scale, void* stream);
 
 /* Pool-128 online ragged prefill in ONE launch (c128_online.cuh page,
- * flash_c128_online_prefill; same results as kvc_c128_online_prefill with
- * load_indices = indices).  The page orders state reads before state writes
- * with two launches; here each work item from kvc_c128_plan_prefill_fused
- * carries the only read that can conflict with its write, so one workgroup
- * does both in order and the second launch (latency-bound, a few
- * microseconds) disappears.  Requires the state rows indices[b] of the
- * requests in the call to be distinct (as the write pass of the two-launch
- * form already does).
- *   state, kv_score_in, num_tokens, ape, indices, batch: as
- *                  kvc_c128_online_prefill (reads and writes use indices)
+ * flash_c128_online_prefill; same results as kvc_c128_online_prefill).  The
+ * page orders state reads before state writes with two launches; here each
+ * work item from kvc_c128_plan_prefill_fused carries the only read that can
+ * conflict with its write, so one workgroup does both in order and the
+ * second launch (latency-bound, a few microseconds) disappears.  Requires
+ * that no request reads a state row another request of the call writes: the
+ * rows indices[b] are distinct, and load_indices[b] is no other request's
+ * indices[b'] (true when load_indices is NULL).
+ *   state, kv_score_in, num_tokens, ape, indices, load_indices, batch: as
+ *                  kvc_c128_online_prefill
  *   out            device fp32 [num_tokens, 128], or NULL when out_fp8 is
  *                  given; chunk-closing rows only
  *   out_fp8, out_scale  device uint8 [num_tokens, 128] and fp32
@@ -406,8 +406,9 @@ int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* 
 int kvc_c128_online_prefill_fused(float* state, int64_t num_slots, const float* kv_score_in,
                                   float* out, uint8_t* out_fp8, float* out_scale,
                                   int round_scale, int64_t num_tokens, const float* ape,
-                                  const int32_t* indices, int64_t batch,
-                                  const kvc_online_item* items, uint32_t n_items, void* stream);
+                                  const int32_t* indices, const int32_t* load_indices,
+                                  int64_t batch, const kvc_online_item* items, uint32_t n_items,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------
  * Diagnostics.

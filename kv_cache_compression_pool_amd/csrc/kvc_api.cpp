@@ -601,8 +601,9 @@ int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* 
 int kvc_c128_online_prefill_fused(float* state, int64_t num_slots, const float* kv_score_in,
                                   float* out, uint8_t* out_fp8, float* out_scale,
                                   int round_scale, int64_t num_tokens, const float* ape,
-                                  const int32_t* indices, int64_t batch,
-                                  const kvc_online_item* items, uint32_t n_items, void* stream) {
+                                  const int32_t* indices, const int32_t* load_indices,
+                                  int64_t batch, const kvc_online_item* items, uint32_t n_items,
+                                  void* stream) {
   const char* fn = "kvc_c128_online_prefill_fused";
   if (batch < 0 || num_slots < 0 || num_tokens < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
   if (n_items == 0) return ok();
@@ -619,7 +620,7 @@ int kvc_c128_online_prefill_fused(float* state, int64_t num_slots, const float* 
     return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
   return hip_status(kvc::launch_c128_prefill_fused(state, num_slots, kv_score_in, out, out_fp8,
                                                    out_scale, round_scale != 0, num_tokens, ape,
-                                                   indices, batch, items, n_items,
+                                                   indices, load_indices, batch, items, n_items,
                                                    (hipStream_t)stream),
                     "kvc_c128_online_prefill_fused launch");
 }

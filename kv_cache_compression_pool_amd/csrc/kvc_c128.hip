@@ -338,16 +338,17 @@ __global__ __launch_bounds__(64 * kWaves) void c128_prefill_kernel(
 
 // Single-launch prefill over work items {compress plan, write plan}.  An item
 // that holds both belongs to one request whose first (mid-chunk) compress
-// segment reads the stored state that its write plan replaces: the workgroup
-// finishes the compress plan, whose state loads were consumed before the
-// barrier, and only then stores the new state.  No other item of the call
-// touches that request's state row, so no ordering between workgroups is
-// needed.
+// segment reads the stored state (row load_indices[b]) that its write plan
+// replaces (row indices[b]): the workgroup finishes the compress plan, whose
+// state loads were consumed before the barrier, and only then stores the new
+// state.  No other item of the call touches those rows (the caller guarantees
+// that no request reads a row another request writes), so no ordering between
+// workgroups is needed.
 template <bool kQuant>
 __global__ __launch_bounds__(64 * kCompressWaves) void c128_prefill_fused_kernel(
     float* __restrict__ state, int64_t num_slots, const float* __restrict__ in,
     EmitSink o, int64_t num_tokens, const float* __restrict__ ape,
-    const int32_t* __restrict__ indices, int64_t batch,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ load_indices, int64_t batch,
     const kvc_online_item* __restrict__ items, uint32_t n_items) {
   __shared__ PlanLds<kCompressWaves> lds;
   if (blockIdx.x >= n_items) return;
@@ -355,10 +356,10 @@ __global__ __launch_bounds__(64 * kCompressWaves) void c128_prefill_fused_kernel
   const uint4 pc = it[0];
   const uint4 pw = it[1];
   prefill_plan<false, kCompressWaves, kQuant>(pc, state, num_slots, in, o, num_tokens, ape,
-                                              indices, indices, batch, lds);
+                                              indices, load_indices, batch, lds);
   __syncthreads();   // the LDS partials are reused by the write plan
   prefill_plan<true, kCompressWaves, false>(pw, state, num_slots, in, o, num_tokens, ape, indices,
-                                            indices, batch, lds);
+                                            load_indices, batch, lds);
 }
 
 }  // namespace
@@ -419,17 +420,19 @@ hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in,
 hipError_t launch_c128_prefill_fused(float* state, int64_t num_slots, const float* in, float* out,
                                      uint8_t* codes, float* scales, bool round_scale,
                                      int64_t num_tokens, const float* ape, const int32_t* indices,
-                                     int64_t batch, const kvc_online_item* items,
-                                     uint32_t n_items, hipStream_t stream) {
+                                     const int32_t* load_indices, int64_t batch,
+                                     const kvc_online_item* items, uint32_t n_items,
+                                     hipStream_t stream) {
+  if (!load_indices) load_indices = indices;
   const EmitSink o{out, codes, scales, 0, 0, 0, round_scale};
   if (codes)
     hipLaunchKernelGGL((c128_prefill_fused_kernel<true>), dim3(n_items),
                        dim3(64 * kCompressWaves), 0, stream, state, num_slots, in, o, num_tokens,
-                       ape, indices, batch, items, n_items);
+                       ape, indices, load_indices, batch, items, n_items);
   else
     hipLaunchKernelGGL((c128_prefill_fused_kernel<false>), dim3(n_items),
                        dim3(64 * kCompressWaves), 0, stream, state, num_slots, in, o, num_tokens,
-                       ape, indices, batch, items, n_items);
+                       ape, indices, load_indices, batch, items, n_items);
   return hipGetLastError();
 }
 

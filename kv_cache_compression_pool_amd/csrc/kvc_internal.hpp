@@ -57,12 +57,13 @@ hipError_t launch_c128_prefill(float* state, int64_t num_slots, const float* in,
                                const kvc_online_plan* wplan, uint32_t n_w, hipStream_t stream);
 
 // Single-launch prefill over {compress, write} work items (state rows are
-// read and written at indices[b]).
+// read at load_indices[b], or indices[b] when null, and written at indices[b]).
 hipError_t launch_c128_prefill_fused(float* state, int64_t num_slots, const float* in, float* out,
                                      uint8_t* codes, float* scales, bool round_scale,
                                      int64_t num_tokens, const float* ape, const int32_t* indices,
-                                     int64_t batch, const kvc_online_item* items,
-                                     uint32_t n_items, hipStream_t stream);
+                                     const int32_t* load_indices, int64_t batch,
+                                     const kvc_online_item* items, uint32_t n_items,
+                                     hipStream_t stream);
 
 hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
                                hipStream_t stream);

@@ -90,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.kvc_c128_plan_prefill_fused.argtypes = [_p, _p, _i64, _i64, _p, _i64, _i32, _p]
         L.kvc_c128_fused_capacity.argtypes = [_i64, _i64]
         L.kvc_c128_online_prefill_fused.argtypes = [_p, _i64, _p, _p, _p, _p, _i32, _i64, _p, _p,
-                                                    _i64, _p, _u32, _p]
+                                                    _p, _i64, _p, _u32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
         L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _p]
         for name in EXPORTS[2:]:
@@ -510,7 +510,7 @@ def kvc_c128_online_prefill(state, kv_score_in, out, ape, indices, compress_plan
 
 def kvc_c128_online_prefill_fused(state, kv_score_in, ape, indices, items, n_items, out=None,
                                   out_fp8=None, out_scale=None, round_scale: bool = True,
-                                  stream=None):
+                                  load_indices=None, stream=None):
     """Single-launch prefill over device work items (see items_to_device);
     chunk-closing vectors go to out (fp32 [N,128]) or, with out_fp8 / out_scale,
     through the rotate / e4m3 epilogue."""
@@ -520,6 +520,8 @@ def kvc_c128_online_prefill_fused(state, kv_score_in, ape, indices, items, n_ite
     _shape_ok(kv_score_in, (N, 256), "kv_score_in")
     _shape_ok(ape, (128, 128), "ape")
     _shape_ok(indices, (B,), "indices")
+    if load_indices is not None:
+        _shape_ok(load_indices, (B,), "load_indices")
     _need((out is None) != (out_fp8 is None), "give either out or out_fp8 / out_scale")
     if out is not None:
         _shape_ok(out, (N, 128), "out")
@@ -536,7 +538,8 @@ def kvc_c128_online_prefill_fused(state, kv_score_in, ape, indices, items, n_ite
         _dptr(out, torch.float32, "out", optional=True),
         _dptr(out_fp8, torch.uint8, "out_fp8", optional=True),
         _dptr(out_scale, torch.float32, "out_scale", optional=True), int(round_scale), N,
-        _dptr(ape, torch.float32, "ape"), _dptr(indices, torch.int32, "indices"), B,
+        _dptr(ape, torch.float32, "ape"), _dptr(indices, torch.int32, "indices"),
+        _dptr(load_indices, torch.int32, "load_indices", optional=True), B,
         None if items is None else items.data_ptr(), int(n_items), _stream(stream)))
 
 

@@ -192,12 +192,12 @@ def test_device_entry_points_validate_before_launch():
              None) == kvc.KVC_OK
     # fused prefill: nothing to do, missing items, both / neither output, misaligned items
     f = L.kvc_c128_online_prefill_fused
-    assert f(p, 4, p, p, None, None, 1, 8, p, p, 1, None, 0, None) == kvc.KVC_OK
-    assert f(p, 4, p, p, None, None, 1, 8, p, p, 1, None, 2, None) == kvc.KVC_ERR_NULL
-    assert f(p, 4, p, p, p, p, 1, 8, p, p, 1, p, 2, None) == kvc.KVC_ERR_NULL
-    assert f(p, 4, p, None, None, None, 1, 8, p, p, 1, p, 2, None) == kvc.KVC_ERR_NULL
-    assert f(p, 4, p, None, p, None, 1, 8, p, p, 1, p, 2, None) == kvc.KVC_ERR_NULL
-    assert f(p, 4, p, p, None, None, 1, 8, p, p, 1, ctypes.c_void_p(0x1008), 2, None) \
+    assert f(p, 4, p, p, None, None, 1, 8, p, p, None, 1, None, 0, None) == kvc.KVC_OK
+    assert f(p, 4, p, p, None, None, 1, 8, p, p, None, 1, None, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, p, p, p, 1, 8, p, p, None, 1, p, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, None, None, None, 1, 8, p, p, None, 1, p, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, None, p, None, 1, 8, p, p, None, 1, p, 2, None) == kvc.KVC_ERR_NULL
+    assert f(p, 4, p, p, None, None, 1, 8, p, p, None, 1, ctypes.c_void_p(0x1008), 2, None) \
         == kvc.KVC_ERR_SHAPE
     with pytest.raises(kvc.KvcError) as e:
         kvc.kvc_c128_plan_prefill_fused([10], [11], 11)

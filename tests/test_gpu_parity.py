@@ -422,7 +422,8 @@ def test_c128_prefill_distinct_load_indices():
     compare_state(gst, st, "c128 prefill load_indices")
 
 
-def run_c128_prefill_fused_gpu(d, state, pad=False, quant=False, round_scale=True):
+def run_c128_prefill_fused_gpu(d, state, pad=False, quant=False, round_scale=True,
+                               load_indices=None):
     n = int(d["extend_lens"].sum())
     items = kvc.kvc_c128_plan_prefill_fused(d["seq_lens"], d["extend_lens"], n,
                                             pad_to_capacity=pad)
@@ -436,7 +437,8 @@ def run_c128_prefill_fused_gpu(d, state, pad=False, quant=False, round_scale=Tru
         kw["out"] = torch.full((n, 128), float("nan"), device="cuda")
     kvc.kvc_c128_online_prefill_fused(gst, dev(d["kv_score_in"]), dev(d["ape"]),
                                       dev(d["indices"]), kvc.items_to_device(items), items.size,
-                                      **kw)
+                                      load_indices=None if load_indices is None
+                                      else dev(load_indices), **kw)
     torch.cuda.synchronize()
     outs = [t.cpu().numpy() for k, t in kw.items() if k != "round_scale"]
     return gst.cpu().numpy(), outs, items
@@ -503,6 +505,28 @@ def test_c128_prefill_fused_quant():
         assert np.array_equal(gc, c2.cpu().numpy())
         assert np.array_equal(gs, s2.cpu().numpy())
         assert np.array_equal(gst, g2.cpu().numpy(), equal_nan=True)
+
+
+def test_c128_prefill_fused_distinct_load_indices():
+    """Open-chunk states read from other slots than the ones written back (the
+    single launch's precondition holds: no request reads a written slot)."""
+    d = c128_prefill_case(seed=3, batch=6, max_prior=400, max_extend=300)
+    load = np.setdiff1d(np.arange(d["num_slots"]), d["indices"])[:d["indices"].size]
+    load = np.random.default_rng(4).permutation(load).astype(np.int32)
+    state = d["state"].copy()
+    state[load] = d["state"][d["indices"]]
+    state[d["indices"]] = np.nan
+    st = state.copy()
+    ref = np.full((int(d["extend_lens"].sum()), 128), np.nan, np.float32)
+    oracle.c128_prefill(st, d["kv_score_in"], d["ape"], d["indices"], d["cplan"], d["wplan"],
+                        load_indices=load, out=ref)
+    gst, (gout,), _ = run_c128_prefill_fused_gpu(d, state, load_indices=load)
+    assert np.array_equal(np.isnan(gout), np.isnan(ref))
+    rows = ~np.isnan(ref[:, 0])
+    assert rel_err_rows(gout[rows], ref[rows]).max(initial=0) <= VEC_TOL
+    compare_state(gst, st, "c128 fused prefill load_indices")
+    gst2, gout2, _, _ = run_c128_prefill_gpu(d, state, load_indices=load)
+    assert np.array_equal(gout, gout2, equal_nan=True) and np.array_equal(gst, gst2, equal_nan=True)
 
 
 # ------------------------------------------------------------------ tail-ring seeding
