@@ -387,8 +387,13 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
 //  * a whole wave per request halves each lane's share of the softmax and
 //    rotation (4 slots x 8 channels, then 2 channels) compared with the
 //    32-lane layout: in this latency-bound call the dependent arithmetic of
-//    one completion, not bandwidth, sets the time.
-template <bool kRoundScale, int kMaxN>
+//    one completion, not bandwidth, sets the time;
+//  * kParkTokens (multi-layer launches): the token key / score rows are parked
+//    in LDS after loading instead of staying in registers through the
+//    completion path.  That frees about 27 VGPRs (4 instead of 3 waves per
+//    SIMD), which a throughput-bound multi-layer launch needs, at the cost of
+//    an LDS round trip on a single call's critical path.
+template <bool kRoundScale, int kMaxN, bool kParkTokens>
 __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
     const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
@@ -412,6 +417,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   const int64_t rr = r < num_requests ? r : 0;   // waves past the batch read request 0, stop below
 
   __shared__ float4 s_ape[kPool * 32];
+  __shared__ uint4 s_tok[kParkTokens ? kReqPerBlock : 1][kParkTokens ? kMaxN : 1][2][16];
+  const int w = threadIdx.x >> 6;
   const ApeRegs ape_regs = load_ape(ape);
   int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
   uint4 kv[kMaxN], sv[kMaxN];
@@ -432,6 +439,24 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]), "v"(kv[t].x), "v"(kv[t].y),
                  "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x), "v"(sv[t].y), "v"(sv[t].z),
                  "v"(sv[t].w));
+  if constexpr (kParkTokens) {
+    // Rows 0 and 1 of the wave hold the key / score rows for the whole wave
+    // (LDS accesses of one wave are ordered, so no barrier is needed).
+#pragma unroll
+    for (int t = 0; t < kMaxN; ++t) {
+      if (q == 0) s_tok[w][t][0][c] = kv[t];
+      else if (q == 1) s_tok[w][t][1][c] = sv[t];
+    }
+  }
+  // Token t's key / score chunk c, from registers or from the parked copy.
+  auto tok_key = [&](int t) -> uint4 {
+    if constexpr (kParkTokens) return s_tok[w][t][0][c];
+    else return kv[t];
+  };
+  auto tok_score = [&](int t) -> uint4 {
+    if constexpr (kParkTokens) return s_tok[w][t][1][c];
+    else return sv[t];
+  };
   store_ape(s_ape, ape_regs);
   if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
 
@@ -452,8 +477,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
       if (mask & (1u << t)) {
         uint16_t* ring_k = ring + (int64_t)blk[t] * (2 * kPool * 128);
         const int slot = pos[t] & (kPool - 1);
-        reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = kv[t];
-        reinterpret_cast<uint4*>(ring_k + kPool * 128 + slot * 128)[c] = sv[t];
+        reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = tok_key(t);
+        reinterpret_cast<uint4*>(ring_k + kPool * 128 + slot * 128)[c] = tok_score(t);
       }
     }
   };
@@ -472,9 +497,15 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
       if (t == t1) {
         b1 = blk[t];
         l1 = loc[t];
-        k1 = kv[t];
-        s1 = sv[t];
+        if constexpr (!kParkTokens) {
+          k1 = kv[t];
+          s1 = sv[t];
+        }
       }
+    }
+    if constexpr (kParkTokens) {
+      k1 = tok_key(t1);
+      s1 = tok_score(t1);
     }
     const uint16_t* ring_k = ring + (int64_t)b1 * (2 * kPool * 128);
     const uint16_t* ring_s = ring_k + kPool * 128;
@@ -602,12 +633,23 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
   hipLaunchKernelGGL(KERNEL, grid, block, 0, stream, ring, num_blocks, tail_slot, key, key_sb, \
                      key_st, score, score_sb, score_st, ape, slot_mapping, positions,           \
                      num_requests, next_n, sink, ls)
+  const bool park = num_layers > 1;
   if (next_n <= 4) {
-    if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 4>));
-    else KVC_RING((pool16_ring_wave_kernel<false, 4>));
+    if (round_scale) {
+      if (park) KVC_RING((pool16_ring_wave_kernel<true, 4, true>));
+      else KVC_RING((pool16_ring_wave_kernel<true, 4, false>));
+    } else {
+      if (park) KVC_RING((pool16_ring_wave_kernel<false, 4, true>));
+      else KVC_RING((pool16_ring_wave_kernel<false, 4, false>));
+    }
   } else if (next_n <= 8) {
-    if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 8>));
-    else KVC_RING((pool16_ring_wave_kernel<false, 8>));
+    if (round_scale) {
+      if (park) KVC_RING((pool16_ring_wave_kernel<true, 8, true>));
+      else KVC_RING((pool16_ring_wave_kernel<true, 8, false>));
+    } else {
+      if (park) KVC_RING((pool16_ring_wave_kernel<false, 8, true>));
+      else KVC_RING((pool16_ring_wave_kernel<false, 8, false>));
+    }
   } else {
     grid = dim3((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock),
                 (unsigned)num_layers);
