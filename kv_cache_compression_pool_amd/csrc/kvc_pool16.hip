@@ -421,7 +421,12 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   const int w = threadIdx.x >> 6;
   const ApeRegs ape_regs = load_ape(ape);
   int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
-  uint4 kv[kMaxN], sv[kMaxN];
+  // Without parking every row of the wave loads every token's key and score
+  // chunk c (the rows need them in registers); with parking the wave's four
+  // rows share the 2*kMaxN row loads, kMaxN/2 each.
+  constexpr int kTokRegs = kParkTokens ? 1 : kMaxN;
+  constexpr int kParkLoads = (2 * kMaxN + 3) / 4;
+  uint4 kv[kTokRegs], sv[kTokRegs], pk[kParkTokens ? kParkLoads : 1];
 #pragma unroll
   for (int t = 0; t < kMaxN; ++t) {
     const int tt = t < next_n ? t : next_n - 1;   // in bounds; entries t >= next_n are unused
@@ -429,23 +434,40 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     loc[t] = slot_mapping[e];
     pos[t] = positions[e];
     ts[t] = tail_slot[e];
-    kv[t] = reinterpret_cast<const uint4*>(key + rr * key_sb + tt * key_st)[c];
-    sv[t] = reinterpret_cast<const uint4*>(score + rr * score_sb + tt * score_st)[c];
+    if constexpr (!kParkTokens) {
+      kv[t] = reinterpret_cast<const uint4*>(key + rr * key_sb + tt * key_st)[c];
+      sv[t] = reinterpret_cast<const uint4*>(score + rr * score_sb + tt * score_st)[c];
+    }
+  }
+  if constexpr (kParkTokens) {
+#pragma unroll
+    for (int j = 0; j < kParkLoads; ++j) {
+      const int g = 4 * j + q;                     // row g: token g / 2, key (0) or score (1)
+      const int gg = g < 2 * kMaxN ? g : 2 * kMaxN - 1;
+      const int t = gg >> 1;
+      const int tt = t < next_n ? t : next_n - 1;
+      const uint16_t* src = (gg & 1) ? score + rr * score_sb + tt * score_st
+                                     : key + rr * key_sb + tt * key_st;
+      pk[j] = reinterpret_cast<const uint4*>(src)[c];
+    }
   }
   // Pin the token loads above the barrier: otherwise they are sunk below it
   // and wait for the ape round trip instead of sharing it.
 #pragma unroll
   for (int t = 0; t < kMaxN; ++t)
-    asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]), "v"(kv[t].x), "v"(kv[t].y),
-                 "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x), "v"(sv[t].y), "v"(sv[t].z),
-                 "v"(sv[t].w));
-  if constexpr (kParkTokens) {
-    // Rows 0 and 1 of the wave hold the key / score rows for the whole wave
-    // (LDS accesses of one wave are ordered, so no barrier is needed).
+    asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]));
 #pragma unroll
-    for (int t = 0; t < kMaxN; ++t) {
-      if (q == 0) s_tok[w][t][0][c] = kv[t];
-      else if (q == 1) s_tok[w][t][1][c] = sv[t];
+  for (int t = 0; t < kTokRegs; ++t)
+    asm volatile("" ::"v"(kv[t].x), "v"(kv[t].y), "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x),
+                 "v"(sv[t].y), "v"(sv[t].z), "v"(sv[t].w));
+  if constexpr (kParkTokens) {
+    // Park the rows in LDS for the whole wave (LDS accesses of one wave are
+    // ordered, so no barrier is needed before the wave reads them back).
+#pragma unroll
+    for (int j = 0; j < kParkLoads; ++j) {
+      asm volatile("" ::"v"(pk[j].x), "v"(pk[j].y), "v"(pk[j].z), "v"(pk[j].w));
+      const int g = 4 * j + q;
+      if (g < 2 * kMaxN) s_tok[w][g >> 1][g & 1][c] = pk[j];
     }
   }
   // Token t's key / score chunk c, from registers or from the parked copy.
