@@ -121,6 +121,21 @@ def test_c128_fused_planner_matches_oracle_plans():
             assert e.value.code == kvc.KVC_ERR_PLAN
 
 
+def test_c128_fused_capacity_bound_exhaustive():
+    """The documented item bound floor(N/128) + 2B holds for every single
+    request with prefix and extend up to 400 tokens, and for pairs of them."""
+    for prefix in range(0, 400, 7):
+        for E in range(1, 400, 3):
+            n = kvc.kvc_c128_plan_prefill_fused([prefix + E], [E], E).size
+            assert n <= kvc.kvc_c128_fused_capacity(E, 1), (prefix, E)
+    g = np.random.default_rng(5)
+    for _ in range(500):
+        el = g.integers(1, 400, 2)
+        sl = el + g.integers(0, 400, 2)
+        N = int(el.sum())
+        assert kvc.kvc_c128_plan_prefill_fused(sl, el, N).size <= kvc.kvc_c128_fused_capacity(N, 2)
+
+
 def test_planner_errors():
     with pytest.raises(kvc.KvcError) as e:
         kvc.kvc_c128_plan_prefill([10], [11], 11)
