@@ -1,8 +1,9 @@
 // kvc_device.hpp -- gfx950 device building blocks shared by the kernels:
 // bf16 widening / rounding, base-2 exponentials, DPP lane exchanges inside a
-// 16-lane row and swizzles between two rows, the 128-point Walsh-Hadamard
-// butterfly over 32 lanes, and the e4m3 quantiser.  Everything here is wave64
-// code for CDNA4; no other target.
+// 16-lane row, swizzles between two rows, permlane swaps between the four
+// rows of a wave, the 128-point Walsh-Hadamard butterfly over 32 or 64 lanes,
+// and the e4m3 quantiser.  Everything here is wave64 code for CDNA4; no other
+// target.
 #pragma once
 
 #include <hip/hip_runtime.h>
