@@ -8,15 +8,18 @@ Headline workload (one "step" = one pass of the pool-16 path over the batch):
   power-of-two scales; tokens after each sequence's last full pool are not
   compressed.  Output: packed e4m3 [pools,128] + fp32 scales.
 
-The same JSON line also reports the pool-128 online decode (1024 requests),
-the pool-128 online ragged prefill (32 sequences) and the pool-16 ring decode
-(256 x 4 verify tokens), each against the HBM roofline, and the CPU oracle
-timed on the host.
+The same JSON line also reports, each against the HBM roofline: the pool-128
+online decode (1024 requests; single calls, a 64-call HIP graph and one
+launch over 64 layers), the pool-128 online ragged prefill (32 sequences; two
+launches and one), the pool-16 ring decode (256 x 4 verify tokens; one layer
+and 64), the extension rows (tail-ring seeding, paged output, e4m3
+epilogues, padded work items), and the CPU oracle timed on the host.
 
 Inputs are rotated over several device replicas whose combined footprint
 exceeds the 256 MB Infinity Cache, so the timed reads come from HBM.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --only prefill|c128 ...   (profiling runs)
 """
 from __future__ import annotations
 
