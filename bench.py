@@ -359,6 +359,20 @@ def bench_next_rows(args, torch, kvc, synth, stream):
     out = {}
     steps = max(args.steps // 2, 20)
 
+    # the single-sequence configuration (256 tokens, 16 pools, no pow2 scale):
+    # launch-bound, reported for completeness
+    d = synth.pool16_single(seed=0)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    k1, s1 = to_dev(torch, d["keys"]), to_dev(torch, d["scores"])
+    a1, r1 = to_dev(torch, d["ape"]), to_dev(torch, rows)
+    o1 = torch.empty((rows.size, 128), dtype=torch.uint8, device="cuda")
+    sc1 = torch.empty((rows.size,), device="cuda")
+    _, ev, _ = timed(lambda i: kvc.kvc_compress_prefill(k1, s1, a1, r1, rows.size, o1, sc1, False),
+                     max(args.steps, 50), 5, torch, stream)
+    out["pool16_single_sequence"] = {"workload": "pool16_single_256tok", "pools": int(rows.size),
+                                     "launch_us": round(ev * 1e3, 3),
+                                     "vectors_per_s": round(rows.size / (ev * 1e-3), 1)}
+
     # tail-ring seeding: every token's slot map is read, the last 16 tokens of
     # each request are copied (key + score rows in, ring rows out)
     d = synth.pool16_seed(seed=0)
