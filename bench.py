@@ -350,11 +350,12 @@ def bench_ring(args, torch, kvc, synth, stream):
 
 # ------------------------------------------------------------------ next rows
 def bench_next_rows(args, torch, kvc, synth, stream):
-    """The extensions beyond the core path, each on the configured workload it
-    applies to: tail-ring seeding from the 64-sequence prefill batch, the
-    paged (page size 1) cache write of the prefill, the rotate / e4m3
-    epilogue of the pool-128 paths, and the pool-128 prefill with its work
-    items padded to capacity (as a captured graph replays it)."""
+    """The single-sequence pool-16 configuration and the extensions beyond the
+    core path, each on the configured workload it applies to: tail-ring
+    seeding from the 64-sequence prefill batch, the paged (page size 1) cache
+    write of the prefill, the rotate / e4m3 epilogue of the pool-128 paths, and
+    the pool-128 prefill with its work items padded to capacity (as a captured
+    graph replays it)."""
     import numpy as np
     out = {}
     steps = max(args.steps // 2, 20)
