@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # Tests marked gpu are skipped (not failed) when no GPU is visible, so the
-    # CPU suite stays green; on a GPU machine they run against the HIP library.
+    # CPU suite stays green; on an MI355X they run against the HIP library.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
