@@ -416,10 +416,15 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   const int64_t r = (int64_t)blockIdx.x * kReqPerBlock + (threadIdx.x >> 6);
   const int64_t rr = r < num_requests ? r : 0;   // waves past the batch read request 0, stop below
 
-  __shared__ float4 s_ape[kPool * 32];
   __shared__ uint4 s_tok[kParkTokens ? kReqPerBlock : 1][kParkTokens ? kMaxN : 1][2][16];
+  __shared__ float4 s_ape[kParkTokens ? kPool * 32 : 1];
   const int w = threadIdx.x >> 6;
-  const ApeRegs ape_regs = load_ape(ape);
+  // Multi-layer launches stage ape once per workgroup in LDS (its registers
+  // would cost occupancy); single calls load each completing lane's ape
+  // values with the ring rows instead, which keeps the barrier and the ape
+  // load off the chain of waves that only stash.
+  ApeRegs ape_regs;
+  if constexpr (kParkTokens) ape_regs = load_ape(ape);
   int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
   // Without parking every row of the wave loads every token's key and score
   // chunk c (the rows need them in registers); with parking the wave's four
@@ -451,8 +456,8 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
       pk[j] = reinterpret_cast<const uint4*>(src)[c];
     }
   }
-  // Pin the token loads above the barrier: otherwise they are sunk below it
-  // and wait for the ape round trip instead of sharing it.
+  // Issue every token load in this one round trip (the compiler would
+  // otherwise sink some of them next to their first use).
 #pragma unroll
   for (int t = 0; t < kMaxN; ++t)
     asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]));
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     if constexpr (kParkTokens) return s_tok[w][t][1][c];
     else return sv[t];
   };
-  store_ape(s_ape, ape_regs);
+  if constexpr (kParkTokens) store_ape(s_ape, ape_regs);
   if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
 
   int32_t blk[kMaxN];
@@ -531,17 +536,32 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     }
     const uint16_t* ring_k = ring + (int64_t)b1 * (2 * kPool * 128);
     const uint16_t* ring_s = ring_k + kPool * 128;
+    // The ring rows of the pool (and, for single calls, the lane's ape values:
+    // slots 4q..4q+3, channels 8c..8c+7) in one round trip.
     uint4 S[4], K[4];
+    float4 A[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int slot = 4 * q + i;
       S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
       K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
+      if constexpr (!kParkTokens) {
+        const float4* ap = reinterpret_cast<const float4*>(ape) + slot * 32 + 2 * c;
+        A[i][0] = ap[0];
+        A[i][1] = ap[1];
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       asm volatile("" ::"v"(S[i].x), "v"(S[i].y), "v"(S[i].z), "v"(S[i].w), "v"(K[i].x),
                    "v"(K[i].y), "v"(K[i].z), "v"(K[i].w));
+    if constexpr (kParkTokens) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A[i][0] = s_ape[(4 * q + i) * 32 + 2 * c];
+        A[i][1] = s_ape[(4 * q + i) * 32 + 2 * c + 1];
+      }
+    }
     // Slot 15 is the completing token itself: row 3 replaces what it read
     // there (a load kept unconditional so the row loads stay branch-free).
     if (q == 3) {
@@ -549,12 +569,6 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
       K[3] = k1;
     }
     float x[2];
-    float4 A[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      A[i][0] = s_ape[(4 * q + i) * 32 + 2 * c];
-      A[i][1] = s_ape[(4 * q + i) * 32 + 2 * c + 1];
-    }
     pool_mean_wave(S, K, A, x);
     if (sink.dbg && l1 < sink.rows)   // channels 8c + 2q + t
       reinterpret_cast<float2*>(sink.dbg + (int64_t)l1 * 128)[4 * c + q] = make_float2(x[0], x[1]);
