@@ -686,6 +686,10 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
       if (park) KVC_RING((pool16_ring_wave_kernel<false, 8, true>));
       else KVC_RING((pool16_ring_wave_kernel<false, 8, false>));
     }
+  } else if (next_n <= 16) {
+    // 16 tokens' rows do not fit in registers: always parked in LDS
+    if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 16, true>));
+    else KVC_RING((pool16_ring_wave_kernel<false, 16, true>));
   } else {
     grid = dim3((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock),
                 (unsigned)num_layers);
