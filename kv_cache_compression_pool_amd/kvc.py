@@ -105,12 +105,24 @@ def _check(rc: int) -> None:
         raise KvcError(rc, lib().kvc_last_error().decode())
 
 
+_current_stream = None
+
+
 def _stream(stream) -> int | None:
     """hipStream_t handle: None = torch's current stream; a torch.cuda.Stream
     or a raw integer handle is used as given."""
+    global _current_stream
     if stream is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _current_stream is None:
+            import torch
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            dev = getattr(torch._C, "_cuda_getDevice", None)
+            if raw is not None and dev is not None:
+                # the handle without building a Stream object (a few us per call)
+                _current_stream = lambda: raw(dev())
+            else:
+                _current_stream = lambda: torch.cuda.current_stream().cuda_stream
+        return _current_stream()
     if hasattr(stream, "cuda_stream"):
         return int(stream.cuda_stream)
     return int(stream)
