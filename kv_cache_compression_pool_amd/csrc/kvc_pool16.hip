@@ -57,15 +57,9 @@ __device__ __forceinline__ void widen8(uint4 w, float (&f)[8]) {
   f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
-// Stage ape [16][128] fp32 into LDS as float4 [16][32].
-__device__ __forceinline__ void stage_ape(float4* s_ape, const float* __restrict__ ape) {
-  const float4* src = reinterpret_cast<const float4*>(ape);
-  for (int i = threadIdx.x; i < kPool * 32; i += blockDim.x) s_ape[i] = src[i];
-  __syncthreads();
-}
-
-// The same in two steps for a block of kBlock threads (2 float4 each), so the
-// ape loads can be issued before the slot-row loads.
+// Stage ape [16][128] fp32 into LDS as float4 [16][32], in two steps for a
+// block of kBlock threads (2 float4 each), so the ape loads can be issued
+// before the slot-row loads.
 struct ApeRegs {
   float4 a, b;
 };
@@ -298,101 +292,29 @@ struct RingLayers {
   int64_t ring, key, score, ape, out_rows;
 };
 
-// Tail-ring decode: 32 lanes per request (row h owns ring slots 8h..8h+7),
-// tokens strictly in order.  A token's key / score row is stashed by the row
-// that later reads that slot in a completion, so every ring read sees the
-// stashes of earlier tokens from the same lanes in program order.
-template <bool kRoundScale>
-__global__ __launch_bounds__(kBlock) void pool16_ring_kernel(
-    uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
-    const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
-    const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
-    const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
-    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink,
-    RingLayers ls) {
-  {
-    const int64_t layer = blockIdx.y;
-    ring += layer * ls.ring;
-    key += layer * ls.key;
-    score += layer * ls.score;
-    ape += layer * ls.ape;
-    sink = sink.advanced(layer * ls.out_rows);
-  }
-  __shared__ float4 s_ape[kPool * 32];
-  stage_ape(s_ape, ape);
-
-  const int c = threadIdx.x & 15;
-  const int h = (threadIdx.x >> 4) & 1;
-  const int64_t r = (int64_t)blockIdx.x * kPoolsPerBlock + (threadIdx.x >> 5);
-  if (r >= num_requests) return;
-
-  for (int t = 0; t < next_n; ++t) {
-    const int64_t e = r * next_n + t;
-    const int32_t loc = slot_mapping[e];
-    const int32_t pos = positions[e];
-    const int32_t ts = tail_slot[e];
-    const int64_t blk = (int64_t)(ts > 0 ? ts : 0) / kPool;
-    if (blk >= num_blocks) continue;
-    const bool complete = loc >= 0 && pos >= 0 && (pos & (kPool - 1)) == kPool - 1;
-    const bool stash = pos >= 0 && ts >= 0;
-    if (!complete && !stash) continue;
-
-    uint16_t* ring_k = ring + blk * (2 * kPool * 128);
-    uint16_t* ring_s = ring_k + kPool * 128;
-    const uint4 kv = reinterpret_cast<const uint4*>(key + r * key_sb + t * key_st)[c];
-    const uint4 sv = reinterpret_cast<const uint4*>(score + r * score_sb + t * score_st)[c];
-
-    if (complete) {
-      // Slots 0..14 come from the ring; slot 15 (row 1, i = 7) is this token.
-      uint4 S[kHalf], K[kHalf];
-#pragma unroll
-      for (int i = 0; i < kHalf; ++i) {
-        const int slot = kHalf * h + i;
-        if (slot == kPool - 1) {
-          S[i] = sv;
-          K[i] = kv;
-        } else {
-          S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
-          K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
-        }
-      }
-      float x[8];
-      pool_mean(S, K, s_ape, c, h, x);
-      if (sink.dbg && loc < sink.rows)
-        reinterpret_cast<float4*>(sink.dbg + (int64_t)loc * 128 + 8 * c)[h] =
-            h ? make_float4(x[4], x[5], x[6], x[7]) : make_float4(x[0], x[1], x[2], x[3]);
-      float scale;
-      const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
-      if (loc < sink.rows) sink.store(loc, c, h, codes, scale);
-    }
-    const int slot = pos & (kPool - 1);
-    if (stash && (slot >> 3) == h) {
-      reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = kv;
-      reinterpret_cast<uint4*>(ring_s + slot * 128)[c] = sv;
-    }
-  }
-}
-
-// Ring decode for short verify batches (next_n <= kMaxN) with one request per
-// wave.  The same ordered semantics as pool16_ring_kernel:
-//  * every token's maps and key / score rows are requested up front, in the
-//    same round trip as the ape table (staged in LDS; keeping each lane's
-//    ape values in registers instead measured no faster for one call and
-//    20% slower for multi-layer launches, whose occupancy the extra 24 VGPRs
-//    cut from 3 to 2 waves per SIMD);
-//  * the loop runs over completions, not tokens.  Before completion t* reads
-//    its ring block, the stashes of tokens [done, t*) are stored from the
-//    lanes that read those slots back: row q of the wave stashes and reads
-//    slots 4q..4q+3, so same-lane program order orders them;
-//  * a whole wave per request halves each lane's share of the softmax and
+// Tail-ring decode with one request per wave.  Request r processes its
+// tokens strictly in order (the page's semantics): a token at position p with
+// p % 16 == 15 and an output row completes the pool (ring slots 0..14 plus
+// itself), then every valid token stashes its key / score rows in ring slot
+// p % 16.
+//  * Tokens run in windows of kMaxN (one window unless next_n > kMaxN); a
+//    window's maps and key / score rows are requested in one round trip.
+//  * The loop runs over completions, not tokens.  Before completion t* reads
+//    its ring block, the stashes of the tokens before t* are stored from the
+//    lanes that read those slots back (row q of the wave owns slots
+//    4q..4q+3), so same-lane program order orders them.
+//  * A whole wave per request halves each lane's share of the softmax and
 //    rotation (4 slots x 8 channels, then 2 channels) compared with the
 //    32-lane layout: in this latency-bound call the dependent arithmetic of
-//    one completion, not bandwidth, sets the time;
-//  * kParkTokens (multi-layer launches): the token key / score rows are parked
-//    in LDS after loading instead of staying in registers through the
-//    completion path.  That frees about 27 VGPRs (4 instead of 3 waves per
-//    SIMD), which a throughput-bound multi-layer launch needs, at the cost of
-//    an LDS round trip on a single call's critical path.
+//    one completion, not bandwidth, sets the time.
+//  * ape: single calls load each completing lane's 32 ape values with the
+//    ring rows, so waves that only stash never read it and no barrier sits in
+//    the chain; multi-layer launches stage ape in LDS once per workgroup,
+//    because those registers would cost occupancy there.
+//  * kParkTokens (multi-layer launches, and windows of more than 8 tokens):
+//    the token rows are parked in LDS after loading (the wave's four rows
+//    share the loads) instead of staying in registers through the completion
+//    path: about 30 fewer VGPRs, for an LDS round trip on the critical path.
 template <bool kRoundScale, int kMaxN, bool kParkTokens>
 __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
@@ -425,56 +347,66 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   // load off the chain of waves that only stash.
   ApeRegs ape_regs;
   if constexpr (kParkTokens) ape_regs = load_ape(ape);
+  // Tokens are processed in windows of kMaxN (one window unless next_n >
+  // kMaxN): window tokens t = 0..kMaxN-1 are request tokens base + t.
   int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
   // Without parking every row of the wave loads every token's key and score
   // chunk c (the rows need them in registers); with parking the wave's four
   // rows share the 2*kMaxN row loads, kMaxN/2 each.
   constexpr int kTokRegs = kParkTokens ? 1 : kMaxN;
   constexpr int kParkLoads = (2 * kMaxN + 3) / 4;
-  uint4 kv[kTokRegs], sv[kTokRegs], pk[kParkTokens ? kParkLoads : 1];
+  uint4 kv[kTokRegs], sv[kTokRegs];
+  auto load_window = [&](int base) {
+    uint4 pk[kParkTokens ? kParkLoads : 1];
 #pragma unroll
-  for (int t = 0; t < kMaxN; ++t) {
-    const int tt = t < next_n ? t : next_n - 1;   // in bounds; entries t >= next_n are unused
-    const int64_t e = rr * next_n + tt;
-    loc[t] = slot_mapping[e];
-    pos[t] = positions[e];
-    ts[t] = tail_slot[e];
-    if constexpr (!kParkTokens) {
-      kv[t] = reinterpret_cast<const uint4*>(key + rr * key_sb + tt * key_st)[c];
-      sv[t] = reinterpret_cast<const uint4*>(score + rr * score_sb + tt * score_st)[c];
+    for (int t = 0; t < kMaxN; ++t) {
+      const int tt = base + t < next_n ? base + t : next_n - 1;   // in bounds; unused if clamped
+      const int64_t e = rr * next_n + tt;
+      loc[t] = slot_mapping[e];
+      pos[t] = positions[e];
+      ts[t] = tail_slot[e];
+      if constexpr (!kParkTokens) {
+        kv[t] = reinterpret_cast<const uint4*>(key + rr * key_sb + tt * key_st)[c];
+        sv[t] = reinterpret_cast<const uint4*>(score + rr * score_sb + tt * score_st)[c];
+      }
     }
-  }
-  if constexpr (kParkTokens) {
+    if constexpr (kParkTokens) {
 #pragma unroll
-    for (int j = 0; j < kParkLoads; ++j) {
-      const int g = 4 * j + q;                     // row g: token g / 2, key (0) or score (1)
-      const int gg = g < 2 * kMaxN ? g : 2 * kMaxN - 1;
-      const int t = gg >> 1;
-      const int tt = t < next_n ? t : next_n - 1;
-      const uint16_t* src = (gg & 1) ? score + rr * score_sb + tt * score_st
-                                     : key + rr * key_sb + tt * key_st;
-      pk[j] = reinterpret_cast<const uint4*>(src)[c];
+      for (int j = 0; j < kParkLoads; ++j) {
+        const int g = 4 * j + q;                     // row g: token g / 2, key (0) or score (1)
+        const int gg = g < 2 * kMaxN ? g : 2 * kMaxN - 1;
+        const int t = base + (gg >> 1);
+        const int tt = t < next_n ? t : next_n - 1;
+        const uint16_t* src = (gg & 1) ? score + rr * score_sb + tt * score_st
+                                       : key + rr * key_sb + tt * key_st;
+        pk[j] = reinterpret_cast<const uint4*>(src)[c];
+      }
     }
-  }
-  // Issue every token load in this one round trip (the compiler would
-  // otherwise sink some of them next to their first use).
+    // Issue every token load in this one round trip (the compiler would
+    // otherwise sink some of them next to their first use).
 #pragma unroll
-  for (int t = 0; t < kMaxN; ++t)
-    asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]));
+    for (int t = 0; t < kMaxN; ++t)
+      asm volatile("" ::"v"(loc[t]), "v"(pos[t]), "v"(ts[t]));
 #pragma unroll
-  for (int t = 0; t < kTokRegs; ++t)
-    asm volatile("" ::"v"(kv[t].x), "v"(kv[t].y), "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x),
-                 "v"(sv[t].y), "v"(sv[t].z), "v"(sv[t].w));
-  if constexpr (kParkTokens) {
-    // Park the rows in LDS for the whole wave (LDS accesses of one wave are
-    // ordered, so no barrier is needed before the wave reads them back).
+    for (int t = 0; t < kTokRegs; ++t)
+      asm volatile("" ::"v"(kv[t].x), "v"(kv[t].y), "v"(kv[t].z), "v"(kv[t].w), "v"(sv[t].x),
+                   "v"(sv[t].y), "v"(sv[t].z), "v"(sv[t].w));
+    if constexpr (kParkTokens) {
+      // Park the rows in LDS for the whole wave.  The hardware runs one
+      // wave's LDS accesses in order, so the earlier window's reads precede
+      // these writes and the writes precede the reads that follow; the empty
+      // asm statements keep the compiler from moving accesses across them.
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < kParkLoads; ++j) {
-      asm volatile("" ::"v"(pk[j].x), "v"(pk[j].y), "v"(pk[j].z), "v"(pk[j].w));
-      const int g = 4 * j + q;
-      if (g < 2 * kMaxN) s_tok[w][g >> 1][g & 1][c] = pk[j];
+      for (int j = 0; j < kParkLoads; ++j) {
+        asm volatile("" ::"v"(pk[j].x), "v"(pk[j].y), "v"(pk[j].z), "v"(pk[j].w));
+        const int g = 4 * j + q;
+        if (g < 2 * kMaxN) s_tok[w][g >> 1][g & 1][c] = pk[j];
+      }
+      asm volatile("" ::: "memory");
     }
-  }
+  };
+  load_window(0);
   // Token t's key / score chunk c, from registers or from the parked copy.
   auto tok_key = [&](int t) -> uint4 {
     if constexpr (kParkTokens) return s_tok[w][t][0][c];
@@ -487,13 +419,14 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   if constexpr (kParkTokens) store_ape(s_ape, ape_regs);
   if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
 
+  for (int base = 0;;) {   // uniform over the wave and the workgroup
   int32_t blk[kMaxN];
   uint32_t completes = 0, stashes = 0;
 #pragma unroll
   for (int t = 0; t < kMaxN; ++t) {
     const int64_t b = (int64_t)(ts[t] > 0 ? ts[t] : 0) / kPool;
     blk[t] = (int32_t)b;   // ts is int32, so the block index fits
-    if (t >= next_n || b >= num_blocks) continue;
+    if (base + t >= next_n || b >= num_blocks) continue;
     if (loc[t] >= 0 && pos[t] >= 0 && (pos[t] & (kPool - 1)) == kPool - 1) completes |= 1u << t;
     if (pos[t] >= 0 && ts[t] >= 0 && ((pos[t] & (kPool - 1)) >> 2) == q) stashes |= 1u << t;
   }
@@ -577,6 +510,13 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
     if (l1 < sink.rows) sink.store2(l1, c, q, codes, scale);
   }
   stash_range(stashes & ~done);
+  // Launches pick kMaxN >= next_n except for the 16-token instance, which is
+  // also the one that walks longer verify batches window by window.
+  if constexpr (kMaxN < 16) break;
+  base += kMaxN;
+  if (base >= next_n) break;
+  load_window(base);
+  }
 }
 
 // Tail-ring seeding.  Each lane decides for one token whether it is among its
@@ -686,15 +626,11 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
       if (park) KVC_RING((pool16_ring_wave_kernel<false, 8, true>));
       else KVC_RING((pool16_ring_wave_kernel<false, 8, false>));
     }
-  } else if (next_n <= 16) {
-    // 16 tokens' rows do not fit in registers: always parked in LDS
+  } else {
+    // 16 tokens' rows do not fit in registers: parked in LDS, and longer
+    // verify batches run in windows of 16 tokens
     if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 16, true>));
     else KVC_RING((pool16_ring_wave_kernel<false, 16, true>));
-  } else {
-    grid = dim3((unsigned)((num_requests + kPoolsPerBlock - 1) / kPoolsPerBlock),
-                (unsigned)num_layers);
-    if (round_scale) KVC_RING((pool16_ring_kernel<true>));
-    else KVC_RING((pool16_ring_kernel<false>));
   }
 #undef KVC_RING
   return hipGetLastError();

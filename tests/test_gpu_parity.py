@@ -280,8 +280,9 @@ def test_ring_decode_full_size_c3():
 
 
 # 1-4 and 5-8 take the whole-wave kernel with 4 / 8 prefetched tokens, longer
-# batches the per-token kernel.
-@pytest.mark.parametrize("next_n", [1, 2, 3, 5, 8, 9, 16, 21])
+# batches its 16-token form, window by window past 16 (21: a ragged second
+# window, 48: three full windows).
+@pytest.mark.parametrize("next_n", [1, 2, 3, 5, 8, 9, 16, 21, 48])
 def test_ring_decode_ordered_verify_tokens(next_n):
     d = synth.pool16_ring(seed=10 + next_n, num_requests=37, next_n=next_n, pad_frac=0.1)
     d["round_scale"] = next_n % 2 == 1

@@ -37,7 +37,7 @@ def test_sweep_pool16_prefill(case):
 @pytest.mark.parametrize("case", range(CASES))
 def test_sweep_ring_decode(case):
     g = np.random.default_rng(3000 + case)
-    next_n = int(g.integers(1, 13))
+    next_n = int(g.integers(1, 37))   # up to three 16-token windows
     d = synth.pool16_ring(seed=4000 + case, num_requests=int(g.integers(1, 70)), next_n=next_n,
                           pad_frac=float(g.uniform(0, 0.3)))
     d["round_scale"] = bool(case % 2)
