@@ -500,22 +500,13 @@ int check_prefill(const char* fn, float* state, int64_t num_slots, const float* 
   return KVC_OK;
 }
 
-}  // namespace
-
-int kvc_c128_online_decode(float* state, int64_t num_slots, const float* kv_score_in, float* out,
-                           const float* ape, const int32_t* indices, const int32_t* seq_lens,
-                           int64_t batch, void* stream) {
-  return kvc_c128_online_decode_layers(state, 0, num_slots, kv_score_in, 0, out, 0, ape, 0,
-                                       indices, seq_lens, batch, 1, stream);
-}
-
-int kvc_c128_online_decode_layers(float* state, int64_t state_layer_stride, int64_t num_slots,
-                                  const float* kv_score_in, int64_t in_layer_stride, float* out,
-                                  int64_t out_layer_stride, const float* ape,
-                                  int64_t ape_layer_stride, const int32_t* indices,
-                                  const int32_t* seq_lens, int64_t batch, int64_t num_layers,
-                                  void* stream) {
-  const char* fn = "kvc_c128_online_decode";
+// fp32-output decode over num_layers layers (layer strides in elements;
+// ignored for one layer).
+int c128_decode_fp32(const char* fn, float* state, int64_t state_layer_stride, int64_t num_slots,
+                     const float* kv_score_in, int64_t in_layer_stride, float* out,
+                     int64_t out_layer_stride, const float* ape, int64_t ape_layer_stride,
+                     const int32_t* indices, const int32_t* seq_lens, int64_t batch,
+                     int64_t num_layers, void* stream) {
   if (batch < 0 || num_slots < 0 || num_layers < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
   if (batch == 0 || num_layers == 0) return ok();
   int rc = check_decode(fn, state, num_slots, kv_score_in, ape, indices, seq_lens, batch);
@@ -529,11 +520,32 @@ int kvc_c128_online_decode_layers(float* state, int64_t state_layer_stride, int6
        state_layer_stride % 4 || in_layer_stride % 4 || out_layer_stride % 4 ||
        ape_layer_stride % 4))
     return fail(KVC_ERR_SHAPE, "%s: layer strides must cover a layer and keep 16-byte rows", fn);
+  if (num_layers == 1) state_layer_stride = in_layer_stride = out_layer_stride = ape_layer_stride = 0;
   return hip_status(kvc::launch_c128_decode(state, state_layer_stride, num_slots, kv_score_in,
                                             in_layer_stride, out, out_layer_stride, nullptr,
                                             nullptr, false, ape, ape_layer_stride, indices,
                                             seq_lens, batch, num_layers, (hipStream_t)stream),
-                    "kvc_c128_online_decode launch");
+                    fn);
+}
+
+}  // namespace
+
+int kvc_c128_online_decode(float* state, int64_t num_slots, const float* kv_score_in, float* out,
+                           const float* ape, const int32_t* indices, const int32_t* seq_lens,
+                           int64_t batch, void* stream) {
+  return c128_decode_fp32("kvc_c128_online_decode", state, 0, num_slots, kv_score_in, 0, out, 0,
+                          ape, 0, indices, seq_lens, batch, 1, stream);
+}
+
+int kvc_c128_online_decode_layers(float* state, int64_t state_layer_stride, int64_t num_slots,
+                                  const float* kv_score_in, int64_t in_layer_stride, float* out,
+                                  int64_t out_layer_stride, const float* ape,
+                                  int64_t ape_layer_stride, const int32_t* indices,
+                                  const int32_t* seq_lens, int64_t batch, int64_t num_layers,
+                                  void* stream) {
+  return c128_decode_fp32("kvc_c128_online_decode_layers", state, state_layer_stride, num_slots,
+                          kv_score_in, in_layer_stride, out, out_layer_stride, ape,
+                          ape_layer_stride, indices, seq_lens, batch, num_layers, stream);
 }
 
 int kvc_c128_online_decode_quant(float* state, int64_t num_slots, const float* kv_score_in,

@@ -193,6 +193,16 @@ def test_device_entry_points_validate_before_launch():
         == kvc.KVC_ERR_NULL
     assert L.kvc_c128_online_prefill(p, 4, p, p, 8, p, p, None, 1, ctypes.c_void_p(0x1008), 3,
                                      None, 0, None) == kvc.KVC_ERR_SHAPE
+    # multi-layer c128 decode: layer strides that overlap layers, too many layers
+    d = L.kvc_c128_online_decode_layers
+    assert d(p, 4 * 384 - 4, 4, p, 2 * 256, p, 2 * 128, p, 128 * 128, p, p, 2, 3, None) \
+        == kvc.KVC_ERR_SHAPE
+    assert b"kvc_c128_online_decode_layers" in L.kvc_last_error()
+    assert d(p, 4 * 384, 4, p, 2 * 256, p, 2 * 128 - 4, p, 128 * 128, p, p, 2, 3, None) \
+        == kvc.KVC_ERR_SHAPE
+    assert d(p, 4 * 384, 4, p, 2 * 256, p, 2 * 128, p, 128 * 128, p, p, 2, 70000, None) \
+        == kvc.KVC_ERR_SHAPE
+    assert d(p, 0, 4, p, 0, p, 0, p, 0, p, p, 2, 0, None) == kvc.KVC_OK
     # multi-layer ring decode: too many layers, layer strides that overlap layers
     r = L.kvc_compress_decode_ring_layers
     assert r(p, 4 * 4096, 4, p, p, 4 * 512, 512, 128, p, 4 * 512, 512, 128, p, 2048, p, p, 4, 4,
