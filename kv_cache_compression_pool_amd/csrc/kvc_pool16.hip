@@ -356,7 +356,16 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   constexpr int kTokRegs = kParkTokens ? 1 : kMaxN;
   constexpr int kParkLoads = (2 * kMaxN + 3) / 4;
   uint4 kv[kTokRegs], sv[kTokRegs];
-  auto load_window = [&](int base) {
+  // Token t's key / score chunk c, from registers or from the parked copy.
+  auto tok_key = [&](int t) -> uint4 {
+    if constexpr (kParkTokens) return s_tok[w][t][0][c];
+    else return kv[t];
+  };
+  auto tok_score = [&](int t) -> uint4 {
+    if constexpr (kParkTokens) return s_tok[w][t][1][c];
+    else return sv[t];
+  };
+  for (int base = 0;;) {   // windows; uniform over the wave and the workgroup
     uint4 pk[kParkTokens ? kParkLoads : 1];
 #pragma unroll
     for (int t = 0; t < kMaxN; ++t) {
@@ -405,117 +414,106 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
       }
       asm volatile("" ::: "memory");
     }
-  };
-  load_window(0);
-  // Token t's key / score chunk c, from registers or from the parked copy.
-  auto tok_key = [&](int t) -> uint4 {
-    if constexpr (kParkTokens) return s_tok[w][t][0][c];
-    else return kv[t];
-  };
-  auto tok_score = [&](int t) -> uint4 {
-    if constexpr (kParkTokens) return s_tok[w][t][1][c];
-    else return sv[t];
-  };
-  if constexpr (kParkTokens) store_ape(s_ape, ape_regs);
-  if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
-
-  for (int base = 0;;) {   // uniform over the wave and the workgroup
-  int32_t blk[kMaxN];
-  uint32_t completes = 0, stashes = 0;
-#pragma unroll
-  for (int t = 0; t < kMaxN; ++t) {
-    const int64_t b = (int64_t)(ts[t] > 0 ? ts[t] : 0) / kPool;
-    blk[t] = (int32_t)b;   // ts is int32, so the block index fits
-    if (base + t >= next_n || b >= num_blocks) continue;
-    if (loc[t] >= 0 && pos[t] >= 0 && (pos[t] & (kPool - 1)) == kPool - 1) completes |= 1u << t;
-    if (pos[t] >= 0 && ts[t] >= 0 && ((pos[t] & (kPool - 1)) >> 2) == q) stashes |= 1u << t;
-  }
-
-  auto stash_range = [&](uint32_t mask) {
-#pragma unroll
-    for (int t = 0; t < kMaxN; ++t) {
-      if (mask & (1u << t)) {
-        uint16_t* ring_k = ring + (int64_t)blk[t] * (2 * kPool * 128);
-        const int slot = pos[t] & (kPool - 1);
-        reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = tok_key(t);
-        reinterpret_cast<uint4*>(ring_k + kPool * 128 + slot * 128)[c] = tok_score(t);
-      }
+    if (base == 0) {
+      if constexpr (kParkTokens) store_ape(s_ape, ape_regs);
+      if (r >= num_requests) return;   // whole waves: the row exchanges below stay complete
     }
-  };
-
-  uint32_t done = 0;   // tokens whose stash has been stored: bits below the cursor
-  while (completes) {  // uniform over the wave: one request per wave
-    const int t1 = __builtin_ctz(completes);
-    completes &= completes - 1;
-    const uint32_t before = (1u << t1) - 1;
-    stash_range(stashes & before & ~done);
-    done = before;
-    int32_t b1 = 0, l1 = 0;
-    uint4 k1 = make_uint4(0, 0, 0, 0), s1 = k1;
+    int32_t blk[kMaxN];
+    uint32_t completes = 0, stashes = 0;
 #pragma unroll
     for (int t = 0; t < kMaxN; ++t) {
-      if (t == t1) {
-        b1 = blk[t];
-        l1 = loc[t];
-        if constexpr (!kParkTokens) {
-          k1 = kv[t];
-          s1 = sv[t];
+      const int64_t b = (int64_t)(ts[t] > 0 ? ts[t] : 0) / kPool;
+      blk[t] = (int32_t)b;   // ts is int32, so the block index fits
+      if (base + t >= next_n || b >= num_blocks) continue;
+      if (loc[t] >= 0 && pos[t] >= 0 && (pos[t] & (kPool - 1)) == kPool - 1) completes |= 1u << t;
+      if (pos[t] >= 0 && ts[t] >= 0 && ((pos[t] & (kPool - 1)) >> 2) == q) stashes |= 1u << t;
+    }
+
+    auto stash_range = [&](uint32_t mask) {
+#pragma unroll
+      for (int t = 0; t < kMaxN; ++t) {
+        if (mask & (1u << t)) {
+          uint16_t* ring_k = ring + (int64_t)blk[t] * (2 * kPool * 128);
+          const int slot = pos[t] & (kPool - 1);
+          reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = tok_key(t);
+          reinterpret_cast<uint4*>(ring_k + kPool * 128 + slot * 128)[c] = tok_score(t);
         }
       }
-    }
-    if constexpr (kParkTokens) {
-      k1 = tok_key(t1);
-      s1 = tok_score(t1);
-    }
-    const uint16_t* ring_k = ring + (int64_t)b1 * (2 * kPool * 128);
-    const uint16_t* ring_s = ring_k + kPool * 128;
-    // The ring rows of the pool (and, for single calls, the lane's ape values:
-    // slots 4q..4q+3, channels 8c..8c+7) in one round trip.
-    uint4 S[4], K[4];
-    float4 A[4][2];
+    };
+
+    uint32_t done = 0;   // tokens whose stash has been stored: bits below the cursor
+    while (completes) {  // uniform over the wave: one request per wave
+      const int t1 = __builtin_ctz(completes);
+      completes &= completes - 1;
+      const uint32_t before = (1u << t1) - 1;
+      stash_range(stashes & before & ~done);
+      done = before;
+      int32_t b1 = 0, l1 = 0;
+      uint4 k1 = make_uint4(0, 0, 0, 0), s1 = k1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = 4 * q + i;
-      S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
-      K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
-      if constexpr (!kParkTokens) {
-        const float4* ap = reinterpret_cast<const float4*>(ape) + slot * 32 + 2 * c;
-        A[i][0] = ap[0];
-        A[i][1] = ap[1];
+      for (int t = 0; t < kMaxN; ++t) {
+        if (t == t1) {
+          b1 = blk[t];
+          l1 = loc[t];
+          if constexpr (!kParkTokens) {
+            k1 = kv[t];
+            s1 = sv[t];
+          }
+        }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      asm volatile("" ::"v"(S[i].x), "v"(S[i].y), "v"(S[i].z), "v"(S[i].w), "v"(K[i].x),
-                   "v"(K[i].y), "v"(K[i].z), "v"(K[i].w));
-    if constexpr (kParkTokens) {
+      if constexpr (kParkTokens) {
+        k1 = tok_key(t1);
+        s1 = tok_score(t1);
+      }
+      const uint16_t* ring_k = ring + (int64_t)b1 * (2 * kPool * 128);
+      const uint16_t* ring_s = ring_k + kPool * 128;
+      // The ring rows of the pool (and, for single calls, the lane's ape
+      // values: slots 4q..4q+3, channels 8c..8c+7) in one round trip.
+      uint4 S[4], K[4];
+      float4 A[4][2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        A[i][0] = s_ape[(4 * q + i) * 32 + 2 * c];
-        A[i][1] = s_ape[(4 * q + i) * 32 + 2 * c + 1];
+        const int slot = 4 * q + i;
+        S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
+        K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
+        if constexpr (!kParkTokens) {
+          const float4* ap = reinterpret_cast<const float4*>(ape) + slot * 32 + 2 * c;
+          A[i][0] = ap[0];
+          A[i][1] = ap[1];
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        asm volatile("" ::"v"(S[i].x), "v"(S[i].y), "v"(S[i].z), "v"(S[i].w), "v"(K[i].x),
+                     "v"(K[i].y), "v"(K[i].z), "v"(K[i].w));
+      if constexpr (kParkTokens) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          A[i][0] = s_ape[(4 * q + i) * 32 + 2 * c];
+          A[i][1] = s_ape[(4 * q + i) * 32 + 2 * c + 1];
+        }
+      }
+      // Slot 15 is the completing token itself: row 3 replaces what it read
+      // there (a load kept unconditional so the row loads stay branch-free).
+      if (q == 3) {
+        S[3] = s1;
+        K[3] = k1;
+      }
+      float x[2];
+      pool_mean_wave(S, K, A, x);
+      if (sink.dbg && l1 < sink.rows)   // channels 8c + 2q + t
+        reinterpret_cast<float2*>(sink.dbg + (int64_t)l1 * 128)[4 * c + q] =
+            make_float2(x[0], x[1]);
+      float scale;
+      const uint32_t codes = rotate_quantise64(x, c, q, kRoundScale, scale);
+      if (l1 < sink.rows) sink.store2(l1, c, q, codes, scale);
     }
-    // Slot 15 is the completing token itself: row 3 replaces what it read
-    // there (a load kept unconditional so the row loads stay branch-free).
-    if (q == 3) {
-      S[3] = s1;
-      K[3] = k1;
-    }
-    float x[2];
-    pool_mean_wave(S, K, A, x);
-    if (sink.dbg && l1 < sink.rows)   // channels 8c + 2q + t
-      reinterpret_cast<float2*>(sink.dbg + (int64_t)l1 * 128)[4 * c + q] = make_float2(x[0], x[1]);
-    float scale;
-    const uint32_t codes = rotate_quantise64(x, c, q, kRoundScale, scale);
-    if (l1 < sink.rows) sink.store2(l1, c, q, codes, scale);
-  }
-  stash_range(stashes & ~done);
-  // Launches pick kMaxN >= next_n except for the 16-token instance, which is
-  // also the one that walks longer verify batches window by window.
-  if constexpr (kMaxN < 16) break;
-  base += kMaxN;
-  if (base >= next_n) break;
-  load_window(base);
+    stash_range(stashes & ~done);
+    // Launches pick kMaxN >= next_n except for the 16-token instance, which is
+    // also the one that walks longer verify batches window by window.
+    if constexpr (kMaxN < 16) break;
+    base += kMaxN;
+    if (base >= next_n) break;
   }
 }
 
