@@ -11,8 +11,8 @@ Headline workload (one "step" = one pass of the pool-16 path over the batch):
 The same JSON line also reports, each against the HBM roofline: the pool-128
 online decode (1024 requests; single calls, a 64-call HIP graph and one
 launch over 64 layers), the pool-128 online ragged prefill (32 sequences; two
-launches and one), the pool-16 ring decode (256 x 4 verify tokens; one layer
-and 64), the extension rows (tail-ring seeding, paged output, e4m3
+launches and one), the pool-16 ring decode (256 x 4 verify tokens; single
+calls, a 64-call HIP graph and one launch over 64 layers), the extension rows (tail-ring seeding, paged output, e4m3
 epilogues, padded work items), and the CPU oracle timed on the host.
 
 Inputs are rotated over several device replicas whose combined footprint
@@ -319,6 +319,38 @@ def bench_ring(args, torch, kvc, synth, stream):
     total_ms, ev_ms, host = timed(step, steps, max(args.warmup, 5), torch, stream)
     res = dict(requests=R_req, next_n=N, completions=comps, total_ms=total_ms, steps=steps,
                ev_ms=ev_ms, host_s=host, alg_bytes=alg)
+
+    # Sustained single calls, as for the pool-128 decode: 64 calls captured in
+    # one HIP graph, each on its own replica of the ring, keys and scores
+    # (replicas totalling more than twice the MALL, so the rows come from
+    # HBM); the graphs are replayed in turn.
+    G = 64
+    per_rep = (ring.numel() + key.numel() + score.numel()) * 2
+    RG = G * max(1, -(-(2 * MALL_BYTES) // (G * per_rep)))
+    rings = [ring.clone() for _ in range(RG)]
+    keys = [key.clone() for _ in range(RG)]
+    scores = [score.clone() for _ in range(RG)]
+
+    def step_r(i):
+        kvc.kvc_compress_decode_ring(rings[i], ts, keys[i], scores[i], ape, sm, pos, out, scl,
+                                     True)
+
+    graphs = []
+    for gi in range(RG // G):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(G):
+                step_r(gi * G + k)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    def replay(i):
+        graphs[i % len(graphs)].replay()
+
+    n_rep = max(args.steps // 10, 8)
+    tg, evg, _ = timed(replay, n_rep, 2, torch, stream, host_us_per_call=100.0)
+    res["graph"] = dict(calls=G, replays=n_rep, total_ms=tg, call_ms=evg / G, replicas=RG)
+    del graphs, rings, keys, scores
 
     # Multi-layer form: the same requests and tokens in each of `layers`
     # layers (own ring, keys, scores and ape per layer) in one launch; the
@@ -674,6 +706,13 @@ def main():
             "tokens_per_s": round(c3["requests"] * c3["next_n"] * c3["steps"] / (c3["total_ms"] * 1e-3), 1),
             "launch_us": round(c3["ev_ms"] * 1e3, 3), "bytes_per_launch": c3["alg_bytes"],
             "hbm_gbs": round(g3, 1), "hbm_frac": round(g3 / PEAK_HBM_GBS, 4)}
+        if "graph" in c3:
+            cg = c3["graph"]
+            gg = gbs(c3["alg_bytes"], cg["call_ms"])
+            line["ring_decode"]["graph_64_calls"] = {
+                "calls_per_graph": cg["calls"], "call_us": round(cg["call_ms"] * 1e3, 3),
+                "hbm_gbs": round(gg, 1), "hbm_frac": round(gg / PEAK_HBM_GBS, 4),
+                "replicas": cg["replicas"]}
         if "layers" in c3:
             cl = c3["layers"]
             gl = gbs(cl["alg_bytes"], cl["ev_ms"])
