@@ -2,12 +2,12 @@
 
 Every kernel forms its addresses in 64-bit arithmetic.  Each case places the
 rows it checks past the first 4 GiB of a large device allocation (pool-16
-keys and scores, the tail ring, the pool-128 state and ragged input), runs
-the kernel through the C ABI on the large buffers, and compares the result
-with the oracle run on compact copies of the same seeded rows.  The rest of
-each allocation is either never read or filled with zeros, whose outputs are
-known exactly.  The device holds 288 GB; a case allocates at most about
-11 GB and releases it.
+keys and scores, prefill tokens and the tail ring, the pool-128 state and
+ragged input), runs the kernel through the C ABI on the large buffers, and
+compares the result with the oracle run on compact copies of the same seeded
+rows.  The rest of each allocation is either never read or filled with
+zeros, whose outputs are known exactly.  The device holds 288 GB; a case
+allocates at most about 11 GB and releases it.
 """
 import numpy as np
 import pytest
@@ -108,6 +108,38 @@ def test_ring_decode_blocks_past_4gib():
     ref_c, ref_s, _ = reference_for(gx, ox, rc, rs, True, "ring decode past 4 GiB")
     check_codes(gc, ref_c, "ring decode past 4 GiB")
     check_scales(gsc, ref_s, True, "ring decode past 4 GiB")
+
+
+def test_seed_tail_ring_rows_and_blocks_past_4gib():
+    """The last request of a prefill batch: its 40 token rows sit past 4 GiB
+    (128 KiB row stride) and its ring block past 4 GiB of the ring."""
+    stride = 1 << 16
+    T = FOUR_GIB // (2 * stride) + 256                # 33,024 tokens
+    n_req = 40
+    nb = FOUR_GIB // 8192 + 1024
+    assert (T - n_req) * stride * 2 >= FOUR_GIB and (nb - 1) * 8192 >= FOUR_GIB
+    g = synth.rng(76, "large_seed")
+    kb = synth.bf16_normal(g, (n_req, 128))
+    sb = synth.bf16_normal(g, (n_req, 128))
+    ring0 = synth.bf16_normal(g, (1, 2, 16, 128))
+    pos = np.arange(n_req)
+    # compact oracle problem: one request, ring block 0
+    ring = ring0.copy()
+    oracle.seed_tail_ring(ring, kb, sb, (pos % 16).astype(np.int32))
+    note(f"tail-ring seeding: {T} tokens x {stride} elements, ring block {nb - 1} of {nb}")
+    buf = torch.empty((T, stride), dtype=torch.int16, device="cuda")
+    buf[T - n_req:, :128] = dev(kb, torch.int16)
+    buf[T - n_req:, 128:256] = dev(sb, torch.int16)
+    tslot = np.full(T, -1, np.int32)                  # earlier tokens: padding, never copied
+    tslot[T - n_req:] = 16 * (nb - 1) + pos % 16
+    big = torch.empty((nb, 2, 16, 128), dtype=torch.int16, device="cuda")
+    big[nb - 1:] = dev(ring0, torch.int16)
+    kvc.kvc_seed_tail_ring(big, buf[:, :128], buf[:, 128:256], dev(tslot))
+    torch.cuda.synchronize()
+    got = big[nb - 1:].cpu().numpy().view(np.uint16)
+    del buf, big
+    assert np.array_equal(got, ring)
+    assert not np.array_equal(ring, ring0)            # the request's last 16 tokens landed
 
 
 def test_c128_decode_state_past_4gib():
