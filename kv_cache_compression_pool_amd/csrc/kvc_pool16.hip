@@ -19,7 +19,9 @@
 //     and bits 3-6 across the 16 lanes of a row (DPP), the absmax is a DPP row
 //     reduction plus one swizzle, and each lane stores 4 codes, so the 128-byte
 //     code vector leaves as one coalesced 32-lane store.
-//   * Slot rows are streamed with non-temporal loads; ape ([16,128] fp32) is
+//   * Slot rows are streamed with non-temporal loads, through buffer
+//     resources with 32-bit offsets when keys and scores each span less than
+//     4 GiB (64-bit global addresses otherwise); ape ([16,128] fp32) is
 //     staged once per workgroup in LDS (measured faster than per-lane reads
 //     of ape through the L1).
 //   * At most 128 VGPRs, so four waves per SIMD keep enough loads in flight.
@@ -47,6 +49,23 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 // Streaming 128-bit load that does not keep the line in the caches.
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The same load through a buffer resource: the base address sits in scalar
+// registers and each lane adds a 32-bit byte offset, which spares the 64-bit
+// address arithmetic of the prefill's 16 row loads per lane (measured: 73.7%
+// instead of 71.6% of HBM peak on the ragged prefill).  Reads at or past the
+// resource's byte count return zeros.  Word 3 of the resource sets only
+// DATA_FORMAT = 32 bit (value 4 in bits 15..18); untyped loads take their
+// size from the instruction.  Cache-policy bit 1 is the non-temporal hint.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 load_stream(BufRsrc r, uint32_t byte_offset) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 2);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -234,13 +253,16 @@ struct OutSink {
   }
 };
 
-template <bool kRoundScale, bool kDbg>
+// kBuf: keys and scores each span less than 4 GiB (key_bytes / score_bytes
+// from their base), so the row loads go through buffer resources with 32-bit
+// offsets; otherwise through 64-bit global addresses.
+template <bool kRoundScale, bool kDbg, bool kBuf>
 __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
     const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
     int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
     const int32_t* __restrict__ src_rows, int64_t n_pools, OutSink sink,
     const int64_t* __restrict__ loc, const uint8_t* __restrict__ write_mask,
-    float* __restrict__ dbg) {
+    float* __restrict__ dbg, uint32_t key_bytes, uint32_t score_bytes) {
   __shared__ float4 s_ape[kPool * 32];
   const int c = threadIdx.x & 15;
   const int h = (threadIdx.x >> 4) & 1;
@@ -263,13 +285,24 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   uint4 S[kHalf], K[kHalf];
   {
     const int64_t row = (ok ? r0 : 0) + kHalf * h;
-    const uint4* sp = reinterpret_cast<const uint4*>(scores + row * score_stride) + c;
-    const uint4* kp = reinterpret_cast<const uint4*>(keys + row * key_stride) + c;
-    const int64_t ss = score_stride >> 3, ks = key_stride >> 3;
+    if constexpr (kBuf) {
+      const BufRsrc rs = make_rsrc(scores, score_bytes), rk = make_rsrc(keys, key_bytes);
+      const uint32_t so = (uint32_t)(row * score_stride * 2) + 16u * c;
+      const uint32_t ko = (uint32_t)(row * key_stride * 2) + 16u * c;
+      const uint32_t ss = (uint32_t)(score_stride * 2), ks = (uint32_t)(key_stride * 2);
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) S[i] = load_stream(sp + i * ss);
+      for (int i = 0; i < kHalf; ++i) S[i] = load_stream(rs, so + i * ss);
 #pragma unroll
-    for (int i = 0; i < kHalf; ++i) K[i] = load_stream(kp + i * ks);
+      for (int i = 0; i < kHalf; ++i) K[i] = load_stream(rk, ko + i * ks);
+    } else {
+      const uint4* sp = reinterpret_cast<const uint4*>(scores + row * score_stride) + c;
+      const uint4* kp = reinterpret_cast<const uint4*>(keys + row * key_stride) + c;
+      const int64_t ss = score_stride >> 3, ks = key_stride >> 3;
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) S[i] = load_stream(sp + i * ss);
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) K[i] = load_stream(kp + i * ks);
+    }
   }
   store_ape(s_ape, ape_regs);
   if (!ok) return;
@@ -576,14 +609,28 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
   const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
   const OutSink sink{out_fp8, out_scale, out_rows, paged, nullptr};
-#define KVC_LAUNCH(RS, DBG)                                                                   \
-  hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG>), grid, block, 0, stream, keys,          \
+  // Bytes from each base to the end of its last row: buffer loads when both
+  // fit in 32-bit offsets.
+  const int64_t key_bytes = (num_rows - 1) * key_stride * 2 + 256;
+  const int64_t score_bytes = (num_rows - 1) * score_stride * 2 + 256;
+  const bool buf = key_bytes < (1LL << 32) && score_bytes < (1LL << 32);
+  const uint32_t kb = buf ? (uint32_t)key_bytes : 0u, sb = buf ? (uint32_t)score_bytes : 0u;
+#define KVC_LAUNCH(RS, DBG, BUF)                                                              \
+  hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF>), grid, block, 0, stream, keys,     \
                      key_stride, scores, score_stride, num_rows, ape, src_rows, n_pools,     \
-                     sink, loc, write_mask, dbg)
-  if (round_scale) {
-    if (dbg) KVC_LAUNCH(true, true); else KVC_LAUNCH(true, false);
+                     sink, loc, write_mask, dbg, kb, sb)
+  if (buf) {
+    if (round_scale) {
+      if (dbg) KVC_LAUNCH(true, true, true); else KVC_LAUNCH(true, false, true);
+    } else {
+      if (dbg) KVC_LAUNCH(false, true, true); else KVC_LAUNCH(false, false, true);
+    }
   } else {
-    if (dbg) KVC_LAUNCH(false, true); else KVC_LAUNCH(false, false);
+    if (round_scale) {
+      if (dbg) KVC_LAUNCH(true, true, false); else KVC_LAUNCH(true, false, false);
+    } else {
+      if (dbg) KVC_LAUNCH(false, true, false); else KVC_LAUNCH(false, false, false);
+    }
   }
 #undef KVC_LAUNCH
   return hipGetLastError();
