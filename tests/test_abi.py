@@ -31,6 +31,14 @@ def test_library_exports_every_declared_symbol():
     assert L.kvc_version() >= 100
 
 
+def test_header_serves_a_plain_c_client(tmp_path):
+    """include/kvc.h compiles as C11 and the library links into a C program
+    (the client the GPU tests run; built here into a scratch path)."""
+    from tests.c_abi import build_client
+    out = build_client.build(str(tmp_path / "kvc_c_client"))
+    assert os.access(out, os.X_OK)
+
+
 def test_pool_planner_matches_oracle():
     g = np.random.default_rng(1)
     for _ in range(50):
