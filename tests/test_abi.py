@@ -243,6 +243,45 @@ def test_device_entry_points_validate_before_launch():
     assert b"even" in L.kvc_last_error()
 
 
+def test_last_error_is_per_thread():
+    """Each host thread reads the message of its own last failed call, even
+    while other threads fail differently at the same time."""
+    import threading
+    L = kvc.lib()
+    n = ctypes.c_int64()
+    bad_pool = np.array([32], np.int64)
+    errors = []
+
+    def fail_pool_size():
+        for _ in range(500):
+            rc = L.kvc_plan_pool_prefill(bad_pool.ctypes.data, 1, 8, None, 0, ctypes.byref(n))
+            msg = L.kvc_last_error()
+            if rc != kvc.KVC_ERR_UNSUPPORTED or b"pool_size 8" not in msg:
+                errors.append(("pool", rc, msg))
+
+    def fail_convert():
+        for _ in range(500):
+            rc = L.kvc_diag_convert(ctypes.c_void_p(0x1000), None, None, 3, None)
+            msg = L.kvc_last_error()
+            if rc != kvc.KVC_ERR_SHAPE or b"even" not in msg:
+                errors.append(("convert", rc, msg))
+
+    def succeed():
+        out = np.empty(2, np.int32)
+        for _ in range(500):
+            rc = L.kvc_plan_pool_prefill(bad_pool.ctypes.data, 1, 16, out.ctypes.data, 2,
+                                         ctypes.byref(ctypes.c_int64()))
+            if rc != kvc.KVC_OK or L.kvc_last_error() != b"":
+                errors.append(("ok", rc, L.kvc_last_error()))
+
+    threads = [threading.Thread(target=f) for f in (fail_pool_size, fail_convert, succeed) * 2]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
+
+
 def test_plan_struct_layout():
     assert kvc.PLAN_DTYPE.itemsize == 16
     assert kvc.ITEM_DTYPE.itemsize == 32
