@@ -826,3 +826,54 @@ def test_explicit_stream_argument():
         kvc.kvc_compress_prefill(k, s, a, r, n, c, sc, False, stream=handle)
         side.synchronize()
         assert torch.equal(c, ref_c) and torch.equal(sc, ref_s)
+
+
+def test_concurrent_streams_match_serial_calls():
+    """The library keeps no state between calls: pool-16 prefill, ring decode
+    and pool-128 decode issued on three streams at once, each on its own
+    buffers, give exactly what the same calls give one after another."""
+    p = synth.pool16_ragged(seed=21, num_seqs=12, max_len=900)
+    rows = kvc.kvc_plan_pool_prefill(p["seq_lens"])
+    n = rows.size
+    pk, ps, pa, pr = (dev(p["keys"], torch.int16), dev(p["scores"], torch.int16), dev(p["ape"]),
+                      dev(rows))
+    r = synth.pool16_ring(seed=22, num_requests=48, next_n=4)
+    rmaps = [dev(r[k]) for k in ("tail_slot_mapping", "slot_mapping", "positions")]
+    rk, rsc, ra = dev(r["key"], torch.int16), dev(r["score"], torch.int16), dev(r["ape"])
+    c = c128_decode_case(seed=23, batch=200, num_slots=400, emit_frac=0.2)
+    cx, ca, ci, cl = dev(c["kv_score_in"]), dev(c["ape"]), dev(c["indices"]), dev(c["seq_lens"])
+    reps = 6
+
+    def fresh():
+        return dict(
+            pc=[torch.zeros((n, 128), dtype=torch.uint8, device="cuda") for _ in range(reps)],
+            ps=[torch.zeros((n,), device="cuda") for _ in range(reps)],
+            ring=[dev(r["ring"], torch.int16) for _ in range(reps)],
+            rc=[torch.zeros((r["num_out"], 128), dtype=torch.uint8, device="cuda")
+                for _ in range(reps)],
+            rs=[torch.zeros((r["num_out"],), device="cuda") for _ in range(reps)],
+            st=[dev(c["state"]) for _ in range(reps)],
+            co=[torch.zeros((200, 128), device="cuda") for _ in range(reps)])
+
+    def run(b, i, streams):
+        s0, s1, s2 = streams
+        kvc.kvc_compress_prefill(pk, ps, pa, pr, n, b["pc"][i], b["ps"][i], True, stream=s0)
+        kvc.kvc_compress_decode_ring(b["ring"][i], rmaps[0], rk, rsc, ra, rmaps[1], rmaps[2],
+                                     b["rc"][i], b["rs"][i], True, stream=s1)
+        kvc.kvc_c128_online_decode(b["st"][i], cx, b["co"][i], ca, ci, cl, stream=s2)
+
+    serial = fresh()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    for i in range(reps):
+        run(serial, i, (cur, cur, cur))
+    torch.cuda.synchronize()
+    conc = fresh()
+    side = [torch.cuda.Stream() for _ in range(3)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        run(conc, i, side)
+    torch.cuda.synchronize()
+    for key in serial:
+        for i in range(reps):
+            assert torch.equal(serial[key][i].nan_to_num(7.0), conc[key][i].nan_to_num(7.0)), key
