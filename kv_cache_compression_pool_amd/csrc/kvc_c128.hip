@@ -86,21 +86,36 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
   const int64_t b = (int64_t)blockIdx.x * kReq + (threadIdx.x >> 5);
   const int q = threadIdx.x & 31;                       // channels 4q..4q+3
   if (b >= batch) return;
+  // Two dependent round trips: (slot, length, input row), then (ape row,
+  // stored state).  The empty asm statements take each group's values at
+  // once, so its loads issue together; otherwise the compiler sinks the row
+  // loads below the slot check and the state loads below the score sum,
+  // which makes three and four round trips.
   const int32_t idx = indices[b];
   const int32_t L = seq_lens[b];
   const float4* row = reinterpret_cast<const float4*>(in + layer * in_ls + b * 256);
   const float4 kv = row[q];
   const float4 sc = row[32 + q];
+  asm volatile("" ::"v"(idx), "v"(L), "v"(kv.x), "v"(kv.y), "v"(kv.z), "v"(kv.w), "v"(sc.x),
+               "v"(sc.y), "v"(sc.z), "v"(sc.w));
   if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
   const int c = (L - 1) & 127;
   const float4 bias = reinterpret_cast<const float4*>(ape + layer * ape_ls + c * 128)[q];
   float4* st = reinterpret_cast<float4*>(state + layer * state_ls + (int64_t)idx * 384);
+  float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f), s4 = m4, k4 = m4;
+  if (c != 0) {   // the first token of a chunk does not read the state
+    m4 = st[q];
+    s4 = st[32 + q];
+    k4 = st[64 + q];
+  }
+  asm volatile("" ::"v"(bias.x), "v"(bias.y), "v"(bias.z), "v"(bias.w), "v"(m4.x), "v"(m4.y),
+               "v"(m4.z), "v"(m4.w), "v"(s4.x), "v"(s4.y), "v"(s4.z), "v"(s4.w), "v"(k4.x),
+               "v"(k4.y), "v"(k4.z), "v"(k4.w));
 
   float s[4] = {sc.x + bias.x, sc.y + bias.y, sc.z + bias.z, sc.w + bias.w};
   float k[4] = {kv.x, kv.y, kv.z, kv.w};
   float M[4], S[4], K[4];
   if (c != 0) {
-    const float4 m4 = st[q], s4 = st[32 + q], k4 = st[64 + q];
     const float om[4] = {m4.x, m4.y, m4.z, m4.w};
     const float os[4] = {s4.x, s4.y, s4.z, s4.w};
     const float ok[4] = {k4.x, k4.y, k4.z, k4.w};
