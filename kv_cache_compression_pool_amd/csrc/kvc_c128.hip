@@ -8,8 +8,8 @@
 // Work mapping on MI355X:
 //   decode   one request per half-wave (32 lanes x float4 = one 512 B state
 //            row); two requests per 64-thread workgroup so even a small batch
-//            spreads over many CUs.  Loads that do not depend on the slot
-//            index (input row, lengths) are issued before the state load.
+//            spreads over many CUs.  Slots and lengths come through scalar
+//            loads; the input row, ape row and state then load together.
 //   prefill  one 512-thread workgroup per plan.  Wave w covers chunk
 //            positions [16w, 16w+16); its two half-waves take even / odd
 //            positions, 4 channels per lane, so every token row is read with
@@ -82,24 +82,32 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
     float* __restrict__ state, int64_t state_ls, int64_t num_slots, const float* __restrict__ in,
     int64_t in_ls, EmitSink o, const float* __restrict__ ape, int64_t ape_ls,
     const int32_t* __restrict__ indices, const int32_t* __restrict__ seq_lens, int64_t batch) {
+  static_assert(kReq == 1 || kReq % 2 == 0, "a wave holds two whole requests");
   const int64_t layer = blockIdx.y;
   const int64_t b = (int64_t)blockIdx.x * kReq + (threadIdx.x >> 5);
   const int q = threadIdx.x & 31;                       // channels 4q..4q+3
+  // One scalar round trip, then one vector round trip.  The slots and lengths
+  // of the wave's two requests are read at wave-uniform addresses (scalar
+  // loads, which return sooner than vector ones); the input row, the ape row
+  // (it depends on the length) and the stored state (it depends on the slot)
+  // then issue together, pinned by the empty asm statement below.  Measured:
+  // a single call 3.70 -> 3.38 us, 64 layers 75.3% -> 76.9% of HBM peak,
+  // against two vector round trips.
+  int32_t i0 = -1, i1 = -1, l0 = 0, l1 = 0;
+  {
+    const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t b0 = (int64_t)blockIdx.x * kReq + 2 * v;
+    if (b0 < batch) { i0 = indices[b0]; l0 = seq_lens[b0]; }
+    if (b0 + 1 < batch) { i1 = indices[b0 + 1]; l1 = seq_lens[b0 + 1]; }
+  }
   if (b >= batch) return;
-  // Two dependent round trips: (slot, length, input row), then (ape row,
-  // stored state).  The empty asm statements take each group's values at
-  // once, so its loads issue together; otherwise the compiler sinks the row
-  // loads below the slot check and the state loads below the score sum,
-  // which makes three and four round trips.
-  const int32_t idx = indices[b];
-  const int32_t L = seq_lens[b];
+  const int32_t idx = (threadIdx.x & 32) ? i1 : i0;
+  const int32_t L = (threadIdx.x & 32) ? l1 : l0;
+  if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
+  const int c = (L - 1) & 127;
   const float4* row = reinterpret_cast<const float4*>(in + layer * in_ls + b * 256);
   const float4 kv = row[q];
   const float4 sc = row[32 + q];
-  asm volatile("" ::"v"(idx), "v"(L), "v"(kv.x), "v"(kv.y), "v"(kv.z), "v"(kv.w), "v"(sc.x),
-               "v"(sc.y), "v"(sc.z), "v"(sc.w));
-  if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
-  const int c = (L - 1) & 127;
   const float4 bias = reinterpret_cast<const float4*>(ape + layer * ape_ls + c * 128)[q];
   float4* st = reinterpret_cast<float4*>(state + layer * state_ls + (int64_t)idx * 384);
   float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f), s4 = m4, k4 = m4;
@@ -108,9 +116,10 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
     s4 = st[32 + q];
     k4 = st[64 + q];
   }
-  asm volatile("" ::"v"(bias.x), "v"(bias.y), "v"(bias.z), "v"(bias.w), "v"(m4.x), "v"(m4.y),
-               "v"(m4.z), "v"(m4.w), "v"(s4.x), "v"(s4.y), "v"(s4.z), "v"(s4.w), "v"(k4.x),
-               "v"(k4.y), "v"(k4.z), "v"(k4.w));
+  asm volatile("" ::"v"(kv.x), "v"(kv.y), "v"(kv.z), "v"(kv.w), "v"(sc.x), "v"(sc.y), "v"(sc.z),
+               "v"(sc.w), "v"(bias.x), "v"(bias.y), "v"(bias.z), "v"(bias.w), "v"(m4.x),
+               "v"(m4.y), "v"(m4.z), "v"(m4.w), "v"(s4.x), "v"(s4.y), "v"(s4.z), "v"(s4.w),
+               "v"(k4.x), "v"(k4.y), "v"(k4.z), "v"(k4.w));
 
   float s[4] = {sc.x + bias.x, sc.y + bias.y, sc.z + bias.z, sc.w + bias.w};
   float k[4] = {kv.x, kv.y, kv.z, kv.w};
