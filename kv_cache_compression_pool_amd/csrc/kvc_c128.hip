@@ -8,8 +8,9 @@
 // Work mapping on MI355X:
 //   decode   one request per half-wave (32 lanes x float4 = one 512 B state
 //            row); two requests per 64-thread workgroup so even a small batch
-//            spreads over many CUs.  Slots and lengths come through scalar
-//            loads; the input row, ape row and state then load together.
+//            spreads over many CUs.  Two round trips: slots, lengths and
+//            input rows, then ape rows and states (multi-layer launches read
+//            slots and lengths through scalar loads first).
 //   prefill  one 512-thread workgroup per plan.  Wave w covers chunk
 //            positions [16w, 16w+16); its two half-waves take even / odd
 //            positions, 4 channels per lane, so every token row is read with
@@ -86,28 +87,46 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
   const int64_t layer = blockIdx.y;
   const int64_t b = (int64_t)blockIdx.x * kReq + (threadIdx.x >> 5);
   const int q = threadIdx.x & 31;                       // channels 4q..4q+3
-  // One scalar round trip, then one vector round trip.  The slots and lengths
-  // of the wave's two requests are read at wave-uniform addresses (scalar
-  // loads, which return sooner than vector ones); the input row, the ape row
-  // (it depends on the length) and the stored state (it depends on the slot)
-  // then issue together, pinned by the empty asm statement below.  Measured:
-  // a single call 3.70 -> 3.38 us, 64 layers 75.3% -> 76.9% of HBM peak,
-  // against two vector round trips.
-  int32_t i0 = -1, i1 = -1, l0 = 0, l1 = 0;
-  {
+  // Two round trips.  Each issues its loads together (the empty asm
+  // statements take all their values at once; without them the compiler had
+  // sunk the input-row loads below the slot check and the state loads below
+  // the score sum: three or four dependent round trips).
+  //  * Multi-layer launches (kReq > 2): the slots and lengths of the wave's
+  //    two requests are read at wave-uniform addresses, through scalar loads;
+  //    then the input row, the ape row (it depends on the length) and the
+  //    stored state (it depends on the slot) load together.  64 layers:
+  //    75.3% -> 76.9% of HBM peak against the two vector round trips below.
+  //  * Single calls: slot, length and input row, then ape row and state.  The
+  //    scalar form was faster back to back (3.38 instead of 3.67 us) but no
+  //    faster after an unrelated kernel (both 4.0 us) and slower under the
+  //    profiler's per-dispatch tracing (4.7 us), so single calls keep this.
+  constexpr bool kScalarSlots = kReq > 2;
+  int32_t idx, L;
+  float4 kv, sc;
+  const float4* row = reinterpret_cast<const float4*>(in + layer * in_ls + b * 256);
+  if constexpr (kScalarSlots) {
+    int32_t i0 = -1, i1 = -1, l0 = 0, l1 = 0;
     const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t b0 = (int64_t)blockIdx.x * kReq + 2 * v;
     if (b0 < batch) { i0 = indices[b0]; l0 = seq_lens[b0]; }
     if (b0 + 1 < batch) { i1 = indices[b0 + 1]; l1 = seq_lens[b0 + 1]; }
+    if (b >= batch) return;
+    idx = (threadIdx.x & 32) ? i1 : i0;
+    L = (threadIdx.x & 32) ? l1 : l0;
+    if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
+    kv = row[q];
+    sc = row[32 + q];
+  } else {
+    if (b >= batch) return;
+    idx = indices[b];
+    L = seq_lens[b];
+    kv = row[q];
+    sc = row[32 + q];
+    asm volatile("" ::"v"(idx), "v"(L), "v"(kv.x), "v"(kv.y), "v"(kv.z), "v"(kv.w), "v"(sc.x),
+                 "v"(sc.y), "v"(sc.z), "v"(sc.w));
+    if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
   }
-  if (b >= batch) return;
-  const int32_t idx = (threadIdx.x & 32) ? i1 : i0;
-  const int32_t L = (threadIdx.x & 32) ? l1 : l0;
-  if (L <= 0 || idx < 0 || (int64_t)idx >= num_slots) return;
   const int c = (L - 1) & 127;
-  const float4* row = reinterpret_cast<const float4*>(in + layer * in_ls + b * 256);
-  const float4 kv = row[q];
-  const float4 sc = row[32 + q];
   const float4 bias = reinterpret_cast<const float4*>(ape + layer * ape_ls + c * 128)[q];
   float4* st = reinterpret_cast<float4*>(state + layer * state_ls + (int64_t)idx * 384);
   float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f), s4 = m4, k4 = m4;
