@@ -293,6 +293,44 @@ def test_ring_decode_ordered_verify_tokens(next_n):
     check_scales(gs, rs, d["round_scale"], "ring scales")
 
 
+def irregular_ring_case(seed, num_requests, next_n):
+    """Positions drawn independently in [0, 60] (so a verify batch may close
+    several pools, revisit a slot or go backwards), each token in one of its
+    request's two ring blocks, 10% padding, 5% of valid tokens with a -1 tail
+    slot (read block 0, which no request owns; nothing is stashed)."""
+    g = np.random.default_rng(seed)
+    R, N = num_requests, next_n
+    pos = g.integers(0, 61, size=(R, N)).astype(np.int32)
+    pad = g.random((R, N)) < 0.1
+    blk = 1 + 2 * np.arange(R)[:, None] + g.integers(0, 2, size=(R, N))
+    ts = (16 * blk + pos % 16).astype(np.int32)
+    ts[~pad & (g.random((R, N)) < 0.05)] = -1
+    closes = ~pad & (pos % 16 == 15) & (g.random((R, N)) < 0.9)
+    loc = np.full((R, N), -1, np.int32)
+    loc[closes] = g.permutation(int(closes.sum())).astype(np.int32)
+    pos[pad], ts[pad], loc[pad] = -1, -1, -1
+    key = synth.bf16_normal(g, (R, N, 128))
+    score = synth.bf16_normal(g, (R, N, 128))
+    key[pad] = synth.BF16_NAN
+    score[pad] = synth.BF16_NAN
+    return dict(ring=synth.bf16_normal(g, (2 * R + 1, 2, 16, 128)), tail_slot_mapping=ts,
+                key=key, score=score, ape=synth.ape_pool16(g), slot_mapping=loc, positions=pos,
+                num_out=int(closes.sum()) + 3, round_scale=bool(seed % 2))
+
+
+@pytest.mark.parametrize("next_n", [4, 8, 13, 24])
+def test_ring_decode_irregular_positions(next_n):
+    """Several completions per verify batch, repeated slots and tokens in
+    different blocks: every instance (4, 8, 16 tokens; windows past 16) keeps
+    the per-request token order."""
+    d = irregular_ring_case(70 + next_n, 24, next_n)
+    note(f"ring decode irregular 24x{next_n}: {d['num_out'] - 3} completions")
+    gring, gc, gs, ring, rc, rs = run_ring(d)
+    assert np.array_equal(gring, ring)
+    check_codes(gc, rc, "irregular ring codes")
+    check_scales(gs, rs, d["round_scale"], "irregular ring scales")
+
+
 def test_ring_decode_sentinel_tail_slot_and_out_of_range_loc():
     d = synth.pool16_ring(seed=3, num_requests=4, next_n=2, pad_frac=0.0)
     # requests own ring blocks 1..4; block 0 is read only through the sentinel
