@@ -380,6 +380,35 @@ def bench_ring(args, torch, kvc, synth, stream):
     return res
 
 
+# ------------------------------------------------------------------ host planners
+def bench_planners(kvc, synth, reps=200):
+    """Host planner cost per call (the C planner through the binding, which
+    allocates the output arrays) on the configured batches: pool start rows
+    of the 64-sequence pool-16 batch, the pool-128 segment plans and the
+    single-launch work items of the 32-sequence pool-128 batch."""
+    p = synth.pool16_ragged(seed=0)
+    c = synth.c128_prefill(seed=0)
+    n_tok = int(c["extend_lens"].sum())
+    calls = {
+        "pool16_plan_64seq": lambda: kvc.kvc_plan_pool_prefill(p["seq_lens"]),
+        "c128_plan_32seq": lambda: kvc.kvc_c128_plan_prefill(c["seq_lens"], c["extend_lens"],
+                                                             n_tok),
+        "c128_plan_fused_32seq": lambda: kvc.kvc_c128_plan_prefill_fused(
+            c["seq_lens"], c["extend_lens"], n_tok),
+    }
+    out = {}
+    for name, f in calls.items():
+        f()
+        best = float("inf")
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                f()
+            best = min(best, (time.perf_counter() - t0) / reps)
+        out[name + "_us"] = round(best * 1e6, 2)
+    return out
+
+
 # ------------------------------------------------------------------ next rows
 def bench_next_rows(args, torch, kvc, synth, stream):
     """The single-sequence pool-16 configuration and the extensions beyond the
@@ -724,6 +753,7 @@ def main():
                 "hbm_frac": round(gl / PEAK_HBM_GBS, 4), "replicas": cl["replicas"]}
         log("next rows (seeding, paged write, epilogues, padding)")
         line["next_rows"] = bench_next_rows(args, torch, kvc, synth, stream)
+        line["host_planners"] = bench_planners(kvc, synth)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(p)

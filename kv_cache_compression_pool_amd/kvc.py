@@ -159,6 +159,14 @@ def _np_ptr(a):
     return None if a is None else a.ctypes.data
 
 
+def _head(a: np.ndarray, n: int) -> np.ndarray:
+    """A compact copy of the first n records of a structured array (copied
+    as bytes: numpy copies structured records field by field, ~15x slower)."""
+    out = np.empty(n, a.dtype)
+    out.view(np.uint8)[:] = a[:n].view(np.uint8)
+    return out
+
+
 # ------------------------------------------------------------------ planners
 def kvc_plan_pool_prefill(seq_lens, pool_size: int = 16) -> np.ndarray:
     """First row of every complete pool of a ragged batch (host int32 array)."""
@@ -178,13 +186,15 @@ def kvc_c128_plan_prefill(seq_lens, extend_lens, num_tokens: int, pad_to_capacit
     if sl.size != el.size:
         raise ValueError("seq_lens and extend_lens differ in length")
     cap = max(int(num_tokens), 1)
-    cp = np.zeros(cap, PLAN_DTYPE)
-    wp = np.zeros(cap, PLAN_DTYPE)
+    # capacity is one entry per token; only the entries written are returned,
+    # so the buffers need no clearing (untouched pages are never faulted in)
+    cp = np.empty(cap, PLAN_DTYPE)
+    wp = np.empty(cap, PLAN_DTYPE)
     nc, nw = ctypes.c_uint32(), ctypes.c_uint32()
     _check(lib().kvc_c128_plan_prefill(_np_ptr(sl), _np_ptr(el), sl.size, int(num_tokens),
                                        _np_ptr(cp), _np_ptr(wp), int(pad_to_capacity),
                                        ctypes.byref(nc), ctypes.byref(nw)))
-    return cp[:nc.value].copy(), wp[:nw.value].copy()
+    return _head(cp, nc.value), _head(wp, nw.value)
 
 
 def kvc_c128_fused_capacity(num_tokens: int, max_batch: int) -> int:
@@ -204,12 +214,12 @@ def kvc_c128_plan_prefill_fused(seq_lens, extend_lens, num_tokens: int,
         raise ValueError("seq_lens and extend_lens differ in length")
     if capacity is None:
         capacity = kvc_c128_fused_capacity(num_tokens, sl.size)
-    items = np.zeros(max(int(capacity), 1), ITEM_DTYPE)
+    items = np.empty(max(int(capacity), 1), ITEM_DTYPE)
     n = ctypes.c_uint32()
     _check(lib().kvc_c128_plan_prefill_fused(_np_ptr(sl), _np_ptr(el), sl.size, int(num_tokens),
                                              _np_ptr(items), int(capacity), int(pad_to_capacity),
                                              ctypes.byref(n)))
-    return items[:n.value].copy()
+    return _head(items, n.value)
 
 
 # ------------------------------------------------------------------ device entry points
