@@ -580,6 +580,8 @@ def cpu_baseline(res, passes=30):
     dt = time.perf_counter() - t0
     return {"value": round(n * passes / dt, 1), "unit": "vectors/s", "cores": threads,
             "kind": "oracle", "single_thread_value": round(n / dt1, 1), "cpu": cpu_model(),
+            "gbs": round(res["alg_bytes"] * passes / dt / 1e9, 2),
+            "single_thread_gbs": round(res["alg_bytes"] / dt1 / 1e9, 3),
             "sample": f"full pool-16 ragged batch ({n} pools): 1 pass on 1 thread "
                       f"({dt1:.2f} s), then {passes} passes split over {threads} threads "
                       f"({dt:.2f} s wall)"}
