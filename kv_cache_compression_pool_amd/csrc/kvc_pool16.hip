@@ -6,29 +6,33 @@
 // Walsh-Hadamard rotation / sqrt(128), bf16 round, per-vector fp8 e4m3 scale.
 //
 // Work mapping (MI355X-first, not the pages' one-program-per-pool layout):
-//   * A pool is owned by 32 lanes: two 16-lane DPP rows, row h taking slots
-//     8h..8h+7.  Lane c of a row owns channels 8c..8c+7, so each slot row of
-//     keys or scores is one 128-bit load per lane (16 lanes x 16 B = the
-//     256 B bf16 row).  A wave compresses two pools.
-//   * Each lane runs the two-pass softmax over its 8 slots x 8 channels in
-//     fp32 registers.  The rows exchange only their per-channel max (before
-//     the exponentials, so no rescaling is needed) and their partial sums,
-//     with one ds_swizzle each.
-//   * The epilogue is split between the rows (4 channels per lane): the
-//     rotation keeps channel bits 0-1 in registers, bit 2 across the two rows
-//     and bits 3-6 across the 16 lanes of a row (DPP), the absmax is a DPP row
-//     reduction plus one swizzle, and each lane stores 4 codes, so the 128-byte
-//     code vector leaves as one coalesced 32-lane store.
+//   * A pool is owned by one wave.  Lane 16q + c takes slots 4q..4q+3 and
+//     channels 8c..8c+7, so each slot row of keys or scores is one 128-bit
+//     load per lane (16 lanes x 16 B = the 256 B bf16 row) and a lane holds
+//     4 x 8 values of each.  A workgroup of four waves compresses four pools.
+//   * Each lane runs the two-pass softmax over its 4 slots x 8 channels in
+//     fp32 registers.  The per-channel max is all-reduced over the wave's four
+//     16-lane rows before the exponentials (no rescaling needed); the partial
+//     sums are reduce-scattered, so each lane finishes two channels.  Row
+//     exchanges are gfx950's permlane swaps (VALU, no LDS).
+//   * The epilogue rotates the two channels a lane holds: channel bit 0 in a
+//     register, bits 1-2 across rows, bits 3-6 across the 16 lanes of a row
+//     (DPP); the absmax is a wave reduction; each lane stores 2 codes, so the
+//     128-byte code vector leaves as one coalesced store.
+//   * Batches of more than 24,576 pools run two pools per wave instead
+//     (pool16_prefill_pair_kernel): 32 lanes per pool, a 16-lane row per 8
+//     slots, 8 x 8 values per lane, the rows exchanging max and sums by
+//     ds_swizzle.  One pool per wave halves the arithmetic a wave runs after
+//     its last row arrives (a shorter drain at the end of a launch) and needs
+//     73 instead of 120 VGPRs; two pools per wave keep more bytes in flight
+//     per SIMD (64 KB at four waves against 48 KB at six), which wins on
+//     large batches.
 //   * Slot rows are streamed with non-temporal loads, through buffer
 //     resources with 32-bit offsets when keys and scores each span less than
 //     4 GiB (64-bit global addresses otherwise); ape ([16,128] fp32) is
 //     staged once per workgroup in LDS (measured faster than per-lane reads
 //     of ape through the L1).
-//   * At most 128 VGPRs, so four waves per SIMD keep enough loads in flight.
-//   * Ring decode of short verify batches is latency-bound, not bandwidth-
-//     bound: there one request takes a whole wave (row q of the wave owns
-//     slots 4q..4q+3) so each lane's share of the dependent arithmetic is
-//     halved; rows exchange through gfx950's permlane swaps.
+//   * Ring decode uses the same whole-wave layout for one request per wave.
 // The path is HBM-bound (about 8.3 KB read per 132 B written); there is no
 // dense contraction, so no MFMA.
 #include "kvc_device.hpp"
@@ -38,10 +42,14 @@ namespace kvc {
 namespace {
 
 constexpr int kPool = 16;
-constexpr int kHalf = 8;                       // slots per 16-lane row
-constexpr int kPoolsPerBlock = 8;              // 32 lanes per pool
-constexpr int kBlock = kPoolsPerBlock * 32;    // 256 threads = 4 waves
+constexpr int kBlock = 256;                    // 4 waves per workgroup
+constexpr int kPoolsPerBlock = kBlock / 64;    // prefill, one pool per wave
+constexpr int kHalf = 8;                       // prefill, two pools per wave: slots per 16-lane row
+constexpr int kPairPoolsPerBlock = kBlock / 32;
 constexpr int kMinWavesPerEU = 4;              // caps VGPRs at 128
+// Ragged prefill batches of at most this many pools run one pool per wave;
+// larger ones two pools per wave (see launch_pool16_prefill).
+constexpr int64_t kWavePerPoolMaxPools = 24576;
 constexpr int64_t kPagedBytes = 132;           // page of one token: 128 codes + fp32 scale
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -142,8 +150,8 @@ __device__ __forceinline__ void pool_mean(const uint4 (&S)[kHalf], const uint4 (
   }
 }
 
-// Softmax-weighted mean of one pool, whole-wave layout (one pool per wave,
-// for latency-bound calls).  Lane 16q + c holds the gate scores S[i] and keys
+// Softmax-weighted mean of one pool, whole-wave layout (one pool per wave).
+// Lane 16q + c holds the gate scores S[i] and keys
 // K[i] of slot 4q + i, channels 8c..8c+7.  Returns x[t] = the mean of channel
 // 8c + 2q + t, t = 0..1: the max is all-reduced over the four rows, the sums
 // are reduce-scattered (first across the wave halves, then across row pairs),
@@ -221,6 +229,8 @@ struct OutSink {
   int64_t rows;        // rows / pages available
   bool paged;
   float* dbg;          // ring decode: fp32 [rows, 128] pre-rounding means, or null
+  // 32-lane layout: lane 16h + c of a pool stores the codes of channels
+  // 8c + 4h .. 8c + 4h + 3; its lane 0 also stores the scale.
   __device__ __forceinline__ void store(int64_t row, int c, int h, uint32_t code4,
                                         float scale) const {
     if (paged) {
@@ -240,8 +250,8 @@ struct OutSink {
     if (dbg) o.dbg += rows_by * 128;
     return o;
   }
-  // Whole-wave layout: lane 16q + c stores the codes of channels 8c + 2q and
-  // 8c + 2q + 1 (low 16 bits of code2).
+  // Lane 16q + c of a wave stores the codes of channels 8c + 2q and
+  // 8c + 2q + 1 (low 16 bits of code2); lane 0 also stores the scale.
   __device__ __forceinline__ void store2(int64_t row, int c, int q, uint32_t code2,
                                          float scale) const {
     uint8_t* base = codes + row * (paged ? kPagedBytes : 128);
@@ -253,11 +263,12 @@ struct OutSink {
   }
 };
 
-// kBuf: keys and scores each span less than 4 GiB (key_bytes / score_bytes
-// from their base), so the row loads go through buffer resources with 32-bit
-// offsets; otherwise through 64-bit global addresses.
+// Two pools per wave (32-lane layout), for large batches: a pool's two
+// 16-lane rows take slots 8h..8h+7, lane c channels 8c..8c+7.  Twice the
+// bytes in flight per wave of the one-pool-per-wave kernel, at 120 VGPRs.
+// kBuf as for pool16_prefill_kernel.
 template <bool kRoundScale, bool kDbg, bool kBuf>
-__global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
+__global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_pair_kernel(
     const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
     int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
     const int32_t* __restrict__ src_rows, int64_t n_pools, OutSink sink,
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   __shared__ float4 s_ape[kPool * 32];
   const int c = threadIdx.x & 15;
   const int h = (threadIdx.x >> 4) & 1;
-  const int64_t pool = (int64_t)blockIdx.x * kPoolsPerBlock + (threadIdx.x >> 5);
+  const int64_t pool = (int64_t)blockIdx.x * kPairPoolsPerBlock + (threadIdx.x >> 5);
   int64_t r0 = -1, dst = pool;
   bool ok = pool < n_pools;
   // The wave's two plan entries (pools 2v and 2v+1 of the workgroup) are read
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   int32_t e0 = 0, e1 = 0;
   if (src_rows) {
     const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int64_t p0 = (int64_t)blockIdx.x * kPoolsPerBlock + 2 * v;
+    const int64_t p0 = (int64_t)blockIdx.x * kPairPoolsPerBlock + 2 * v;
     if (p0 < n_pools) e0 = src_rows[p0];
     if (p0 + 1 < n_pools) e1 = src_rows[p0 + 1];
   }
@@ -327,6 +338,78 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   float scale;
   const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
   sink.store(dst, c, h, codes, scale);
+}
+
+// One pool per wave.
+// kBuf: keys and scores each span less than 4 GiB (key_bytes / score_bytes
+// from their base), so the row loads go through buffer resources with 32-bit
+// offsets; otherwise through 64-bit global addresses.
+template <bool kRoundScale, bool kDbg, bool kBuf>
+__global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
+    const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
+    int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
+    const int32_t* __restrict__ src_rows, int64_t n_pools, OutSink sink,
+    const int64_t* __restrict__ loc, const uint8_t* __restrict__ write_mask,
+    float* __restrict__ dbg, uint32_t key_bytes, uint32_t score_bytes) {
+  __shared__ float4 s_ape[kPool * 32];
+  const int c = threadIdx.x & 15;
+  const int q = (threadIdx.x >> 4) & 3;
+  // The pool index is wave-uniform, so its plan entry (and, when paged, its
+  // destination and mask byte) comes through scalar loads, which return
+  // before the vector path would: the row loads wait on them.
+  const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t pool = (int64_t)blockIdx.x * kPoolsPerBlock + v;
+  int64_t r0 = -1, dst = pool;
+  bool ok = pool < n_pools;
+  if (ok) {
+    r0 = src_rows ? (int64_t)src_rows[pool] : pool * kPool;
+    if (loc) dst = loc[pool];
+    if (write_mask && !write_mask[pool]) ok = false;
+  }
+  ok = ok && r0 >= 0 && r0 + kPool <= num_rows && dst >= 0 && dst < sink.rows;
+
+  // ape is requested first; the row loads are unconditional (a skipped pool
+  // reads rows 0..15, which exist: the launcher only runs with num_rows >=
+  // 16), so no branch forces the compiler to wait on them early.
+  const ApeRegs ape_regs = load_ape(ape);
+  uint4 S[4], K[4];
+  {
+    const int64_t row = (ok ? r0 : 0) + 4 * q;
+    if constexpr (kBuf) {
+      const BufRsrc rs = make_rsrc(scores, score_bytes), rk = make_rsrc(keys, key_bytes);
+      const uint32_t so = (uint32_t)(row * score_stride * 2) + 16u * c;
+      const uint32_t ko = (uint32_t)(row * key_stride * 2) + 16u * c;
+      const uint32_t ss = (uint32_t)(score_stride * 2), ks = (uint32_t)(key_stride * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[i] = load_stream(rs, so + i * ss);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) K[i] = load_stream(rk, ko + i * ks);
+    } else {
+      const uint4* sp = reinterpret_cast<const uint4*>(scores + row * score_stride) + c;
+      const uint4* kp = reinterpret_cast<const uint4*>(keys + row * key_stride) + c;
+      const int64_t ss = score_stride >> 3, ks = key_stride >> 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[i] = load_stream(sp + i * ss);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) K[i] = load_stream(kp + i * ks);
+    }
+  }
+  store_ape(s_ape, ape_regs);
+  if (!ok) return;   // uniform over the wave: the row exchanges below stay complete
+
+  float4 A[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    A[i][0] = s_ape[(4 * q + i) * 32 + 2 * c];
+    A[i][1] = s_ape[(4 * q + i) * 32 + 2 * c + 1];
+  }
+  float x[2];
+  pool_mean_wave(S, K, A, x);
+  if constexpr (kDbg)   // channels 8c + 2q + t
+    reinterpret_cast<float2*>(dbg + pool * 128)[4 * c + q] = make_float2(x[0], x[1]);
+  float scale;
+  const uint32_t codes = rotate_quantise64(x, c, q, kRoundScale, scale);
+  sink.store2(dst, c, q, codes, scale);
 }
 
 // Per-layer strides of a multi-layer ring decode (blockIdx.y = layer): ring,
@@ -625,7 +708,15 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
                                  const int64_t* loc, const uint8_t* write_mask, bool round_scale,
                                  float* dbg, hipStream_t stream) {
   if (num_rows < kPool || n_pools <= 0) return hipSuccess;   // no pool can be complete
-  const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
+  // One pool per wave halves the arithmetic a wave runs after its rows
+  // arrive, which shortens the launch's drain; two pools per wave keep more
+  // bytes in flight per SIMD (64 KB at four waves against 48 KB at six),
+  // which wins once the drain is a small share.  Measured on the ragged
+  // workload: one per wave 2-4% faster at 7k-23k pools, two per wave 1-3%
+  // faster at 31k-62k pools.
+  const bool pair = n_pools > kWavePerPoolMaxPools;
+  const int64_t per_block = pair ? kPairPoolsPerBlock : kPoolsPerBlock;
+  const dim3 grid((unsigned)((n_pools + per_block - 1) / per_block));
   const dim3 block(kBlock);
   const OutSink sink{out_fp8, out_scale, out_rows, paged, nullptr};
   // Bytes from each base to the end of its last row: buffer loads when both
@@ -635,9 +726,16 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
   const bool buf = key_bytes < (1LL << 32) && score_bytes < (1LL << 32);
   const uint32_t kb = buf ? (uint32_t)key_bytes : 0u, sb = buf ? (uint32_t)score_bytes : 0u;
 #define KVC_LAUNCH(RS, DBG, BUF)                                                              \
-  hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF>), grid, block, 0, stream, keys,     \
-                     key_stride, scores, score_stride, num_rows, ape, src_rows, n_pools,     \
-                     sink, loc, write_mask, dbg, kb, sb)
+  do {                                                                                        \
+    if (pair)                                                                                 \
+      hipLaunchKernelGGL((pool16_prefill_pair_kernel<RS, DBG, BUF>), grid, block, 0, stream,  \
+                         keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
+                         n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
+    else                                                                                      \
+      hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF>), grid, block, 0, stream, keys, \
+                         key_stride, scores, score_stride, num_rows, ape, src_rows, n_pools,  \
+                         sink, loc, write_mask, dbg, kb, sb);                                 \
+  } while (0)
   if (buf) {
     if (round_scale) {
       if (dbg) KVC_LAUNCH(true, true, true); else KVC_LAUNCH(true, false, true);

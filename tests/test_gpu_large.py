@@ -32,7 +32,8 @@ def _release_memory():
     torch.cuda.empty_cache()
 
 
-def test_pool16_prefill_rows_past_4gib():
+@pytest.mark.parametrize("reps", [1, 4100])   # 6 pools: one per wave; 24,600: two per wave
+def test_pool16_prefill_rows_past_4gib(reps):
     stride = 1 << 16                                  # elements per row: 128 KiB rows
     R = FOUR_GIB // (2 * stride) + 256                # 33,024 rows, 4.33 GB
     src = np.array([0, 16, R - 96, R - 64, R - 33, R - 16], np.int64)
@@ -48,14 +49,23 @@ def test_pool16_prefill_rows_past_4gib():
     for p, r0 in enumerate(src):
         buf[r0:r0 + 16, :128] = k_rows[16 * p:16 * p + 16]
         buf[r0:r0 + 16, 128:256] = s_rows[16 * p:16 * p + 16]
-    out = torch.full((n, 128), 0x7F, dtype=torch.uint8, device="cuda")
-    scale = torch.full((n,), float("nan"), device="cuda")
-    dbg = torch.full((n, 128), float("nan"), device="cuda")
-    kvc.kvc_compress_prefill(buf[:, :128], buf[:, 128:256], dev(ape), dev(src.astype(np.int32)),
-                             n, out, scale, True, dbg)
+    # every pool of the launch reads one of the six row groups
+    srcs = np.tile(src, reps)
+    m = srcs.size
+    out = torch.full((m, 128), 0x7F, dtype=torch.uint8, device="cuda")
+    scale = torch.full((m,), float("nan"), device="cuda")
+    dbg = torch.full((m, 128), float("nan"), device="cuda")
+    kvc.kvc_compress_prefill(buf[:, :128], buf[:, 128:256], dev(ape), dev(srcs.astype(np.int32)),
+                             m, out, scale, True, dbg)
     torch.cuda.synchronize()
     gc, gs, gx = out.cpu().numpy(), scale.cpu().numpy(), dbg.cpu().numpy()
     del buf
+    # repeats of a row group give the same bits; the six distinct pools are
+    # then held to the oracle
+    for a in (gc, gs, gx):
+        rep = a.reshape(reps, n, -1)
+        assert np.array_equal(rep.view(np.uint8), np.broadcast_to(rep[:1], rep.shape).view(np.uint8))
+    gc, gs, gx = gc[:n], gs[:n], gx[:n]
     rc, rs, rx = oracle.compress_prefill(kb, sb, ape, None, True)
     assert rel_err_rows(gx, rx).max() <= VEC_TOL
     ref_c, ref_s, _ = reference_for(gx, rx, rc, rs, True, "pool16 prefill past 4 GiB")
