@@ -738,6 +738,7 @@ def main():
         g3 = gbs(c3["alg_bytes"], c3["ev_ms"])
         line["ring_decode"] = {
             "workload": "pool16_ring_decode_256x4", "completions_per_call": c3["completions"],
+            "completions_per_s": round(c3["completions"] * c3["steps"] / (c3["total_ms"] * 1e-3), 1),
             "tokens_per_s": round(c3["requests"] * c3["next_n"] * c3["steps"] / (c3["total_ms"] * 1e-3), 1),
             "launch_us": round(c3["ev_ms"] * 1e3, 3), "bytes_per_launch": c3["alg_bytes"],
             "hbm_gbs": round(g3, 1), "hbm_frac": round(g3 / PEAK_HBM_GBS, 4)}
