@@ -719,12 +719,23 @@ def test_paged_ring_decode_matches_packed():
     assert np.array_equal(cache.cpu().numpy(), exp)
 
 
-@pytest.mark.parametrize("next_n", [4, 9])
-def test_ring_decode_layers_equal_separate_calls(next_n):
+@pytest.mark.parametrize("next_n,irregular", [(4, False), (6, False), (9, False), (4, True),
+                                               (8, True)])
+def test_ring_decode_layers_equal_separate_calls(next_n, irregular):
     """One launch over 5 layers (own ring, keys, scores and ape per layer,
-    shared maps) equals 5 single-layer calls, each checked against the oracle."""
+    shared maps) equals 5 single-layer calls, each checked against the oracle.
+    Covers the 4-, 8- and 16-token instances; the irregular cases close
+    several pools per verify batch (a wave's later completions reuse the ape
+    table it already holds in LDS)."""
     L, R = 5, 37
-    base = synth.pool16_ring(seed=40 + next_n, num_requests=R, next_n=next_n, pad_frac=0.1)
+    if irregular:
+        R = 120
+        base = irregular_ring_case(140 + next_n, R, next_n)
+        closing = (base["positions"] % 16 == 15) & (base["slot_mapping"] >= 0)
+        assert (closing.sum(axis=1) >= 2).any()
+    else:
+        base = synth.pool16_ring(seed=40 + next_n, num_requests=R, next_n=next_n, pad_frac=0.1)
+    rs_mode = bool(base["round_scale"])
     pad = base["positions"] < 0
     g = np.random.default_rng(41)
     layers = []
@@ -744,7 +755,7 @@ def test_ring_decode_layers_equal_separate_calls(next_n):
         gring, gc, gsc, ring, ref_c, ref_s = run_ring(d)
         assert np.array_equal(gring, ring)
         check_codes(gc, ref_c, f"ring layer {l} codes")
-        check_scales(gsc, ref_s, True, f"ring layer {l} scales")
+        check_scales(gsc, ref_s, rs_mode, f"ring layer {l} scales")
         singles.append((gring, gc, gsc))
     n_out = base["num_out"]
     mring = dev(np.stack([d["ring"] for d in layers]), torch.int16)
@@ -755,7 +766,7 @@ def test_ring_decode_layers_equal_separate_calls(next_n):
     ms = torch.full((L, n_out), 5.0, device="cuda")
     kvc.kvc_compress_decode_ring_layers(mring, dev(base["tail_slot_mapping"]), mkey, mscore, mape,
                                         dev(base["slot_mapping"]), dev(base["positions"]), mo, ms,
-                                        True)
+                                        rs_mode)
     torch.cuda.synchronize()
     mring, mo, ms = mring.cpu().numpy().view(np.uint16), mo.cpu().numpy(), ms.cpu().numpy()
     for l, (gring, gc, gsc) in enumerate(singles):
