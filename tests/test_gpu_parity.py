@@ -719,25 +719,14 @@ def test_paged_ring_decode_matches_packed():
     assert np.array_equal(cache.cpu().numpy(), exp)
 
 
-@pytest.mark.parametrize("next_n,irregular", [(4, False), (6, False), (9, False), (4, True),
-                                               (8, True)])
-def test_ring_decode_layers_equal_separate_calls(next_n, irregular):
-    """One launch over 5 layers (own ring, keys, scores and ape per layer,
-    shared maps) equals 5 single-layer calls, each checked against the oracle.
-    Covers the 4-, 8- and 16-token instances; the irregular cases close
-    several pools per verify batch (a wave's later completions reuse the ape
-    table it already holds in LDS)."""
-    L, R = 5, 37
-    if irregular:
-        R = 120
-        base = irregular_ring_case(140 + next_n, R, next_n)
-        closing = (base["positions"] % 16 == 15) & (base["slot_mapping"] >= 0)
-        assert (closing.sum(axis=1) >= 2).any()
-    else:
-        base = synth.pool16_ring(seed=40 + next_n, num_requests=R, next_n=next_n, pad_frac=0.1)
+def check_ring_layers(base, L, seed):
+    """One launch over L layers (own ring, keys, scores and ape per layer,
+    shared maps) equals L single-layer calls, each checked against the
+    oracle.  Layer 0 uses base's rows; the others draw their own."""
+    R = base["key"].shape[0]
     rs_mode = bool(base["round_scale"])
     pad = base["positions"] < 0
-    g = np.random.default_rng(41)
+    g = np.random.default_rng(seed)
     layers = []
     for l in range(L):
         d = dict(base)
@@ -749,7 +738,7 @@ def test_ring_decode_layers_equal_separate_calls(next_n, irregular):
             d["score"][pad] = synth.BF16_NAN
             d["ape"] = synth.ape_pool16(g)
         layers.append(d)
-    note(f"ring decode layers {L}x{R}x{next_n}")
+    note(f"ring decode layers {L}x{R}x{base['key'].shape[1]}")
     singles = []
     for l, d in enumerate(layers):
         gring, gc, gsc, ring, ref_c, ref_s = run_ring(d)
@@ -773,6 +762,21 @@ def test_ring_decode_layers_equal_separate_calls(next_n, irregular):
         assert np.array_equal(mring[l], gring), f"layer {l}: ring differs"
         assert np.array_equal(mo[l], gc), f"layer {l}: codes differ"
         assert np.array_equal(ms[l].view(np.uint32), gsc.view(np.uint32)), f"layer {l}: scales"
+
+
+@pytest.mark.parametrize("next_n,irregular", [(4, False), (6, False), (9, False), (4, True),
+                                               (8, True)])
+def test_ring_decode_layers_equal_separate_calls(next_n, irregular):
+    """Covers the 4-, 8- and 16-token instances; the irregular cases close
+    several pools per verify batch (a wave's later completions reuse the ape
+    table it already holds in LDS)."""
+    if irregular:
+        base = irregular_ring_case(140 + next_n, 120, next_n)
+        closing = (base["positions"] % 16 == 15) & (base["slot_mapping"] >= 0)
+        assert (closing.sum(axis=1) >= 2).any()
+    else:
+        base = synth.pool16_ring(seed=40 + next_n, num_requests=37, next_n=next_n, pad_frac=0.1)
+    check_ring_layers(base, 5, 41)
 
 
 # ------------------------------------------------------------------ c128 layers / quantised epilogue

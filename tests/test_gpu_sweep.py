@@ -2,6 +2,8 @@
 the oracle to the same bar as the fixed-case parity tests.  The shapes cross
 the kernels' internal boundaries (pools per workgroup, requests per wave,
 verify-batch kernel choice, chunk edges, segments per request) at random."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -10,13 +12,15 @@ import oracle
 import kv_cache_compression_pool_amd as kvc
 from kv_cache_compression_pool_amd import synth
 from tests.helpers import c128_decode_case, c128_prefill_case, rel_err_rows
-from tests.test_gpu_parity import (VEC_TOL, check_codes, check_scales, compare_c128_prefill,
-                                   compare_c128_prefill_fused, compare_prefill, compare_state,
-                                   dev, note, run_ring)
+from tests.test_gpu_parity import (VEC_TOL, check_codes, check_ring_layers, check_scales,
+                                   compare_c128_prefill, compare_c128_prefill_fused,
+                                   compare_prefill, compare_state, dev, irregular_ring_case, note,
+                                   run_ring)
 
 pytestmark = pytest.mark.gpu
 
-CASES = 12
+# More cases on demand: KVC_SWEEP_CASES=N
+CASES = int(os.environ.get("KVC_SWEEP_CASES", "12"))
 
 
 @pytest.mark.parametrize("case", range(CASES))
@@ -46,6 +50,22 @@ def test_sweep_ring_decode(case):
     assert np.array_equal(gring, ring)
     check_codes(gc, rc, "sweep ring codes")
     check_scales(gs, rs, d["round_scale"], "sweep ring scales")
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_sweep_ring_decode_layers(case):
+    """Multi-layer launches (the instances that park token rows and stage
+    ape in LDS) against single-layer calls and the oracle."""
+    g = np.random.default_rng(9000 + case)
+    next_n = int(g.integers(1, 9))
+    R = int(g.integers(1, 90))
+    if case % 2:
+        base = irregular_ring_case(9500 + case, R, next_n)
+    else:
+        base = synth.pool16_ring(seed=9600 + case, num_requests=R, next_n=next_n,
+                                 pad_frac=float(g.uniform(0, 0.3)))
+        base["round_scale"] = bool(case % 4 == 0)
+    check_ring_layers(base, int(g.integers(2, 7)), 9700 + case)
 
 
 @pytest.mark.parametrize("case", range(CASES))
