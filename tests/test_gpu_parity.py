@@ -463,6 +463,65 @@ def test_c128_prefill_full_size_c5():
     compare_c128_prefill(c128_prefill_case(seed=0), "c128 prefill 32 seqs")
 
 
+def test_c128_prefill_then_decode_equals_one_prefill():
+    """A request prefilled up to some length and then decoded token by token
+    ends where one prefill over all its tokens ends: every closed chunk's
+    vector (from the prefill or from the decode step that closes it) and the
+    open chunk's state agree (max bit-exact, sum and kv within tolerance)."""
+    g = np.random.default_rng(31)
+    T = np.array([1, 127, 128, 129, 300, 256, 385, 200], np.int64)     # total tokens
+    P = np.array([1, 1, 100, 129, 130, 1, 256, 200], np.int64)         # prefilled part
+    B, S = T.size, 16
+    D = T - P                                                           # decoded one by one
+    idx = g.permutation(S)[:B].astype(np.int32)
+    x = [g.standard_normal((int(t), 256)).astype(np.float32) for t in T]
+    ape = dev((g.standard_normal((128, 128)) * 0.1).astype(np.float32))
+    note(f"c128 prefill then decode: totals {T.tolist()}, prefilled {P.tolist()}")
+
+    def prefill(lens):
+        st = torch.full((S, 384), float("nan"), device="cuda")
+        n = int(lens.sum())
+        xin = dev(np.concatenate([x[b][:int(lens[b])] for b in range(B)]))
+        out = torch.full((n, 128), float("nan"), device="cuda")
+        cp, wp = kvc.kvc_c128_plan_prefill(lens, lens, n)
+        kvc.kvc_c128_online_prefill(st, xin, out, ape, dev(idx), kvc.plans_to_device(cp), cp.size,
+                                    kvc.plans_to_device(wp), wp.size)
+        return st, out
+
+    # path A: prefill P, then decode the rest in steps
+    stA, outA = prefill(P)
+    emitted = {}
+    for k in range(int(D.max())):
+        act = np.nonzero(D > k)[0]
+        xin = dev(np.stack([x[b][int(P[b]) + k] for b in act]))
+        out = torch.full((act.size, 128), float("nan"), device="cuda")
+        kvc.kvc_c128_online_decode(stA, xin, out, ape, dev(idx[act]),
+                                   dev((P[act] + k + 1).astype(np.int32)))
+        out = out.cpu().numpy()
+        for j, b in enumerate(act):
+            if (int(P[b]) + k) % 128 == 127:
+                emitted[(b, int(P[b]) + k)] = out[j]
+            else:
+                assert np.isnan(out[j]).all()
+    # path B: one prefill over every token
+    stB, outB = prefill(T)
+    torch.cuda.synchronize()
+    outA, outB = outA.cpu().numpy(), outB.cpu().numpy()
+    offA = np.concatenate([[0], np.cumsum(P)[:-1]])
+    offB = np.concatenate([[0], np.cumsum(T)[:-1]])
+    n_chunks = 0
+    for b in range(B):
+        for p in range(127, int(T[b]), 128):
+            ref = outB[offB[b] + p]
+            got = outA[offA[b] + p] if p < P[b] else emitted[(b, p)]
+            assert rel_err_rows(got[None], ref[None]).max() <= VEC_TOL, f"request {b} chunk {p}"
+            n_chunks += 1
+    assert n_chunks == int((T // 128).sum())
+    open_rows = idx[T % 128 != 0]
+    compare_state(stA.cpu().numpy()[open_rows], stB.cpu().numpy()[open_rows],
+                  "c128 prefill + decode vs one prefill")
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_c128_prefill_small_and_padded_plans(seed):
     d = c128_prefill_case(seed=seed, batch=5, max_prior=700, max_extend=900)
