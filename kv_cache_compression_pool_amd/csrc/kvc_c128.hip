@@ -117,11 +117,19 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
   float4 kv, sc;
   const float4* row = reinterpret_cast<const float4*>(in + layer * in_ls + b * 256);
   if constexpr (kScalarSlots) {
-    int32_t i0 = -1, i1 = -1, l0 = 0, l1 = 0;
+    // The wave's two slots and lengths at clamped indices (no branch), then
+    // every other kernel argument into SGPRs: two scalar waits before the
+    // vector loads instead of four (64 layers 44.32-44.40 -> 44.11-44.22 us).
+    // The asm statement comes after the slot loads, which keeps them scalar.
     const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t b0 = (int64_t)blockIdx.x * kReq + 2 * v;
-    if (b0 < batch) { i0 = indices[b0]; l0 = seq_lens[b0]; }
-    if (b0 + 1 < batch) { i1 = indices[b0 + 1]; l1 = seq_lens[b0 + 1]; }
+    const int64_t c0 = b0 < batch ? b0 : batch - 1, c1 = b0 + 1 < batch ? b0 + 1 : batch - 1;
+    int32_t i0 = indices[c0], l0 = seq_lens[c0], i1 = indices[c1], l1 = seq_lens[c1];
+    asm volatile("" ::"s"(state), "s"(state_ls), "s"(num_slots), "s"(in), "s"(in_ls), "s"(ape),
+                 "s"(ape_ls), "s"(o.out), "s"(o.codes), "s"(o.scales), "s"(i0), "s"(l0), "s"(i1),
+                 "s"(l1));
+    if (b0 >= batch) { i0 = -1; l0 = 0; }
+    if (b0 + 1 >= batch) { i1 = -1; l1 = 0; }
     if (b >= batch) return;
     idx = (threadIdx.x & 32) ? i1 : i0;
     L = (threadIdx.x & 32) ? l1 : l0;
@@ -436,6 +444,7 @@ hipError_t launch_c128_decode(float* state, int64_t state_ls, int64_t num_slots,
                               float* scales, bool round_scale, const float* ape, int64_t ape_ls,
                               const int32_t* indices, const int32_t* seq_lens, int64_t batch,
                               int64_t num_layers, hipStream_t stream) {
+  if (batch <= 0 || num_layers <= 0) return hipSuccess;   // kernels clamp indices to batch - 1
   const EmitSink o{out, codes, scales, out_ls, batch * 128, batch, round_scale};
 #define KVC_DECODE(QUANT, REQ)                                                                 \
   hipLaunchKernelGGL((c128_decode_kernel<QUANT, REQ>),                                         \
