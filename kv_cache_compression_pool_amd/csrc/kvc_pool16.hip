@@ -405,9 +405,11 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_pair_ke
 // kBuf: keys and scores each span less than 4 GiB (key_bytes / score_bytes
 // from their base), so the row loads go through buffer resources with 32-bit
 // offsets; otherwise through 64-bit global addresses.
-// kPacked: a plan is given and the output is packed (no loc, no write mask),
-// the common case, which then runs without branches before its row loads.
-template <bool kRoundScale, bool kDbg, bool kBuf, bool kPacked>
+// kPlan: 1 = a plan and packed output (no loc, no write mask), the common
+// case; 2 = a plan and paged output (loc given, write mask optional); both
+// then load their plan entry (and loc) without branches before the row loads.
+// 0 = anything else.
+template <bool kRoundScale, bool kDbg, bool kBuf, int kPlan>
 __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
     const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
     int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
@@ -424,18 +426,28 @@ __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
   const int64_t pool = (int64_t)blockIdx.x * kPoolsPerBlock + v;
   int64_t r0 = -1, dst = pool;
   bool ok = pool < n_pools;
-  if constexpr (kPacked) {
-    // Plan entry first (index clamped, so no branch), then every kernel
-    // argument into SGPRs: one wait for the arguments and one for the plan
-    // before the row loads, instead of four behind the null-pointer checks
-    // (21.0-21.3 -> 20.7-20.8 us on the 64-sequence batch).  The asm
-    // statement comes after the plan load, which keeps that load scalar.
+  if constexpr (kPlan != 0) {
+    // Plan entry (and loc) first, index clamped so no branch, then every
+    // kernel argument into SGPRs: one wait for the arguments and one for the
+    // plan before the row loads, instead of four behind the null-pointer
+    // checks (packed: 21.0-21.3 -> 20.7-20.8 us on the 64-sequence batch;
+    // paged: 21.3-21.6 -> 21.2-21.3 us).  The asm statement comes after those
+    // loads, which keeps them scalar; the optional mask byte is read after
+    // it, through a vector load.
     const int64_t pc = ok ? pool : n_pools - 1;
     const int32_t e = src_rows[pc];
+    int64_t dl = pool;
+    if constexpr (kPlan == 2) dl = loc[pc];
     asm volatile("" ::"s"(keys), "s"(key_stride), "s"(scores), "s"(score_stride), "s"(num_rows),
                  "s"(ape), "s"(n_pools), "s"(sink.codes), "s"(sink.scales), "s"(sink.rows),
-                 "s"(dbg), "s"(key_bytes), "s"(score_bytes), "s"(e));
-    if (ok) r0 = e;
+                 "s"(dbg), "s"(key_bytes), "s"(score_bytes), "s"(e), "s"(dl));
+    if (ok) {
+      r0 = e;
+      dst = dl;
+      if constexpr (kPlan == 2) {
+        if (write_mask && !write_mask[pool]) ok = false;
+      }
+    }
   } else if (ok) {
     r0 = src_rows ? (int64_t)src_rows[pool] : pool * kPool;
     if (loc) dst = loc[pool];
@@ -799,7 +811,8 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
   // workload: one per wave 2-4% faster at 7k-23k pools, two per wave 1-3%
   // faster at 31k-62k pools.
   const bool pair = n_pools > kWavePerPoolMaxPools;
-  const bool packed = src_rows && !loc && !write_mask;   // n_pools >= 1 here
+  // n_pools >= 1 here, so the kernels' clamped plan index is valid
+  const int plan_mode = !src_rows ? 0 : (!loc && !write_mask) ? 1 : loc ? 2 : 0;
   const int64_t per_block = pair ? kPairPoolsPerBlock : kPoolsPerBlock;
   const dim3 grid((unsigned)((n_pools + per_block - 1) / per_block));
   const dim3 block(kBlock);
@@ -816,12 +829,16 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
       hipLaunchKernelGGL((pool16_prefill_pair_kernel<RS, DBG, BUF>), grid, block, 0, stream,  \
                          keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
                          n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
-    else if (packed)                                                                          \
-      hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, true>), grid, block, 0, stream, \
+    else if (plan_mode == 1)                                                                  \
+      hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, 1>), grid, block, 0, stream,    \
+                         keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
+                         n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
+    else if (plan_mode == 2)                                                                  \
+      hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, 2>), grid, block, 0, stream,    \
                          keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
                          n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
     else                                                                                      \
-      hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, false>), grid, block, 0, stream, \
+      hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, 0>), grid, block, 0, stream,    \
                          keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
                          n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
   } while (0)
