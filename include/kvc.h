@@ -350,8 +350,13 @@ int kvc_c128_online_decode_quant(float* state, int64_t num_slots, const float* k
  *      and written to out row ragged_id.  The state buffer is only read.
  *   2. every write plan: the same, but the (max, sum, kv) state is written to
  *      row indices[b].
- * Because pass 1 finishes before pass 2 starts, every read sees the state as
- * it was when the call was made.
+ * Because pass 1 finishes before pass 2 starts, every read of pass 1 sees
+ * the state as it was when the call was made.  In pass 2 a write plan that
+ * starts mid-chunk reads row load_indices[b] while other workgroups of the
+ * same launch write rows indices[b'], so the call requires that no request
+ * reads a state row another request of the call writes: the rows indices[b]
+ * are distinct, and load_indices[b] is no other request's indices[b'] (true
+ * when load_indices is NULL).  Otherwise the result is undefined.
  *   state          device fp32 [num_slots, 384]
  *   kv_score_in    device fp32 [num_tokens, 256]
  *   out            device fp32 [num_tokens, 128]; only chunk-closing rows
@@ -372,8 +377,8 @@ int kvc_c128_online_prefill(float* state, int64_t num_slots, const float* kv_sco
 /* kvc_c128_online_prefill with the rotate/quantise epilogue (as in
  * kvc_c128_online_decode_quant) on every chunk-closing vector: out_fp8
  * device uint8 [num_tokens, 128] and out_scale device fp32 [num_tokens],
- * written at row ragged_id of each compress plan.  State handling is
- * identical to kvc_c128_online_prefill. */
+ * written at row ragged_id of each compress plan.  State handling, and the
+ * requirement on load_indices, are those of kvc_c128_online_prefill. */
 int kvc_c128_online_prefill_quant(float* state, int64_t num_slots, const float* kv_score_in,
                                   uint8_t* out_fp8, float* out_scale, int64_t num_tokens,
                                   const float* ape, const int32_t* indices,
@@ -422,14 +427,25 @@ int kvc_c128_online_prefill_fused(float* state, int64_t num_slots, const float* 
 int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
                      void* stream);
 
-/* Streaming-read reference: reads `bytes` bytes at src (16-byte aligned,
- * bytes a multiple of 16) with 128-bit non-temporal loads from 1024
- * workgroups of 256 threads and writes one XOR word per thread to
- * sink[0 .. 262143] (sink_words must be >= 262144).  It does no other work,
- * so its time over a buffer is the practical HBM read rate the compression
- * kernels are compared with. */
+/* Plain streaming read, for measurement: reads `bytes` bytes at src
+ * (16-byte aligned, bytes a multiple of 16) with 128-bit non-temporal loads,
+ * one shot.  Workgroup w (256 threads) reads bytes [w*4096*L, (w+1)*4096*L),
+ * L = loads_per_lane (4, 8 or 16), every lane issuing its L loads before it
+ * uses any, and writes the XOR of all 32-bit words it read to sink[w]
+ * (sink_words >= ceil(bytes / (4096*L)); zero padding past `bytes`).  It
+ * does no other work: its time over a buffer is what a read-only kernel of
+ * this simple shape reaches, a reference for the compression kernels rather
+ * than a bound on them.
+ * Errors: KVC_ERR_SHAPE (size, alignment, sink too small),
+ *         KVC_ERR_UNSUPPORTED (loads_per_lane), KVC_ERR_NULL, KVC_ERR_HIP. */
 int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
-                         void* stream);
+                         int loads_per_lane, void* stream);
+
+/* Launches a kernel that does nothing, with `workgroups` workgroups of
+ * `threads` threads (1..1024), for measuring the launch and dispatch floor
+ * that a kernel of that grid pays.  workgroups == 0 is a no-op.
+ * Errors: KVC_ERR_SHAPE, KVC_ERR_HIP. */
+int kvc_diag_empty_launch(int64_t workgroups, int threads, void* stream);
 
 #ifdef __cplusplus
 }

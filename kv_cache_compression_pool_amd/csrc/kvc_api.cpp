@@ -648,15 +648,32 @@ int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int6
 }
 
 int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
-                         void* stream) {
-  if (bytes < 0 || bytes % 16) return fail(KVC_ERR_SHAPE, "kvc_diag_stream_read: bytes must be a multiple of 16");
+                         int loads_per_lane, void* stream) {
+  const char* fn = "kvc_diag_stream_read";
+  if (bytes < 0 || bytes % 16) return fail(KVC_ERR_SHAPE, "%s: bytes must be a multiple of 16", fn);
+  if (loads_per_lane != 4 && loads_per_lane != 8 && loads_per_lane != 16)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: loads_per_lane %d (4, 8 or 16)", fn, loads_per_lane);
   if (bytes == 0) return ok();
-  if (!src || !sink) return fail(KVC_ERR_NULL, "kvc_diag_stream_read: NULL pointer");
-  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(KVC_ERR_SHAPE, "kvc_diag_stream_read: misaligned pointer");
-  if (sink_words < (int64_t)kvc::kStreamBlocks * 256)
-    return fail(KVC_ERR_SHAPE, "kvc_diag_stream_read: sink needs %d words", kvc::kStreamBlocks * 256);
-  return hip_status(kvc::launch_diag_stream_read(src, bytes, sink, (hipStream_t)stream),
+  if (!src || !sink) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
+  const int64_t per_block = 4096LL * loads_per_lane;
+  const int64_t blocks = (bytes + per_block - 1) / per_block;
+  if (blocks > 0x7fffffffLL) return fail(KVC_ERR_SHAPE, "%s: buffer too large", fn);
+  if (sink_words < blocks)
+    return fail(KVC_ERR_SHAPE, "%s: sink needs %lld words", fn, (long long)blocks);
+  return hip_status(kvc::launch_diag_stream_read(src, bytes, sink, loads_per_lane,
+                                                 (hipStream_t)stream),
                     "kvc_diag_stream_read launch");
+}
+
+int kvc_diag_empty_launch(int64_t workgroups, int threads, void* stream) {
+  const char* fn = "kvc_diag_empty_launch";
+  if (workgroups < 0 || workgroups > 0x7fffffffLL)
+    return fail(KVC_ERR_SHAPE, "%s: workgroups out of range", fn);
+  if (threads < 1 || threads > 1024) return fail(KVC_ERR_SHAPE, "%s: threads must be 1..1024", fn);
+  if (workgroups == 0) return ok();
+  return hip_status(kvc::launch_diag_empty(workgroups, threads, (hipStream_t)stream),
+                    "kvc_diag_empty_launch launch");
 }
 
 }  // extern "C"

@@ -1,6 +1,7 @@
 // kvc_diag.hip -- verification and measurement helpers (not part of the
 // compression path): the device number-format conversions the kernels use,
-// exposed elementwise, and a plain streaming-read reference kernel.
+// exposed elementwise, a plain streaming-read kernel and an empty kernel
+// (launch floor).
 #include "kvc_device.hpp"
 #include "kvc_internal.hpp"
 
@@ -27,26 +28,37 @@ __global__ __launch_bounds__(256) void diag_convert_kernel(const float* __restri
   }
 }
 
-// Plain streaming read: 4 independent 128-bit loads in flight per lane,
-// grid-stride over the buffer.
+// Plain streaming read, one shot: workgroup w reads the 16-byte words
+// [w*256*L, (w+1)*256*L), load u of thread i taking word w*256*L + u*256 + i,
+// so each wave-wide load covers 1 KB of consecutive bytes and every lane
+// issues its L non-temporal loads before it uses any of them.  The words are
+// XOR-folded over the workgroup and the result is written to sink[w]; the
+// fold keeps the loads alive and lets a test check that every word was read.
+template <int L>
 __global__ __launch_bounds__(256) void diag_stream_read_kernel(const u32x4_t* __restrict__ p,
                                                                int64_t n16,
                                                                uint32_t* __restrict__ sink) {
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  uint32_t acc = 0;
-  for (int64_t base = tid; base < n16; base += 4 * stride) {
-    u32x4_t v[4];
+  const int64_t base = (int64_t)blockIdx.x * (256 * L) + threadIdx.x;
+  u32x4_t v[L];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = base + u * stride;
-      v[u] = i < n16 ? __builtin_nontemporal_load(p + i) : (u32x4_t){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  for (int u = 0; u < L; ++u) {
+    const int64_t i = base + u * 256;
+    v[u] = i < n16 ? __builtin_nontemporal_load(p + i) : (u32x4_t){0u, 0u, 0u, 0u};
   }
-  sink[tid] = acc;
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < L; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
+  __shared__ uint32_t s_fold[4];
+  if ((threadIdx.x & 63) == 0) s_fold[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = s_fold[0] ^ s_fold[1] ^ s_fold[2] ^ s_fold[3];
 }
+
+// A kernel that does nothing: its launch-to-launch time with a given grid is
+// the dispatch floor that any kernel of that grid pays.
+__global__ __launch_bounds__(1024) void diag_empty_kernel() {}
 
 }  // namespace
 
@@ -59,9 +71,27 @@ hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8
 }
 
 hipError_t launch_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink,
-                                   hipStream_t stream) {
-  hipLaunchKernelGGL(diag_stream_read_kernel, dim3(kStreamBlocks), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4_t*>(src), bytes / 16, sink);
+                                   int loads_per_lane, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  const int64_t per_block = 256LL * loads_per_lane;
+  const dim3 grid((unsigned)((n16 + per_block - 1) / per_block));
+  const u32x4_t* p = reinterpret_cast<const u32x4_t*>(src);
+  switch (loads_per_lane) {
+    case 4:
+      hipLaunchKernelGGL(diag_stream_read_kernel<4>, grid, dim3(256), 0, stream, p, n16, sink);
+      break;
+    case 8:
+      hipLaunchKernelGGL(diag_stream_read_kernel<8>, grid, dim3(256), 0, stream, p, n16, sink);
+      break;
+    default:
+      hipLaunchKernelGGL(diag_stream_read_kernel<16>, grid, dim3(256), 0, stream, p, n16, sink);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_diag_empty(int64_t workgroups, int threads, hipStream_t stream) {
+  hipLaunchKernelGGL(diag_empty_kernel, dim3((unsigned)workgroups), dim3(threads), 0, stream);
   return hipGetLastError();
 }
 

@@ -36,7 +36,8 @@ EXPORTS = ("kvc_version", "kvc_last_error", "kvc_plan_pool_prefill", "kvc_c128_p
            "kvc_c128_online_decode_quant", "kvc_c128_online_prefill",
            "kvc_c128_online_prefill_quant", "kvc_c128_plan_prefill_fused",
            "kvc_c128_fused_capacity",
-           "kvc_c128_online_prefill_fused", "kvc_diag_convert", "kvc_diag_stream_read")
+           "kvc_c128_online_prefill_fused", "kvc_diag_convert", "kvc_diag_stream_read",
+           "kvc_diag_empty_launch")
 
 
 class KvcError(RuntimeError):
@@ -92,7 +93,8 @@ def lib() -> ctypes.CDLL:
         L.kvc_c128_online_prefill_fused.argtypes = [_p, _i64, _p, _p, _p, _p, _i32, _i64, _p, _p,
                                                     _p, _i64, _p, _u32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
-        L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _p]
+        L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _i32, _p]
+        L.kvc_diag_empty_launch.argtypes = [_i64, _i32, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
         L.kvc_c128_fused_capacity.restype = _i64
@@ -572,18 +574,26 @@ def kvc_diag_convert(x, bf16_out=None, fp8_out=None, stream=None):
         _dptr(fp8_out, torch.uint8, "fp8_out", optional=True), x.numel(), _stream(stream)))
 
 
-STREAM_SINK_WORDS = 1024 * 256
+def stream_read_sink_words(nbytes: int, loads_per_lane: int) -> int:
+    """Sink words kvc_diag_stream_read needs: one per 256-thread workgroup."""
+    return -(-int(nbytes) // (4096 * int(loads_per_lane)))
 
 
-def kvc_diag_stream_read(src, sink, stream=None):
+def kvc_diag_stream_read(src, sink, loads_per_lane: int = 8, stream=None):
     """Plain streaming read of a device tensor's bytes (see kvc.h); sink is a
-    device int32/uint32 tensor of at least STREAM_SINK_WORDS entries."""
+    device int32/uint32 tensor of at least stream_read_sink_words() entries."""
     nbytes = src.numel() * src.element_size()
+    nbytes -= nbytes % 16
     _need(src.is_cuda and src.is_contiguous(), "src must be a contiguous device tensor")
-    _need(sink.is_cuda and sink.element_size() == 4 and sink.numel() >= STREAM_SINK_WORDS,
-          "sink must hold STREAM_SINK_WORDS 4-byte words")
-    _check(lib().kvc_diag_stream_read(src.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(),
-                                      sink.numel(), _stream(stream)))
+    _need(sink.is_cuda and sink.element_size() == 4 and sink.is_contiguous(),
+          "sink must be a contiguous device tensor of 4-byte words")
+    _check(lib().kvc_diag_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(),
+                                      int(loads_per_lane), _stream(stream)))
+
+
+def kvc_diag_empty_launch(workgroups: int, threads: int, stream=None):
+    """Launch an empty kernel of the given grid (launch-floor measurements)."""
+    _check(lib().kvc_diag_empty_launch(int(workgroups), int(threads), _stream(stream)))
 
 
 def plans_to_device(plan: np.ndarray, device="cuda"):

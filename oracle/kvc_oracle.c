@@ -549,8 +549,12 @@ static void c128_segment(const float* state, const float* in, const float* ape,
 
 /* Prefill: first every compress plan (reads state rows, writes only out rows
  * ragged_id), then every write plan (writes state rows indices[b]).  The
- * order makes every state read see the state as it was before the call.
- * load_indices NULL means indices.  All-ones plans are skipped. */
+ * order makes every compress-plan read see the state as it was before the
+ * call.  A write plan that starts mid-chunk reads row load_indices[b] as it
+ * stands when that plan runs here; that is also the state before the call
+ * whenever no request reads a row that another request of the call writes
+ * (the device entry points require this; with load_indices NULL = indices it
+ * always holds, the indices being distinct).  All-ones plans are skipped. */
 void orc_c128_prefill(float* state, int64_t num_slots, const float* in, float* out,
                       const float* ape, const int32_t* indices, const int32_t* load_indices,
                       const orc_plan* cplan, uint32_t n_c, const orc_plan* wplan, uint32_t n_w) {

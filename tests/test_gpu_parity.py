@@ -22,6 +22,8 @@ from tests.helpers import c128_decode_case, c128_prefill_case, e4m3_ordinal, rel
 pytestmark = pytest.mark.gpu
 
 VEC_TOL = 2e-3
+# Batches of at least this many codes are also held to the raw 0.1% bar.
+RAW_CHECK_MIN_CODES = 100_000
 
 
 def dev(a, dtype=None):
@@ -57,7 +59,20 @@ def check_scales(got, ref, round_scale, what):
             assert np.all(np.abs(got[bad] / ref[bad] - 1) <= 2.0**-7)
 
 
-def reference_for(gx, rx, rc, rs, round_scale, what):
+# Fp32 accumulation error allowed in a channel that rounds to a different
+# bf16 value than the oracle's, in fp32 ulps (2^-23) of the vector's max-abs
+# value.  A pool-16 mean sums 16 weighted terms (observed at most about 1.5
+# ulps); a pool-128 mean sums 128 through several partial merges (observed
+# at most about 1.5 ulps).
+FLIP_ULPS_POOL16 = 8
+FLIP_ULPS_POOL128 = 16
+# Pools whose bf16 rounding differs anywhere: at most this share of the batch
+# (observed 0.9% on the 64-sequence ragged batch), or FLIP_FLOOR pools.
+FLIP_FRAC = 0.02
+FLIP_FLOOR = 8
+
+
+def reference_for(gx, rx, rc, rs, round_scale, what, ulps=FLIP_ULPS_POOL16):
     """Reference codes / scales for the GPU output.
 
     Where the GPU's fp32 pooled vector rounds to the same bf16 vector as the
@@ -66,27 +81,42 @@ def reference_for(gx, rx, rc, rs, round_scale, what):
     rounding error of a bf16 rounding boundary, so both roundings are correct),
     the reference is the oracle's epilogue applied to the GPU's pooled vector;
     e4m3 resolves near-zero values far more finely than a one-bf16-ulp input
-    change, so those codes cannot be compared directly.  Such pools must stay
-    rare."""
+    change, so those codes cannot be compared directly.  Every such channel
+    must be within `ulps` fp32 ulps of the vector's max-abs value of the
+    oracle's mean, and such pools must stay rare."""
     n = rx.shape[0]
     gb = oracle.bf16_rne(gx.ravel()).reshape(n, 128)
     rb = oracle.bf16_rne(rx.ravel()).reshape(n, 128)
     ch = gb != rb
     flip = ch.any(axis=1)
     ref_c, ref_s = rc.copy(), rs.copy()
+    worst = 0.0
     if flip.any():
-        # Every channel that rounds differently must be explained by fp32
-        # accumulation error, which is absolute on the vector's scale (so
-        # channels near zero flip most): the two means of that channel differ
-        # by at most 64 fp32 ulps of the vector's max-abs value.
+        # fp32 accumulation error is absolute on the vector's scale, so
+        # channels near zero (where bf16 values are closest) flip most
         vmax = np.abs(rx).max(axis=1, keepdims=True)
-        near = np.abs(gx.astype(np.float64) - rx) <= 64 * 2.0**-23 * vmax
-        assert np.all(near[ch]), f"{what}: a channel rounds differently beyond fp32 error"
+        err_ulps = np.abs(gx.astype(np.float64) - rx) / (2.0**-23 * vmax)
+        worst = float(err_ulps[ch].max())
+        assert worst <= ulps, \
+            f"{what}: a channel rounds differently {worst:.1f} fp32 ulps from the oracle's mean"
         ref_c[flip], ref_s[flip] = oracle.pool_epilogue(gx[flip], round_scale)
     # A rounding-mode error would flip about half of all channels.
-    assert flip.sum() <= max(8, 0.05 * n), f"{what}: {flip.sum()} of {n} pools round differently"
-    return ref_c, ref_s, int(flip.sum())
+    nf = int(flip.sum())
+    assert nf <= max(FLIP_FLOOR, FLIP_FRAC * n), f"{what}: {nf} of {n} pools round differently"
+    note(f"{what}: {nf} of {n} vectors at a bf16 boundary ({int(ch.sum())} channels, "
+         f"worst {worst:.2f} fp32 ulps of the vector max)")
+    return ref_c, ref_s, nf
 
+
+def check_raw_codes(got, ref, what):
+    """The literal bar without the boundary rule: at most 0.1% of all codes
+    differ from the oracle's (by any number of steps).  Applied to the
+    full-size batches, where 0.1% is a meaningful count."""
+    d = np.abs(e4m3_ordinal(got) - e4m3_ordinal(ref))
+    n_off = int((d != 0).sum())
+    note(f"{what}: raw vs oracle {n_off} of {d.size} codes differ, largest by {d.max(initial=0)}")
+    assert n_off <= 0.001 * d.size, f"{what}: {n_off} of {d.size} codes differ from the oracle"
+    return n_off
 
 
 # ------------------------------------------------------------------ pool-16 prefill
@@ -116,12 +146,13 @@ def compare_prefill(d, rows, round_scale, what, key_stride=None):
     rc, rs, rx = oracle.compress_prefill(d["keys"], d["scores"], d["ape"], rows, round_scale)
     err = rel_err_rows(gx[:n], rx)
     assert err.max() <= VEC_TOL, f"{what}: fp32 mean rel err {err.max():.3g}"
-    raw = np.abs(e4m3_ordinal(gc[:n]) - e4m3_ordinal(rc))
     ref_c, ref_s, flips = reference_for(gx[:n], rx, rc, rs, round_scale, what)
     n_off = check_codes(gc[:n], ref_c, what)
     check_scales(gs[:n], ref_s, round_scale, what)
+    if n * 128 >= RAW_CHECK_MIN_CODES:
+        check_raw_codes(gc[:n], rc, what)
     note(f"{what}: max rel err {err.max():.3g}, bf16-boundary pools {flips}, codes off by one "
-         f"{n_off}; raw vs oracle: {(raw != 0).sum()} codes differ, max {raw.max()}")
+         f"{n_off}")
 
 
 def test_pool16_single_sequence_c1():
@@ -593,6 +624,56 @@ def compare_c128_prefill_fused(d, what, pad=False):
     return paired
 
 
+@pytest.mark.parametrize("seed", [40, 41])
+def test_c128_prefill_result_is_independent_of_plan_order(seed):
+    """Race check: the plans (two launches) and work items (one launch) reach
+    the GPU in several random orders, with load_indices passed explicitly and
+    equal to indices, so the state rows a request reads are the rows it
+    replaces.  The compress pass only reads the state and each write (or
+    paired item) reads its own row before replacing it, so the outputs and
+    states must be the same for every order, bit for bit, and equal the
+    oracle's within tolerance."""
+    d = c128_prefill_case(seed=seed, batch=12, max_prior=900, max_extend=1100)
+    n = int(d["extend_lens"].sum())
+    note(f"c128 prefill plan order, seed {seed}: {n} tokens")
+    st = d["state"].copy()
+    ref = np.full((n, 128), np.nan, np.float32)
+    oracle.c128_prefill(st, d["kv_score_in"], d["ape"], d["indices"], d["cplan"], d["wplan"],
+                        out=ref)
+    cp, wp = kvc.kvc_c128_plan_prefill(d["seq_lens"], d["extend_lens"], n)
+    items = kvc.kvc_c128_plan_prefill_fused(d["seq_lens"], d["extend_lens"], n)
+    assert wp.size > 0 and np.any(d["prior_counts"] > 0)
+    x, ape, idx = dev(d["kv_score_in"]), dev(d["ape"]), dev(d["indices"])
+    li = dev(d["indices"].copy())
+    g = np.random.default_rng(seed)
+    results = []
+    for k in range(4):
+        pc, pw, pi = (np.arange(a.size) if k == 0 else g.permutation(a.size)
+                      for a in (cp, wp, items))
+        gst = dev(d["state"])
+        gout = torch.full((n, 128), float("nan"), device="cuda")
+        kvc.kvc_c128_online_prefill(gst, x, gout, ape, idx, kvc.plans_to_device(cp[pc]), cp.size,
+                                    kvc.plans_to_device(wp[pw]), wp.size, load_indices=li)
+        fst = dev(d["state"])
+        fout = torch.full((n, 128), float("nan"), device="cuda")
+        kvc.kvc_c128_online_prefill_fused(fst, x, ape, idx, kvc.items_to_device(items[pi]),
+                                          items.size, out=fout, load_indices=li)
+        torch.cuda.synchronize()
+        results.append([t.cpu().numpy() for t in (gst, gout, fst, fout)])
+    for k, r in enumerate(results):
+        for i, (a, b) in enumerate(zip(r, results[0])):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), \
+                f"order {k}: output {i} differs from the planner's order"
+        assert np.array_equal(r[1], r[3], equal_nan=True), f"order {k}: one launch != two"
+        assert np.array_equal(r[0], r[2], equal_nan=True), f"order {k}: states differ"
+    gst, gout = results[0][0], results[0][1]
+    assert np.array_equal(np.isnan(gout), np.isnan(ref))
+    rows = ~np.isnan(ref[:, 0])
+    e = rel_err_rows(gout[rows], ref[rows]).max(initial=0)
+    assert e <= VEC_TOL, f"plan order: out err {e:.3g}"
+    compare_state(gst, st, "plan order state")
+
+
 def test_c128_prefill_fused_full_size_c5():
     assert compare_c128_prefill_fused(c128_prefill_case(seed=0), "c128 fused prefill 32 seqs") > 0
 
@@ -898,7 +979,7 @@ def test_c128_decode_quant_epilogue(round_scale):
     assert np.all(gc[~emit] == 0x33) and np.all(gs[~emit] == 5.0)
     assert rel_err_rows(gout[emit], ro[emit]).max() <= VEC_TOL
     ref_c, ref_s, flips = reference_for(gout[emit], ro[emit], rc[emit], rsc[emit], round_scale,
-                                        "c128 decode quant")
+                                        "c128 decode quant", ulps=FLIP_ULPS_POOL128)
     check_codes(gc[emit], ref_c, "c128 decode quant")
     check_scales(gs[emit], ref_s, round_scale, "c128 decode quant")
     note(f"c128 decode quant: {emit.sum()} vectors, bf16-boundary vectors {flips}")
@@ -925,28 +1006,35 @@ def test_c128_prefill_quant_epilogue():
     assert np.all(gc[~rows[:N]] == 0x33)
     r = rows[:N]
     ref_c, ref_s, flips = reference_for(gout[r], ro[:N][r], rc[:N][r], rsc[:N][r], True,
-                                        "c128 prefill quant")
+                                        "c128 prefill quant", ulps=FLIP_ULPS_POOL128)
     check_codes(gc[r], ref_c, "c128 prefill quant")
+    check_raw_codes(gc[r], rc[:N][r], "c128 prefill quant")
     check_scales(gs[r], ref_s, True, "c128 prefill quant")
     note(f"c128 prefill quant: {r.sum()} vectors, bf16-boundary vectors {flips}")
 
 
-def test_diag_stream_read_reads_every_word():
-    g = np.random.default_rng(30)
-    words = g.integers(0, 2**32, size=(3 * 1024 * 256 * 4 + 4 * 37), dtype=np.uint64).astype(np.uint32)
+@pytest.mark.parametrize("loads", [4, 8, 16])
+def test_diag_stream_read_reads_every_word(loads):
+    g = np.random.default_rng(30 + loads)
+    words = g.integers(0, 2**32, size=(3 * 4096 * loads + 4 * 37), dtype=np.uint64).astype(np.uint32)
     src = dev(words.view(np.int32))
-    sink = torch.zeros(kvc.kvc.STREAM_SINK_WORDS, dtype=torch.int32, device="cuda")
-    kvc.kvc.kvc_diag_stream_read(src, sink)
+    nw = kvc.kvc.stream_read_sink_words(words.size * 4, loads)
+    sink = torch.full((nw + 3,), 7, dtype=torch.int32, device="cuda")
+    kvc.kvc.kvc_diag_stream_read(src, sink, loads)
     torch.cuda.synchronize()
-    n16 = words.size // 4
-    quads = words.reshape(n16, 4)
-    x = np.bitwise_xor.reduce(quads, axis=1)
-    threads = kvc.kvc.STREAM_SINK_WORDS
-    exp = np.zeros(threads, np.uint32)
-    for t0 in range(0, n16, threads):
-        blk = x[t0:t0 + threads]
-        exp[:blk.size] ^= blk
-    assert np.array_equal(sink.cpu().numpy().view(np.uint32), exp)
+    per_block = 1024 * loads                      # 32-bit words per workgroup
+    padded = np.zeros(nw * per_block, np.uint32)
+    padded[:words.size] = words
+    exp = np.bitwise_xor.reduce(padded.reshape(nw, per_block), axis=1)
+    got = sink.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got[:nw], exp)
+    assert np.all(got[nw:] == 7)
+
+
+def test_diag_empty_launch_runs():
+    kvc.kvc.kvc_diag_empty_launch(512, 64)
+    kvc.kvc.kvc_diag_empty_launch(0, 64)
+    torch.cuda.synchronize()
 
 
 def test_explicit_stream_argument():
