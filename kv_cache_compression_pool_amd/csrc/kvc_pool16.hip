@@ -35,8 +35,6 @@
 //   * Ring decode uses the same whole-wave layout for one request per wave.
 // The path is HBM-bound (about 8.3 KB read per 132 B written); there is no
 // dense contraction, so no MFMA.
-#include <type_traits>
-
 #include "kvc_device.hpp"
 #include "kvc_internal.hpp"
 
@@ -77,16 +75,6 @@ __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint4 load_stream(BufRsrc r, uint32_t byte_offset) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 2);
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// f(std::integral_constant<int, I>{}) for I = 0 .. N-1: a loop whose index is
-// a compile-time constant in every iteration, for indexing register arrays.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
 }
 
 __device__ __forceinline__ void widen8(uint4 w, float (&f)[8]) {
@@ -233,6 +221,10 @@ __device__ __forceinline__ void pool_mean_wave_halves(const uint4 (&S)[4], const
   float den[8], acc[8];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
+    // Keep the halves apart: interleaved by the scheduler they need nearly as
+    // many registers as the full-width form (multi-layer ring decode, four
+    // tokens: 92 -> 80 VGPRs, six waves per SIMD instead of five).
+    if (hf) __builtin_amdgcn_sched_barrier(0);
     float u[4][4], m[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) m[j] = -__builtin_huge_valf();
@@ -578,8 +570,12 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   const int wave_in_block = kMaxN <= 8 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))
                                        : (int)(threadIdx.x >> 6);
   // Multi-layer launches: workgroup x of layer y takes request group
-  // (x + y) mod gridDim.x (see pool16_ring_layers_kernel; 24.9 -> 20.4 us on
-  // 64 layers of 256 x 4 with this kernel).  One layer: the identity.
+  // (x + y) mod gridDim.x; one layer: the identity.  Workgroups go to the
+  // eight XCDs round robin in launch order, and the token maps are shared by
+  // all layers, so without the rotation the XCD that holds a group's
+  // completing requests would get them again in every layer, and the
+  // busiest XCD would set the launch time (64 layers of 256 x 4: 24.9 us
+  // without, 20.4 us with, bit-identical).
   const int64_t r = (((int64_t)blockIdx.x + blockIdx.y) % gridDim.x) * kReqPerBlock + wave_in_block;
   const int64_t rr = r < num_requests ? r : 0;   // waves past the batch read request 0, stop below
 
@@ -766,209 +762,6 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   }
 }
 
-// Multi-layer ring decode for verify batches of up to 8 tokens: one wave per
-// (request, layer), blockIdx.y = layer, the token maps shared by all layers.
-// A completion costs one memory round trip after the maps instead of two:
-//  * The token rows are requested first; the maps come through scalar loads,
-//    and as soon as they arrive the wave requests the ring rows of its first
-//    completion, while the token rows are still in flight.
-//  * The ring slots that earlier tokens of the batch stash are therefore not
-//    stored and read back: the completion takes them from those tokens' rows
-//    (parked in LDS), and the stashes are stored after the ring rows have
-//    arrived.  This is the page's in-order semantics: completion t* sees, in
-//    each slot, the latest token before t* that stashes there, or the ring
-//    as the call found it.  A further completion in the same batch (irregular
-//    positions) requests its ring rows when it gets there.
-//  * A stash that a later token of the batch overwrites (same block and
-//    slot) is skipped, so every ring row gets at most one store per call.
-//  * ape ([16,128] fp32 per layer) is staged once per workgroup in LDS
-//    behind the kernel's only barrier, which every wave reaches.
-template <bool kRoundScale, int kMaxN>
-__global__ __launch_bounds__(kBlock) void pool16_ring_layers_kernel(
-    uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
-    const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
-    const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
-    const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
-    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink,
-    RingLayers ls) {
-  static_assert(kMaxN == 4 || kMaxN == 8, "token rows split evenly over the four rows");
-  constexpr int kReqPerBlock = kBlock / 64;
-  constexpr int kLoads = 2 * kMaxN / 4;   // token rows per lane
-  {
-    const int64_t layer = blockIdx.y;
-    ring += layer * ls.ring;
-    key += layer * ls.key;
-    score += layer * ls.score;
-    ape += layer * ls.ape;
-    sink = sink.advanced(layer * ls.out_rows);
-  }
-  const int c = threadIdx.x & 15;
-  const int q = (threadIdx.x >> 4) & 3;
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // Workgroup x of layer y takes request group (x + y) mod gridDim.x.
-  // Workgroups go to the eight XCDs round robin in launch order, and the
-  // maps are shared by all layers, so without the rotation the XCD that
-  // holds a group's completing requests would get them again in every layer,
-  // and the busiest XCD would set the launch time (64 layers of 256 x 4:
-  // 24.0 us without, 20.25 us with, bit-identical).
-  const int64_t grp = ((int64_t)blockIdx.x + blockIdx.y) % gridDim.x;
-  const int64_t r = grp * kReqPerBlock + w;
-  const int64_t rr = r < num_requests ? r : 0;   // waves past the batch stop after the barrier
-  __shared__ float4 s_ape[kPool * 32];
-  __shared__ u32x4_t s_tok[kReqPerBlock][kMaxN][2][16];
-
-  // Token rows: row j of lane (q, c) is token 2j + (q >> 1), key (q even) or
-  // score (q odd), 16-byte chunk c.
-  const bool is_score = q & 1;
-  const ApeRegs ape_regs = load_ape(ape);
-  u32x4_t tok[kLoads];
-  static_for<0, kLoads>([&](auto J) {
-    constexpr int j = decltype(J)::value;
-    const int t = 2 * j + (q >> 1);
-    const int tt = t < next_n ? t : next_n - 1;   // in bounds; unused if clamped
-    const uint16_t* src = is_score ? score + rr * score_sb + tt * score_st
-                                   : key + rr * key_sb + tt * key_st;
-    tok[j] = reinterpret_cast<const u32x4_t*>(src)[c];
-  });
-  int32_t loc[kMaxN], pos[kMaxN], ts[kMaxN];
-#pragma unroll
-  for (int t = 0; t < kMaxN; ++t) {
-    const int tt = t < next_n ? t : next_n - 1;
-    const int64_t e = rr * next_n + tt;
-    loc[t] = slot_mapping[e];
-    pos[t] = positions[e];
-    ts[t] = tail_slot[e];
-  }
-  // All map loads in one scalar round trip (left alone, the compiler
-  // interleaves them with the per-token tests below and waits for each).
-#pragma unroll
-  for (int t = 0; t < kMaxN; ++t) asm volatile("" ::"s"(loc[t]), "s"(pos[t]), "s"(ts[t]));
-  int32_t blk[kMaxN];
-  uint32_t completes = 0, stashes = 0;
-#pragma unroll
-  for (int t = 0; t < kMaxN; ++t) {
-    const int64_t b = (int64_t)(ts[t] > 0 ? ts[t] : 0) / kPool;
-    blk[t] = (int32_t)b;   // ts is int32, so the block index fits
-    if (t >= next_n || b >= num_blocks) continue;
-    if (loc[t] >= 0 && pos[t] >= 0 && (pos[t] & (kPool - 1)) == kPool - 1) completes |= 1u << t;
-    if (pos[t] >= 0 && ts[t] >= 0) stashes |= 1u << t;
-  }
-  if (r >= num_requests) completes = stashes = 0;
-
-  // Stash decision per row j of this lane: the token's rows are stored unless
-  // a later token of the batch stashes the same slot of the same block.
-  // Returns the destination in the ring (elements) or -1.
-  auto stash_dst = [&](auto J) -> int64_t {
-    constexpr int j = decltype(J)::value;
-    const bool hi = q >> 1;
-    const int t = 2 * j + hi;
-    bool keep = (stashes >> t) & 1u;
-#pragma unroll
-    for (int u = 2 * j + 1; u < kMaxN; ++u)
-      if (u > t && ((stashes >> u) & 1u) && blk[u] == blk[t] &&
-          ((pos[u] ^ pos[t]) & (kPool - 1)) == 0)
-        keep = false;
-    const int32_t bt = hi ? blk[2 * j + 1] : blk[2 * j];
-    const int32_t pt = hi ? pos[2 * j + 1] : pos[2 * j];
-    return keep ? (int64_t)bt * (2 * kPool * 128) +
-                      ((is_score ? kPool : 0) + (pt & (kPool - 1))) * 128
-                : -1;
-  };
-  // Stage ape and pass the workgroup barrier.  It waits only for this
-  // workgroup's LDS writes, so ring rows in flight stay in flight.  Both
-  // paths below pass it exactly once.
-  auto stage_ape_and_sync = [&]() {
-    s_ape[threadIdx.x] = ape_regs.a;
-    s_ape[threadIdx.x + kBlock] = ape_regs.b;
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-
-  if (!completes) {   // uniform: the request only stashes (or is past the batch)
-    stage_ape_and_sync();
-    static_for<0, kLoads>([&](auto J) {
-      const int64_t dst = stash_dst(J);
-      if (dst >= 0) reinterpret_cast<u32x4_t*>(ring + dst)[c] = tok[decltype(J)::value];
-    });
-    return;
-  }
-
-  // A completion: its ring rows (slots 4q..4q+3) are requested now, with the
-  // token rows still in flight.
-  auto ring_rows = [&](int t1, uint4 (&S)[4], uint4 (&K)[4], int32_t& l1) {
-    int32_t b1 = 0;
-#pragma unroll
-    for (int t = 0; t < kMaxN; ++t)
-      if (t == t1) {
-        b1 = blk[t];
-        l1 = loc[t];
-      }
-    const uint16_t* ring_k = ring + (int64_t)b1 * (2 * kPool * 128);
-    const uint16_t* ring_s = ring_k + kPool * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      S[i] = reinterpret_cast<const uint4*>(ring_s + (4 * q + i) * 128)[c];
-      K[i] = reinterpret_cast<const uint4*>(ring_k + (4 * q + i) * 128)[c];
-    }
-    return b1;
-  };
-  uint4 S[4], K[4];
-  int32_t l1 = 0;
-  int t1 = __builtin_ctz(completes);
-  int32_t b1 = ring_rows(t1, S, K, l1);
-
-  // Park the token rows for the whole wave (a wave's LDS accesses execute in
-  // order), then the barrier.
-  static_for<0, kLoads>([&](auto J) {
-    constexpr int j = decltype(J)::value;
-    s_tok[w][2 * j + (q >> 1)][is_score][c] = tok[j];
-  });
-  stage_ape_and_sync();
-
-  uint32_t comp = completes;
-  while (comp) {   // uniform over the wave
-    comp &= comp - 1;
-    // Slots stashed before t1 by tokens of this batch (the latest one wins),
-    // then slot 15: the completing token itself.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int slot = 4 * q + i;
-      int src = -1;
-#pragma unroll
-      for (int t = 0; t < kMaxN; ++t)
-        if (t < t1 && ((stashes >> t) & 1u) && blk[t] == b1 && (pos[t] & (kPool - 1)) == slot)
-          src = t;
-      if (q == 3 && i == 3) src = t1;
-      if (src >= 0) {
-        const u32x4_t ps = s_tok[w][src][1][c], pk = s_tok[w][src][0][c];
-        S[i] = make_uint4(ps.x, ps.y, ps.z, ps.w);
-        K[i] = make_uint4(pk.x, pk.y, pk.z, pk.w);
-      }
-    }
-    float x[2];
-    pool_mean_wave_lds(S, K, s_ape, c, q, x);
-
-    if (sink.dbg && l1 < sink.rows)   // channels 8c + 2q + t
-      reinterpret_cast<float2*>(sink.dbg + (int64_t)l1 * 128)[4 * c + q] =
-          make_float2(x[0], x[1]);
-    float scale;
-    const uint32_t codes = rotate_quantise64(x, c, q, kRoundScale, scale);
-    if (l1 < sink.rows) sink.store2(l1, c, q, codes, scale);
-    if (comp) {   // a further completion in the batch (irregular positions)
-      t1 = __builtin_ctz(comp);
-      b1 = ring_rows(t1, S, K, l1);
-    }
-  }
-
-  // The stashes, after every completion's ring rows have arrived, from the
-  // parked rows.
-  static_for<0, kLoads>([&](auto J) {
-    constexpr int j = decltype(J)::value;
-    const int64_t dst = stash_dst(J);
-    if (dst >= 0)
-      reinterpret_cast<u32x4_t*>(ring + dst)[c] = s_tok[w][2 * j + (q >> 1)][is_score][c];
-  });
-}
-
 // Tail-ring seeding.  Each lane decides for one token whether it is among its
 // request's last 16 (no token 16 positions later maps to the same ring
 // block); the wave then copies its few seeded tokens together, two per step,
@@ -1104,11 +897,6 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
                      key_st, score, score_sb, score_st, ape, slot_mapping, positions,           \
                      num_requests, next_n, sink, ls)
   const bool park = num_layers > 1;
-  if (park && next_n <= 4) {
-    if (round_scale) KVC_RING((pool16_ring_layers_kernel<true, 4>));
-    else KVC_RING((pool16_ring_layers_kernel<false, 4>));
-    return hipGetLastError();
-  }
   if (next_n <= 4) {
     if (round_scale) {
       if (park) KVC_RING((pool16_ring_wave_kernel<true, 4, true>));
