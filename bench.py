@@ -39,6 +39,7 @@ MALL_BYTES = 256 << 20                # Infinity Cache capacity
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pool16_prefill_ragged64_traffic.json")
 C128_PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "c128_prefill_32seq_single_launch_traffic.json")
 C128_DECODE_TRAFFIC = os.path.join(ROOT, "profiles", "c128_decode_64layers_traffic.json")
+RING_TRAFFIC = os.path.join(ROOT, "profiles", "ring_decode_64layers_traffic.json")
 KERNEL_SOURCES = ("kvc_pool16.hip", "kvc_device.hpp")
 # The pool-16 prefill launch runs one pool per wave up to this many pools and
 # two pools per wave (a second kernel) above it.
@@ -95,7 +96,7 @@ def timed(fn, steps, warmup, torch, stream, host_us_per_call=60.0):
     busy-wait long enough to cover their host-side launch cost, so they run
     back to back on the device; two events on the launch stream bracket them.
     Returns (device ms for all steps, mean device ms per step, host seconds
-    per step when launches are not hidden behind device work)."""
+    per launch: the time fn takes to enqueue its work)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -103,8 +104,10 @@ def timed(fn, steps, warmup, torch, stream, host_us_per_call=60.0):
     t0 = time.perf_counter()
     for i in range(n_host):
         fn(warmup + i)
-    torch.cuda.synchronize()
+    # launches only: the device runs them asynchronously (20 launches do not
+    # fill the queue, so the host never waits for the device here)
     host = (time.perf_counter() - t0) / n_host
+    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     _hold_queue(torch, stream, ms=steps * host_us_per_call / 1e3 + 2.0)
@@ -143,11 +146,21 @@ def bench_pool16_prefill(args, torch, kvc, synth, stream):
     outs = [torch.empty((n, 128), dtype=torch.uint8, device="cuda") for _ in range(R)]
     scl = [torch.empty((n,), dtype=torch.float32, device="cuda") for _ in range(R)]
 
+    # one prepared call per replica: arguments checked and marshalled once,
+    # as a serving loop launching on the same buffers would
+    calls = [kvc.prepare(kvc.kvc_compress_prefill, keys[r], scores[r], ape, rows_t, n, outs[r],
+                         scl[r], True, stream=stream) for r in range(R)]
+
     def step(i):
+        calls[i % R]()
+
+    total_ms, ev_ms, host = timed(step, args.steps, args.warmup, torch, stream)
+
+    def step_unprepared(i):
         r = i % R
         kvc.kvc_compress_prefill(keys[r], scores[r], ape, rows_t, n, outs[r], scl[r], True)
 
-    total_ms, ev_ms, host = timed(step, args.steps, args.warmup, torch, stream)
+    _, _, host_unprepared = timed(step_unprepared, 20, 2, torch, stream)
     bytes_per_vec = 16 * 256 * 2 + 128 + 4 + 4      # keys+scores rows, codes, scale, plan entry
     alg = bytes_per_vec * n
 
@@ -165,8 +178,8 @@ def bench_pool16_prefill(args, torch, kvc, synth, stream):
         _, read_ms, _ = timed(read_step, args.steps, args.warmup, torch, stream)
         read_gbs[loads] = gbs(read_bytes, read_ms)
     return dict(n=n, tokens=T, replicas=R, total_ms=total_ms, ev_ms=ev_ms,
-                host_s=host, alg_bytes=alg, bytes_per_vec=bytes_per_vec, d=d, rows=rows,
-                stream_read_gbs=read_gbs)
+                host_s=host, host_unprepared_s=host_unprepared, alg_bytes=alg,
+                bytes_per_vec=bytes_per_vec, d=d, rows=rows, stream_read_gbs=read_gbs)
 
 
 def launch_floor(torch, kvc, stream, workgroups, threads, steps=100, graph_calls=64):
@@ -217,14 +230,23 @@ def bench_c128_decode(args, torch, kvc, synth, stream):
     idx = to_dev(torch, d["indices"])
     sl_t = to_dev(torch, d["seq_lens"])
 
+    calls = [kvc.prepare(kvc.kvc_c128_online_decode, states[r], ins[r], outs[r], ape, idx, sl_t,
+                         stream=stream) for r in range(R)]
+
     def step(i):
-        r = i % R
-        kvc.kvc_c128_online_decode(states[r], ins[r], outs[r], ape, idx, sl_t)
+        calls[i % R]()
 
     steps = max(args.steps, 50)
     total_ms, ev_ms, host = timed(step, steps, max(args.warmup, 5), torch, stream)
+
+    def step_unprepared(i):
+        r = i % R
+        kvc.kvc_c128_online_decode(states[r], ins[r], outs[r], ape, idx, sl_t)
+
+    _, _, host_unprepared = timed(step_unprepared, 20, 2, torch, stream)
     res = dict(batch=B, emitted=int((c == 127).sum()), replicas=R, total_ms=total_ms,
-               steps=steps, ev_ms=ev_ms, host_s=host, alg_bytes=alg)
+               steps=steps, ev_ms=ev_ms, host_s=host, host_unprepared_s=host_unprepared,
+               alg_bytes=alg)
 
     # Sustained single calls: 64 calls captured in one HIP graph, each graph
     # covering 64 of the state / input replicas, graphs replayed in turn.
@@ -339,8 +361,11 @@ def bench_ring(args, torch, kvc, synth, stream):
     comps = int(((d["slot_mapping"] >= 0) & valid).sum())
     alg = int(valid.sum()) * (512 + 512 + 12) + comps * (15 * 512 + 132)
 
+    call = kvc.prepare(kvc.kvc_compress_decode_ring, ring, ts, key, score, ape, sm, pos, out, scl,
+                       True, stream=stream)
+
     def step(i):
-        kvc.kvc_compress_decode_ring(ring, ts, key, score, ape, sm, pos, out, scl, True)
+        call()
 
     steps = max(args.steps, 50)
     total_ms, ev_ms, host = timed(step, steps, max(args.warmup, 5), torch, stream)
@@ -852,6 +877,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(p["total_ms"] / args.steps, 5),
         "host_launch_ms_per_step": round(p["host_s"] * 1e3, 5),
+        "host_launch_ms_per_step_unprepared": round(p["host_unprepared_s"] * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -888,7 +914,9 @@ def main():
             "emitted_vectors_per_call": c4["emitted"],
             "launch_us": round(c4["ev_ms"] * 1e3, 3), "bytes_per_launch": c4["alg_bytes"],
             "hbm_gbs": round(g4, 1), "hbm_frac": round(g4 / PEAK_HBM_GBS, 4),
-            "state_replicas": c4["replicas"]}
+            "state_replicas": c4["replicas"],
+            "host_launch_us": round(c4["host_s"] * 1e6, 2),
+            "host_launch_us_unprepared": round(c4["host_unprepared_s"] * 1e6, 2)}
         if "graph" in c4:
             cg = c4["graph"]
             gg = gbs(c4["alg_bytes"], cg["call_ms"])
@@ -943,7 +971,8 @@ def main():
             "completions_per_s": round(c3["completions"] * c3["steps"] / (c3["total_ms"] * 1e-3), 1),
             "tokens_per_s": round(c3["requests"] * c3["next_n"] * c3["steps"] / (c3["total_ms"] * 1e-3), 1),
             "launch_us": round(c3["ev_ms"] * 1e3, 3), "bytes_per_launch": c3["alg_bytes"],
-            "hbm_gbs": round(g3, 1), "hbm_frac": round(g3 / PEAK_HBM_GBS, 4)}
+            "hbm_gbs": round(g3, 1), "hbm_frac": round(g3 / PEAK_HBM_GBS, 4),
+            "host_launch_us": round(c3["host_s"] * 1e6, 2)}
         fl, flg = launch_floor(torch, kvc, stream, (c3["requests"] + 3) // 4, 256)
         line["ring_decode"]["launch_floor_us"] = {
             "grid": f"{(c3['requests'] + 3) // 4} x 256 threads", "single": round(fl, 3),
@@ -963,7 +992,8 @@ def main():
                 "tokens_per_s": round(c3["requests"] * c3["next_n"] * cl["layers"]
                                       / (cl["ev_ms"] * 1e-3), 1),
                 "bytes_per_launch": cl["alg_bytes"], "hbm_gbs": round(gl, 1),
-                "hbm_frac": round(gl / PEAK_HBM_GBS, 4), "replicas": cl["replicas"]}
+                "hbm_frac": round(gl / PEAK_HBM_GBS, 4), "replicas": cl["replicas"],
+                "traffic": measured_traffic(RING_TRAFFIC) if cl["layers"] == 64 else None}
         log("next rows (seeding, paged write, epilogues, padding)")
         line["next_rows"] = bench_next_rows(args, torch, kvc, synth, stream)
         line["host_planners"] = bench_planners(kvc, synth)

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 import numpy as np
 
@@ -107,23 +108,88 @@ def _check(rc: int) -> None:
         raise KvcError(rc, lib().kvc_last_error().decode())
 
 
-_current_stream = None
+_capture = threading.local()
+
+
+def _invoke(name, args, stream):
+    """Call device entry point `name` with its marshalled arguments (all but
+    the stream), or, inside prepare(), return them as a PreparedCall."""
+    if getattr(_capture, "on", False):
+        return PreparedCall(name, args, stream)
+    _check(getattr(lib(), name)(*args, _stream(stream)))
+
+
+class PreparedCall:
+    """One device entry point with its arguments checked and marshalled once
+    (see prepare()).  Calling it issues the C call and nothing else, so a
+    loop that launches the same call on the same buffers pays only the ctypes
+    call.  It holds references to the tensors it was prepared with."""
+
+    __slots__ = ("_fn", "_args", "_stream", "_keep", "name")
+
+    def __init__(self, name, args, stream):
+        self.name = name
+        self._fn = getattr(lib(), name)
+        # converted to ctypes values once (the call then only passes them)
+        self._args = tuple(None if a is None else t(a)
+                           for t, a in zip(self._fn.argtypes, args))
+        # a stream given at preparation is kept; None means torch's current
+        # stream at each call
+        self._stream = None if stream is None else _stream(stream)
+        self._keep = None
+
+    def __call__(self, stream=None):
+        s = self._stream if stream is None else _stream(stream)
+        if s is None:
+            s = _current_stream()
+        rc = self._fn(*self._args, s)
+        if rc != KVC_OK:
+            _check(rc)
+
+
+def prepare(entry_point, *args, **kwargs):
+    """Validate and marshal the arguments of a device entry point of this
+    module once; returns a PreparedCall that launches it.  The buffers must
+    stay the same tensors with the same shapes (the call keeps references to
+    them); their contents may change between calls.  Example:
+        launch = kvc.prepare(kvc.kvc_compress_prefill, keys, scores, ape, rows,
+                             n_pools, out, scale, True)
+        launch()            # on torch's current stream
+    """
+    _capture.on = True
+    try:
+        call = entry_point(*args, **kwargs)
+    finally:
+        _capture.on = False
+    if not isinstance(call, PreparedCall):
+        raise TypeError(f"{getattr(entry_point, '__name__', entry_point)} is not a device "
+                        "entry point of this module")
+    call._keep = (args, kwargs)
+    return call
+
+
+_current_stream_fn = None
+
+
+def _current_stream() -> int:
+    """torch's current hipStream_t handle on the current device."""
+    global _current_stream_fn
+    if _current_stream_fn is None:
+        import torch
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        dev = getattr(torch._C, "_cuda_getDevice", None)
+        if raw is not None and dev is not None:
+            # the handle without building a Stream object (a few us per call)
+            _current_stream_fn = lambda: raw(dev())
+        else:
+            _current_stream_fn = lambda: torch.cuda.current_stream().cuda_stream
+    return _current_stream_fn()
 
 
 def _stream(stream) -> int | None:
     """hipStream_t handle: None = torch's current stream; a torch.cuda.Stream
     or a raw integer handle is used as given."""
-    global _current_stream
     if stream is None:
-        if _current_stream is None:
-            import torch
-            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-            dev = getattr(torch._C, "_cuda_getDevice", None)
-            if raw is not None and dev is not None:
-                # the handle without building a Stream object (a few us per call)
-                _current_stream = lambda: raw(dev())
-            else:
-                _current_stream = lambda: torch.cuda.current_stream().cuda_stream
         return _current_stream()
     if hasattr(stream, "cuda_stream"):
         return int(stream.cuda_stream)
@@ -247,13 +313,12 @@ def kvc_compress_prefill(keys, scores, ape, pool_src_row, n_pools: int, out_fp8,
         _need(dbg_pooled.dim() == 2 and dbg_pooled.shape[0] >= n_pools
               and dbg_pooled.shape[1] == 128 and dbg_pooled.is_contiguous(),
               "dbg_pooled must be a contiguous [>=n_pools, 128] tensor")
-    _check(lib().kvc_compress_prefill(
+    return _invoke("kvc_compress_prefill", (
         k.data_ptr(), k.stride(0), s.data_ptr(), s.stride(0), k.shape[0],
         _dptr(ape, torch.float32, "ape"), pool_size,
         _dptr(pool_src_row, torch.int32, "pool_src_row", optional=True), int(n_pools),
         _dptr(out_fp8, torch.uint8, "out_fp8"), _dptr(out_scale, torch.float32, "out_scale"),
-        int(round_scale), _dptr(dbg_pooled, torch.float32, "dbg_pooled", optional=True),
-        _stream(stream)))
+        int(round_scale), _dptr(dbg_pooled, torch.float32, "dbg_pooled", optional=True)), stream)
 
 
 def kvc_compress_prefill_paged(keys, scores, ape, pool_src_row, n_pools: int, kv_cache, loc,
@@ -281,12 +346,12 @@ def kvc_compress_prefill_paged(keys, scores, ape, pool_src_row, n_pools: int, kv
               and write_mask.element_size() == 1 and write_mask.is_contiguous(),
               "write_mask must be a contiguous 1-byte device tensor of n_pools entries")
         wm = write_mask.data_ptr()
-    _check(lib().kvc_compress_prefill_paged(
+    return _invoke("kvc_compress_prefill_paged", (
         k.data_ptr(), k.stride(0), s.data_ptr(), s.stride(0), k.shape[0],
         _dptr(ape, torch.float32, "ape"), pool_size,
         _dptr(pool_src_row, torch.int32, "pool_src_row", optional=True), n_pools,
         _dptr(kv_cache, torch.uint8, "kv_cache"), kv_cache.numel() // 132, 1,
-        _dptr(loc, torch.int64, "loc"), wm, int(round_scale), _stream(stream)))
+        _dptr(loc, torch.int64, "loc"), wm, int(round_scale)), stream)
 
 
 def kvc_compress_decode_ring_layers(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,
@@ -317,7 +382,7 @@ def kvc_compress_decode_ring_layers(tail_ring, tail_slot_mapping, key, score, ap
     num_out = out_fp8.shape[1]
     _need(tuple(out_scale.shape) == (L, num_out) and out_scale.is_contiguous(),
           "out_scale must be a contiguous [L, num_out] tensor")
-    _check(lib().kvc_compress_decode_ring_layers(
+    return _invoke("kvc_compress_decode_ring_layers", (
         ring.data_ptr(), ring.stride(0), ring.shape[1],
         _dptr(tail_slot_mapping, torch.int32, "tail_slot_mapping"),
         k.data_ptr(), k.stride(0), k.stride(1), k.stride(2),
@@ -325,8 +390,7 @@ def kvc_compress_decode_ring_layers(tail_ring, tail_slot_mapping, key, score, ap
         _dptr(ape, torch.float32, "ape"), ape.stride(0),
         _dptr(slot_mapping, torch.int32, "slot_mapping"), _dptr(positions, torch.int32, "positions"),
         R, N, pool_size, _dptr(out_fp8, torch.uint8, "out_fp8"),
-        _dptr(out_scale, torch.float32, "out_scale"), num_out, L, int(round_scale),
-        _stream(stream)))
+        _dptr(out_scale, torch.float32, "out_scale"), num_out, L, int(round_scale)), stream)
 
 
 def kvc_compress_decode_ring_paged(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,
@@ -349,13 +413,12 @@ def kvc_compress_decode_ring_paged(tail_ring, tail_slot_mapping, key, score, ape
     _shape_ok(ape, (pool_size, 128), "ape")
     _need(kv_cache.is_contiguous() and kv_cache.shape[-1] == 132 and kv_cache.numel() %
           132 == 0, "kv_cache must be a contiguous [pages, 132] uint8 tensor")
-    _check(lib().kvc_compress_decode_ring_paged(
+    return _invoke("kvc_compress_decode_ring_paged", (
         ring.data_ptr(), ring.shape[0], _dptr(tail_slot_mapping, torch.int32, "tail_slot_mapping"),
         k.data_ptr(), k.stride(0), k.stride(1), s.data_ptr(), s.stride(0), s.stride(1),
         _dptr(ape, torch.float32, "ape"), _dptr(slot_mapping, torch.int32, "slot_mapping"),
         _dptr(positions, torch.int32, "positions"), R, N, pool_size,
-        _dptr(kv_cache, torch.uint8, "kv_cache"), kv_cache.numel() // 132, 1, int(round_scale),
-        _stream(stream)))
+        _dptr(kv_cache, torch.uint8, "kv_cache"), kv_cache.numel() // 132, 1, int(round_scale)), stream)
 
 
 def kvc_compress_decode_ring(tail_ring, tail_slot_mapping, key, score, ape, slot_mapping,
@@ -386,14 +449,14 @@ def kvc_compress_decode_ring(tail_ring, tail_slot_mapping, key, score, ape, slot
         _need(dbg_pooled.dim() == 2 and dbg_pooled.shape[0] >= out_fp8.shape[0]
               and dbg_pooled.shape[1] == 128 and dbg_pooled.is_contiguous(),
               "dbg_pooled must be a contiguous [num_out, 128] tensor")
-    _check(lib().kvc_compress_decode_ring(
+    return _invoke("kvc_compress_decode_ring", (
         ring.data_ptr(), ring.shape[0], _dptr(tail_slot_mapping, torch.int32, "tail_slot_mapping"),
         k.data_ptr(), k.stride(0), k.stride(1), s.data_ptr(), s.stride(0), s.stride(1),
         _dptr(ape, torch.float32, "ape"), _dptr(slot_mapping, torch.int32, "slot_mapping"),
         _dptr(positions, torch.int32, "positions"), R, N, pool_size,
         _dptr(out_fp8, torch.uint8, "out_fp8"), _dptr(out_scale, torch.float32, "out_scale"),
         out_fp8.shape[0], int(round_scale),
-        _dptr(dbg_pooled, torch.float32, "dbg_pooled", optional=True), _stream(stream)))
+        _dptr(dbg_pooled, torch.float32, "dbg_pooled", optional=True)), stream)
 
 
 def kvc_seed_tail_ring(tail_ring, key, score, tslot, pool_size: int = 16, stream=None):
@@ -409,10 +472,9 @@ def kvc_seed_tail_ring(tail_ring, key, score, tslot, pool_size: int = 16, stream
     _need(k.dim() == 2 and s.dim() == 2 and k.shape[0] >= n and s.shape[0] >= n,
           "key and score must hold one row per token")
     _shape_ok(tslot, (n,), "tslot")
-    _check(lib().kvc_seed_tail_ring(ring.data_ptr(), ring.shape[0], k.data_ptr(), k.stride(0),
+    return _invoke("kvc_seed_tail_ring", (ring.data_ptr(), ring.shape[0], k.data_ptr(), k.stride(0),
                                     s.data_ptr(), s.stride(0),
-                                    _dptr(tslot, torch.int32, "tslot"), n, pool_size,
-                                    _stream(stream)))
+                                    _dptr(tslot, torch.int32, "tslot"), n, pool_size), stream)
 
 
 def kvc_c128_online_decode(state, kv_score_in, out, ape, indices, seq_lens, stream=None):
@@ -424,11 +486,11 @@ def kvc_c128_online_decode(state, kv_score_in, out, ape, indices, seq_lens, stre
     _shape_ok(ape, (128, 128), "ape")
     _shape_ok(indices, (B,), "indices")
     _shape_ok(seq_lens, (B,), "seq_lens")
-    _check(lib().kvc_c128_online_decode(
+    return _invoke("kvc_c128_online_decode", (
         _dptr(state, torch.float32, "state"), state.shape[0],
         _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out, torch.float32, "out"),
         _dptr(ape, torch.float32, "ape"), _dptr(indices, torch.int32, "indices"),
-        _dptr(seq_lens, torch.int32, "seq_lens"), kv_score_in.shape[0], _stream(stream)))
+        _dptr(seq_lens, torch.int32, "seq_lens"), kv_score_in.shape[0]), stream)
 
 
 def kvc_c128_online_decode_layers(state, kv_score_in, out, ape, indices, seq_lens, stream=None):
@@ -442,12 +504,12 @@ def kvc_c128_online_decode_layers(state, kv_score_in, out, ape, indices, seq_len
     _shape_ok(ape, (Lr, 128, 128), "ape")
     _shape_ok(indices, (B,), "indices")
     _shape_ok(seq_lens, (B,), "seq_lens")
-    _check(lib().kvc_c128_online_decode_layers(
+    return _invoke("kvc_c128_online_decode_layers", (
         _dptr(state, torch.float32, "state"), state.stride(0), state.shape[1],
         _dptr(kv_score_in, torch.float32, "kv_score_in"), kv_score_in.stride(0),
         _dptr(out, torch.float32, "out"), out.stride(0), _dptr(ape, torch.float32, "ape"),
         ape.stride(0), _dptr(indices, torch.int32, "indices"),
-        _dptr(seq_lens, torch.int32, "seq_lens"), B, Lr, _stream(stream)))
+        _dptr(seq_lens, torch.int32, "seq_lens"), B, Lr), stream)
 
 
 def kvc_c128_online_decode_quant(state, kv_score_in, out_fp8, out_scale, ape, indices, seq_lens,
@@ -463,12 +525,12 @@ def kvc_c128_online_decode_quant(state, kv_score_in, out_fp8, out_scale, ape, in
     _shape_ok(ape, (128, 128), "ape")
     _shape_ok(indices, (B,), "indices")
     _shape_ok(seq_lens, (B,), "seq_lens")
-    _check(lib().kvc_c128_online_decode_quant(
+    return _invoke("kvc_c128_online_decode_quant", (
         _dptr(state, torch.float32, "state"), state.shape[0],
         _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out_fp8, torch.uint8, "out_fp8"),
         _dptr(out_scale, torch.float32, "out_scale"), _dptr(ape, torch.float32, "ape"),
         _dptr(indices, torch.int32, "indices"), _dptr(seq_lens, torch.int32, "seq_lens"), B,
-        int(round_scale), _stream(stream)))
+        int(round_scale)), stream)
 
 
 def kvc_c128_online_prefill_quant(state, kv_score_in, out_fp8, out_scale, ape, indices,
@@ -487,15 +549,14 @@ def kvc_c128_online_prefill_quant(state, kv_score_in, out_fp8, out_scale, ape, i
     if load_indices is not None:
         _shape_ok(load_indices, (B,), "load_indices")
     _check_plans(compress_plan, n_compress, write_plan, n_write)
-    _check(lib().kvc_c128_online_prefill_quant(
+    return _invoke("kvc_c128_online_prefill_quant", (
         _dptr(state, torch.float32, "state"), state.shape[0],
         _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out_fp8, torch.uint8, "out_fp8"),
         _dptr(out_scale, torch.float32, "out_scale"), N, _dptr(ape, torch.float32, "ape"),
         _dptr(indices, torch.int32, "indices"),
         _dptr(load_indices, torch.int32, "load_indices", optional=True), B,
         None if compress_plan is None else compress_plan.data_ptr(), int(n_compress),
-        None if write_plan is None else write_plan.data_ptr(), int(n_write), int(round_scale),
-        _stream(stream)))
+        None if write_plan is None else write_plan.data_ptr(), int(n_write), int(round_scale)), stream)
 
 
 def _check_plans(compress_plan, n_compress, write_plan, n_write):
@@ -523,13 +584,13 @@ def kvc_c128_online_prefill(state, kv_score_in, out, ape, indices, compress_plan
     _check_plans(compress_plan, n_compress, write_plan, n_write)
     cp = None if compress_plan is None else compress_plan.data_ptr()
     wp = None if write_plan is None else write_plan.data_ptr()
-    _check(lib().kvc_c128_online_prefill(
+    return _invoke("kvc_c128_online_prefill", (
         _dptr(state, torch.float32, "state"), state.shape[0],
         _dptr(kv_score_in, torch.float32, "kv_score_in"), _dptr(out, torch.float32, "out"),
         kv_score_in.shape[0], _dptr(ape, torch.float32, "ape"),
         _dptr(indices, torch.int32, "indices"),
         _dptr(load_indices, torch.int32, "load_indices", optional=True), indices.shape[0],
-        cp, int(n_compress), wp, int(n_write), _stream(stream)))
+        cp, int(n_compress), wp, int(n_write)), stream)
 
 
 def kvc_c128_online_prefill_fused(state, kv_score_in, ape, indices, items, n_items, out=None,
@@ -556,7 +617,7 @@ def kvc_c128_online_prefill_fused(state, kv_score_in, ape, indices, items, n_ite
         _need(items is not None and items.is_cuda and items.is_contiguous()
               and items.numel() * items.element_size() >= 32 * int(n_items),
               f"items must be a contiguous device tensor of at least {int(n_items)} entries")
-    _check(lib().kvc_c128_online_prefill_fused(
+    return _invoke("kvc_c128_online_prefill_fused", (
         _dptr(state, torch.float32, "state"), state.shape[0],
         _dptr(kv_score_in, torch.float32, "kv_score_in"),
         _dptr(out, torch.float32, "out", optional=True),
@@ -564,14 +625,14 @@ def kvc_c128_online_prefill_fused(state, kv_score_in, ape, indices, items, n_ite
         _dptr(out_scale, torch.float32, "out_scale", optional=True), int(round_scale), N,
         _dptr(ape, torch.float32, "ape"), _dptr(indices, torch.int32, "indices"),
         _dptr(load_indices, torch.int32, "load_indices", optional=True), B,
-        None if items is None else items.data_ptr(), int(n_items), _stream(stream)))
+        None if items is None else items.data_ptr(), int(n_items)), stream)
 
 
 def kvc_diag_convert(x, bf16_out=None, fp8_out=None, stream=None):
     import torch
-    _check(lib().kvc_diag_convert(
+    return _invoke("kvc_diag_convert", (
         _dptr(x, torch.float32, "x"), _dptr(bf16_out, torch.int16, "bf16_out", optional=True),
-        _dptr(fp8_out, torch.uint8, "fp8_out", optional=True), x.numel(), _stream(stream)))
+        _dptr(fp8_out, torch.uint8, "fp8_out", optional=True), x.numel()), stream)
 
 
 def stream_read_sink_words(nbytes: int, loads_per_lane: int) -> int:
@@ -587,13 +648,13 @@ def kvc_diag_stream_read(src, sink, loads_per_lane: int = 8, stream=None):
     _need(src.is_cuda and src.is_contiguous(), "src must be a contiguous device tensor")
     _need(sink.is_cuda and sink.element_size() == 4 and sink.is_contiguous(),
           "sink must be a contiguous device tensor of 4-byte words")
-    _check(lib().kvc_diag_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(),
-                                      int(loads_per_lane), _stream(stream)))
+    return _invoke("kvc_diag_stream_read", (src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(),
+                                      int(loads_per_lane)), stream)
 
 
 def kvc_diag_empty_launch(workgroups: int, threads: int, stream=None):
     """Launch an empty kernel of the given grid (launch-floor measurements)."""
-    _check(lib().kvc_diag_empty_launch(int(workgroups), int(threads), _stream(stream)))
+    return _invoke("kvc_diag_empty_launch", (int(workgroups), int(threads)), stream)
 
 
 def plans_to_device(plan: np.ndarray, device="cuda"):

@@ -299,3 +299,11 @@ def test_plan_struct_layout():
     assert kvc.PLAN_DTYPE.itemsize == 16
     assert kvc.ITEM_DTYPE.itemsize == 32
     assert kvc.PLAN_DTYPE == oracle.PLAN_DTYPE
+
+
+def test_prepare_accepts_device_entry_points_only():
+    """prepare() returns a PreparedCall for device entry points; anything else
+    (here a host planner, which simply runs) is refused."""
+    with pytest.raises(TypeError):
+        kvc.prepare(kvc.kvc_plan_pool_prefill, np.array([32], np.int64))
+    assert callable(kvc.PreparedCall.__call__)

@@ -18,7 +18,8 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_is_reported_only_for_the_measured_sources(tmp_path):
-    for path in (bench.TRAFFIC_FILE, bench.C128_PREFILL_TRAFFIC, bench.C128_DECODE_TRAFFIC):
+    for path in (bench.TRAFFIC_FILE, bench.C128_PREFILL_TRAFFIC, bench.C128_DECODE_TRAFFIC,
+                 bench.RING_TRAFFIC):
         t = json.load(open(path))
         assert 0.99 < t["traffic_over_algorithmic"] < 1.1
         srcs = tuple(t.get("kernel_sources", bench.KERNEL_SOURCES))

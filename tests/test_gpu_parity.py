@@ -1037,6 +1037,47 @@ def test_diag_empty_launch_runs():
     torch.cuda.synchronize()
 
 
+def test_prepared_calls_equal_direct_calls():
+    """A PreparedCall launches exactly what the direct call launches: the
+    same results on the same buffers, new results after the buffers' contents
+    change, and on an explicit stream."""
+    d = synth.pool16_ragged(seed=51, num_seqs=6, max_len=600)
+    rows = kvc.kvc_plan_pool_prefill(d["seq_lens"])
+    n = rows.size
+    k, s_, a, r = dev(d["keys"], torch.int16), dev(d["scores"], torch.int16), dev(d["ape"]), dev(rows)
+    o1 = torch.zeros((n, 128), dtype=torch.uint8, device="cuda")
+    c1 = torch.zeros((n,), device="cuda")
+    kvc.kvc_compress_prefill(k, s_, a, r, n, o1, c1, True)
+    o2 = torch.zeros_like(o1)
+    c2 = torch.zeros_like(c1)
+    launch = kvc.prepare(kvc.kvc_compress_prefill, k, s_, a, r, n, o2, c2, True)
+    assert isinstance(launch, kvc.PreparedCall) and launch.name == "kvc_compress_prefill"
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(c1, c2)
+    k.copy_(dev(d["scores"], torch.int16))               # new contents, same buffers
+    kvc.kvc_compress_prefill(k, s_, a, r, n, o1, c1, True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    launch(stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(c1, c2)
+    # the pool-128 decode, which updates its state in place, twice in a row
+    dd = c128_decode_case(seed=52, batch=100, emit_frac=0.3)
+    st1, st2 = dev(dd["state"]), dev(dd["state"])
+    x, ap, ix, sl = (dev(dd[kk]) for kk in ("kv_score_in", "ape", "indices", "seq_lens"))
+    out1 = torch.full((100, 128), 3.0, device="cuda")
+    out2 = torch.full((100, 128), 3.0, device="cuda")
+    step = kvc.prepare(kvc.kvc_c128_online_decode, st2, x, out2, ap, ix, sl)
+    for _ in range(2):
+        kvc.kvc_c128_online_decode(st1, x, out1, ap, ix, sl)
+        step()
+    torch.cuda.synchronize()
+    assert torch.equal(st1.view(torch.int32), st2.view(torch.int32))   # NaN in unused slots
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32))
+
+
 def test_explicit_stream_argument():
     """Work is enqueued on the stream passed in (a torch.cuda.Stream or its raw
     handle), not on the current stream."""
