@@ -429,17 +429,20 @@ int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int6
 
 /* Plain streaming read, for measurement: reads `bytes` bytes at src
  * (16-byte aligned, bytes a multiple of 16) with 128-bit non-temporal loads,
- * one shot.  Workgroup w (256 threads) reads bytes [w*4096*L, (w+1)*4096*L),
- * L = loads_per_lane (4, 8 or 16), every lane issuing its L loads before it
- * uses any, and writes the XOR of all 32-bit words it read to sink[w]
- * (sink_words >= ceil(bytes / (4096*L)); zero padding past `bytes`).  It
- * does no other work: its time over a buffer is what a read-only kernel of
- * this simple shape reaches, a reference for the compression kernels rather
- * than a bound on them.
+ * one shot.  Workgroup w (256 threads, four waves) reads bytes
+ * [w*4096*L, (w+1)*4096*L), L = loads_per_lane (2, 4, 8 or 16), every lane
+ * issuing its L loads before it uses any.  With fold != 0, wave v of
+ * workgroup w writes the XOR of all 32-bit words it read to sink[4w + v]
+ * (zero padding past `bytes`), for checking that every word was read; with
+ * fold == 0 the sink is practically never written (a lane stores only when
+ * its XOR equals one fixed constant), the form for timing.  sink_words >=
+ * 4*ceil(bytes / (4096*L)) either way.  It does no other work: its time over
+ * a buffer is what a read-only kernel of this simple shape reaches, a
+ * practical reference for the compression kernels.
  * Errors: KVC_ERR_SHAPE (size, alignment, sink too small),
  *         KVC_ERR_UNSUPPORTED (loads_per_lane), KVC_ERR_NULL, KVC_ERR_HIP. */
 int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
-                         int loads_per_lane, void* stream);
+                         int loads_per_lane, int fold, void* stream);
 
 /* Launches a kernel that does nothing, with `workgroups` workgroups of
  * `threads` threads (1..1024), for measuring the launch and dispatch floor

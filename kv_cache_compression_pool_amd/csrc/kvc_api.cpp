@@ -648,20 +648,20 @@ int kvc_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int6
 }
 
 int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
-                         int loads_per_lane, void* stream) {
+                         int loads_per_lane, int fold, void* stream) {
   const char* fn = "kvc_diag_stream_read";
   if (bytes < 0 || bytes % 16) return fail(KVC_ERR_SHAPE, "%s: bytes must be a multiple of 16", fn);
-  if (loads_per_lane != 4 && loads_per_lane != 8 && loads_per_lane != 16)
-    return fail(KVC_ERR_UNSUPPORTED, "%s: loads_per_lane %d (4, 8 or 16)", fn, loads_per_lane);
+  if (loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8 && loads_per_lane != 16)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: loads_per_lane %d (2, 4, 8 or 16)", fn, loads_per_lane);
   if (bytes == 0) return ok();
   if (!src || !sink) return fail(KVC_ERR_NULL, "%s: NULL pointer", fn);
   if (!aligned(src, 16) || !aligned(sink, 4)) return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
   const int64_t per_block = 4096LL * loads_per_lane;
   const int64_t blocks = (bytes + per_block - 1) / per_block;
   if (blocks > 0x7fffffffLL) return fail(KVC_ERR_SHAPE, "%s: buffer too large", fn);
-  if (sink_words < blocks)
-    return fail(KVC_ERR_SHAPE, "%s: sink needs %lld words", fn, (long long)blocks);
-  return hip_status(kvc::launch_diag_stream_read(src, bytes, sink, loads_per_lane,
+  if (sink_words < 4 * blocks)
+    return fail(KVC_ERR_SHAPE, "%s: sink needs %lld words", fn, (long long)(4 * blocks));
+  return hip_status(kvc::launch_diag_stream_read(src, bytes, sink, loads_per_lane, fold != 0,
                                                  (hipStream_t)stream),
                     "kvc_diag_stream_read launch");
 }

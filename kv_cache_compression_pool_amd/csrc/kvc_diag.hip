@@ -28,13 +28,16 @@ __global__ __launch_bounds__(256) void diag_convert_kernel(const float* __restri
   }
 }
 
-// Plain streaming read, one shot: workgroup w reads the 16-byte words
-// [w*256*L, (w+1)*256*L), load u of thread i taking word w*256*L + u*256 + i,
-// so each wave-wide load covers 1 KB of consecutive bytes and every lane
-// issues its L non-temporal loads before it uses any of them.  The words are
-// XOR-folded over the workgroup and the result is written to sink[w]; the
-// fold keeps the loads alive and lets a test check that every word was read.
-template <int L>
+// Plain streaming read, one shot: workgroup w (256 threads) reads the 16-byte
+// words [w*256*L, (w+1)*256*L), load u of thread i taking word w*256*L + u*256
+// + i, so each wave-wide load covers 1 KB of consecutive bytes and every lane
+// issues its L non-temporal loads before it uses any of them.
+// kFold: each wave XOR-folds the words it read across its lanes (DPP and
+// permlane swaps, no LDS, no barrier) and lane 0 writes the result to
+// sink[4w + wave], so a test can check that every word was read.  Without
+// it, a lane stores its XOR only when it equals a constant (practically
+// never), which keeps the loads alive at no cost: the measurement form.
+template <int L, bool kFold>
 __global__ __launch_bounds__(256) void diag_stream_read_kernel(const u32x4_t* __restrict__ p,
                                                                int64_t n16,
                                                                uint32_t* __restrict__ sink) {
@@ -48,12 +51,18 @@ __global__ __launch_bounds__(256) void diag_stream_read_kernel(const u32x4_t* __
   uint32_t acc = 0;
 #pragma unroll
   for (int u = 0; u < L; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
-  __shared__ uint32_t s_fold[4];
-  if ((threadIdx.x & 63) == 0) s_fold[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) sink[blockIdx.x] = s_fold[0] ^ s_fold[1] ^ s_fold[2] ^ s_fold[3];
+  if constexpr (!kFold) {
+    if (acc == 0x9e3779b9u) sink[4 * (int64_t)blockIdx.x + (threadIdx.x >> 6)] = acc;
+    return;
+  }
+  float a = __uint_as_float(acc);
+  a = __uint_as_float(acc ^ __float_as_uint(row_xor<1>(a)));
+  a = __uint_as_float(__float_as_uint(a) ^ __float_as_uint(row_xor<2>(a)));
+  a = __uint_as_float(__float_as_uint(a) ^ __float_as_uint(row_xor<4>(a)));
+  a = __uint_as_float(__float_as_uint(a) ^ __float_as_uint(row_xor<8>(a)));
+  a = __uint_as_float(__float_as_uint(a) ^ __float_as_uint(xor_rows16(a, (threadIdx.x >> 4) & 1)));
+  a = __uint_as_float(__float_as_uint(a) ^ __float_as_uint(xor_rows32(a, (threadIdx.x >> 5) & 1)));
+  if ((threadIdx.x & 63) == 0) sink[4 * (int64_t)blockIdx.x + (threadIdx.x >> 6)] = __float_as_uint(a);
 }
 
 // A kernel that does nothing: its launch-to-launch time with a given grid is
@@ -71,22 +80,27 @@ hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8
 }
 
 hipError_t launch_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink,
-                                   int loads_per_lane, hipStream_t stream) {
+                                   int loads_per_lane, bool fold, hipStream_t stream) {
   const int64_t n16 = bytes / 16;
   const int64_t per_block = 256LL * loads_per_lane;
   const dim3 grid((unsigned)((n16 + per_block - 1) / per_block));
   const u32x4_t* p = reinterpret_cast<const u32x4_t*>(src);
+#define KVC_READ(LL)                                                                       \
+  do {                                                                                     \
+    if (fold)                                                                              \
+      hipLaunchKernelGGL((diag_stream_read_kernel<LL, true>), grid, dim3(256), 0, stream, p, \
+                         n16, sink);                                                       \
+    else                                                                                   \
+      hipLaunchKernelGGL((diag_stream_read_kernel<LL, false>), grid, dim3(256), 0, stream,  \
+                         p, n16, sink);                                                    \
+  } while (0)
   switch (loads_per_lane) {
-    case 4:
-      hipLaunchKernelGGL(diag_stream_read_kernel<4>, grid, dim3(256), 0, stream, p, n16, sink);
-      break;
-    case 8:
-      hipLaunchKernelGGL(diag_stream_read_kernel<8>, grid, dim3(256), 0, stream, p, n16, sink);
-      break;
-    default:
-      hipLaunchKernelGGL(diag_stream_read_kernel<16>, grid, dim3(256), 0, stream, p, n16, sink);
-      break;
+    case 2: KVC_READ(2); break;
+    case 4: KVC_READ(4); break;
+    case 8: KVC_READ(8); break;
+    default: KVC_READ(16); break;
   }
+#undef KVC_READ
   return hipGetLastError();
 }
 

@@ -68,9 +68,10 @@ hipError_t launch_c128_prefill_fused(float* state, int64_t num_slots, const floa
 hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8_out, int64_t n,
                                hipStream_t stream);
 
-// loads_per_lane is 4, 8 or 16; sink needs ceil(bytes / (4096 * loads_per_lane)) words.
+// loads_per_lane is 2, 4, 8 or 16; sink needs 4 * ceil(bytes / (4096 * loads_per_lane))
+// words (one per wave).
 hipError_t launch_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink,
-                                   int loads_per_lane, hipStream_t stream);
+                                   int loads_per_lane, bool fold, hipStream_t stream);
 hipError_t launch_diag_empty(int64_t workgroups, int threads, hipStream_t stream);
 
 }  // namespace kvc

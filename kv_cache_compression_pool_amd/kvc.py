@@ -94,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.kvc_c128_online_prefill_fused.argtypes = [_p, _i64, _p, _p, _p, _p, _i32, _i64, _p, _p,
                                                     _p, _i64, _p, _u32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
-        L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _i32, _p]
+        L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _i32, _i32, _p]
         L.kvc_diag_empty_launch.argtypes = [_i64, _i32, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
@@ -151,7 +151,10 @@ def prepare(entry_point, *args, **kwargs):
     """Validate and marshal the arguments of a device entry point of this
     module once; returns a PreparedCall that launches it.  The buffers must
     stay the same tensors with the same shapes (the call keeps references to
-    them); their contents may change between calls.  Example:
+    them); their contents may change between calls.  A stream given here is
+    used by every call, also under HIP-graph capture; without one each call
+    launches on torch's current stream (the capture stream while capturing).
+    Example:
         launch = kvc.prepare(kvc.kvc_compress_prefill, keys, scores, ape, rows,
                              n_pools, out, scale, True)
         launch()            # on torch's current stream
@@ -636,20 +639,21 @@ def kvc_diag_convert(x, bf16_out=None, fp8_out=None, stream=None):
 
 
 def stream_read_sink_words(nbytes: int, loads_per_lane: int) -> int:
-    """Sink words kvc_diag_stream_read needs: one per 256-thread workgroup."""
-    return -(-int(nbytes) // (4096 * int(loads_per_lane)))
+    """Sink words kvc_diag_stream_read needs: one per wave."""
+    return 4 * -(-int(nbytes) // (4096 * int(loads_per_lane)))
 
 
-def kvc_diag_stream_read(src, sink, loads_per_lane: int = 8, stream=None):
+def kvc_diag_stream_read(src, sink, loads_per_lane: int = 4, fold: bool = False, stream=None):
     """Plain streaming read of a device tensor's bytes (see kvc.h); sink is a
-    device int32/uint32 tensor of at least stream_read_sink_words() entries."""
+    device int32/uint32 tensor of at least stream_read_sink_words() entries;
+    fold=True writes each wave's XOR of the words it read to the sink."""
     nbytes = src.numel() * src.element_size()
     nbytes -= nbytes % 16
     _need(src.is_cuda and src.is_contiguous(), "src must be a contiguous device tensor")
     _need(sink.is_cuda and sink.element_size() == 4 and sink.is_contiguous(),
           "sink must be a contiguous device tensor of 4-byte words")
     return _invoke("kvc_diag_stream_read", (src.data_ptr(), nbytes, sink.data_ptr(), sink.numel(),
-                                      int(loads_per_lane)), stream)
+                                            int(loads_per_lane), int(bool(fold))), stream)
 
 
 def kvc_diag_empty_launch(workgroups: int, threads: int, stream=None):

@@ -243,13 +243,13 @@ def test_device_entry_points_validate_before_launch():
     assert b"even" in L.kvc_last_error()
     # streaming read: size, load count, sink size; empty launch: grid checks
     sr = L.kvc_diag_stream_read
-    assert sr(p, 40, p, 8, 8, None) == kvc.KVC_ERR_SHAPE
-    assert sr(p, 4096, p, 8, 6, None) == kvc.KVC_ERR_UNSUPPORTED
-    assert sr(p, 0, None, 0, 8, None) == kvc.KVC_OK
-    assert sr(p, 3 * 4096 * 8, p, 2, 8, None) == kvc.KVC_ERR_SHAPE
-    assert b"sink needs 3 words" in L.kvc_last_error()
-    assert sr(ctypes.c_void_p(0x1008), 4096, p, 8, 8, None) == kvc.KVC_ERR_SHAPE
-    assert kvc.stream_read_sink_words(3 * 4096 * 8 + 16, 8) == 4
+    assert sr(p, 40, p, 8, 8, 1, None) == kvc.KVC_ERR_SHAPE
+    assert sr(p, 4096, p, 8, 6, 1, None) == kvc.KVC_ERR_UNSUPPORTED
+    assert sr(p, 0, None, 0, 8, 0, None) == kvc.KVC_OK
+    assert sr(p, 3 * 4096 * 8, p, 11, 8, 0, None) == kvc.KVC_ERR_SHAPE
+    assert b"sink needs 12 words" in L.kvc_last_error()
+    assert sr(ctypes.c_void_p(0x1008), 4096, p, 8, 8, 1, None) == kvc.KVC_ERR_SHAPE
+    assert kvc.stream_read_sink_words(3 * 4096 * 8 + 16, 8) == 16
     assert L.kvc_diag_empty_launch(4, 0, None) == kvc.KVC_ERR_SHAPE
     assert L.kvc_diag_empty_launch(4, 1025, None) == kvc.KVC_ERR_SHAPE
     assert L.kvc_diag_empty_launch(-1, 64, None) == kvc.KVC_ERR_SHAPE

@@ -1013,21 +1013,26 @@ def test_c128_prefill_quant_epilogue():
     note(f"c128 prefill quant: {r.sum()} vectors, bf16-boundary vectors {flips}")
 
 
-@pytest.mark.parametrize("loads", [4, 8, 16])
+@pytest.mark.parametrize("loads", [2, 4, 8, 16])
 def test_diag_stream_read_reads_every_word(loads):
     g = np.random.default_rng(30 + loads)
     words = g.integers(0, 2**32, size=(3 * 4096 * loads + 4 * 37), dtype=np.uint64).astype(np.uint32)
     src = dev(words.view(np.int32))
     nw = kvc.kvc.stream_read_sink_words(words.size * 4, loads)
     sink = torch.full((nw + 3,), 7, dtype=torch.int32, device="cuda")
-    kvc.kvc.kvc_diag_stream_read(src, sink, loads)
+    kvc.kvc.kvc_diag_stream_read(src, sink, loads, fold=False)   # the timing form: no stores
     torch.cuda.synchronize()
-    per_block = 1024 * loads                      # 32-bit words per workgroup
-    padded = np.zeros(nw * per_block, np.uint32)
+    assert torch.all(sink == 7)
+    kvc.kvc.kvc_diag_stream_read(src, sink, loads, fold=True)
+    torch.cuda.synchronize()
+    blocks = nw // 4
+    padded = np.zeros(blocks * 1024 * loads, np.uint32)
     padded[:words.size] = words
-    exp = np.bitwise_xor.reduce(padded.reshape(nw, per_block), axis=1)
+    # [workgroup, load u, wave, lane, word]: a wave's words of every load
+    w5 = padded.reshape(blocks, loads, 4, 64, 4)
+    exp = np.bitwise_xor.reduce(w5.transpose(0, 2, 1, 3, 4).reshape(blocks, 4, -1), axis=2)
     got = sink.cpu().numpy().view(np.uint32)
-    assert np.array_equal(got[:nw], exp)
+    assert np.array_equal(got[:nw], exp.ravel())
     assert np.all(got[nw:] == 7)
 
 
@@ -1075,6 +1080,24 @@ def test_prepared_calls_equal_direct_calls():
         step()
     torch.cuda.synchronize()
     assert torch.equal(st1.view(torch.int32), st2.view(torch.int32))   # NaN in unused slots
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32))
+    # captured in a HIP graph (no fixed stream: it launches on the capture
+    # stream) and replayed: the same as two more direct calls
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                           # warm-up before capture
+    torch.cuda.current_stream().wait_stream(side)
+    kvc.kvc_c128_online_decode(st1, x, out1, ap, ix, sl)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(2):
+        g.replay()
+        kvc.kvc_c128_online_decode(st1, x, out1, ap, ix, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(st1.view(torch.int32), st2.view(torch.int32))
     assert torch.equal(out1.view(torch.int32), out2.view(torch.int32))
 
 
