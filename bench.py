@@ -185,11 +185,15 @@ def bench_pool16_prefill(args, torch, kvc, synth, stream):
 def launch_floor(torch, kvc, stream, workgroups, threads, steps=100, graph_calls=64):
     """Launch-to-launch time of an empty kernel with the given grid: back to
     back (behind the busy-wait, as every timed leg) and as one node of a
-    `graph_calls`-node HIP graph.  Returns (us per launch, us per graph node)."""
+    `graph_calls`-node HIP graph; and the host time of one prepared launch of
+    it (the runtime's own launch cost plus one ctypes call).  Returns (us per
+    launch, us per graph node, host us per prepared launch)."""
     def step(i):
         kvc.kvc.kvc_diag_empty_launch(workgroups, threads)
 
     _, ev, _ = timed(step, steps, 5, torch, stream)
+    call = kvc.prepare(kvc.kvc.kvc_diag_empty_launch, workgroups, threads, stream=stream)
+    _, _, host = timed(lambda i: call(), steps, 5, torch, stream)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for _ in range(graph_calls):
@@ -198,7 +202,7 @@ def launch_floor(torch, kvc, stream, workgroups, threads, steps=100, graph_calls
     _, evg, _ = timed(lambda i: g.replay(), max(steps // 10, 8), 2, torch, stream,
                       host_us_per_call=100.0)
     del g
-    return ev * 1e3, evg / graph_calls * 1e3
+    return ev * 1e3, evg / graph_calls * 1e3, host * 1e6
 
 
 # ------------------------------------------------------------------ pool-128 decode
@@ -933,10 +937,10 @@ def main():
                 "hbm_gbs": round(gg, 1), "hbm_frac": round(gg / PEAK_HBM_GBS, 4)}
         # an empty kernel with the single call's grid (two requests per
         # 64-thread workgroup), back to back and inside a 64-node graph
-        fl, flg = launch_floor(torch, kvc, stream, (c4["batch"] + 1) // 2, 64)
+        fl, flg, flh = launch_floor(torch, kvc, stream, (c4["batch"] + 1) // 2, 64)
         line["c128_decode"]["launch_floor_us"] = {
             "grid": f"{(c4['batch'] + 1) // 2} x 64 threads", "single": round(fl, 3),
-            "graph_64_calls_per_call": round(flg, 3),
+            "graph_64_calls_per_call": round(flg, 3), "host_prepared": round(flh, 2),
             "us_at_60pct_of_peak": round(c4["alg_bytes"] / (0.6 * PEAK_HBM_GBS * 1e3), 3)}
         line["c128_decode"]["target_basis"] = (
             "The 60% HBM target is judged on multi_layer: the same 1024 requests decoding one "
@@ -981,10 +985,10 @@ def main():
             "launch_us": round(c3["ev_ms"] * 1e3, 3), "bytes_per_launch": c3["alg_bytes"],
             "hbm_gbs": round(g3, 1), "hbm_frac": round(g3 / PEAK_HBM_GBS, 4),
             "host_launch_us": round(c3["host_s"] * 1e6, 2)}
-        fl, flg = launch_floor(torch, kvc, stream, (c3["requests"] + 3) // 4, 256)
+        fl, flg, flh = launch_floor(torch, kvc, stream, (c3["requests"] + 3) // 4, 256)
         line["ring_decode"]["launch_floor_us"] = {
             "grid": f"{(c3['requests'] + 3) // 4} x 256 threads", "single": round(fl, 3),
-            "graph_64_calls_per_call": round(flg, 3)}
+            "graph_64_calls_per_call": round(flg, 3), "host_prepared": round(flh, 2)}
         if "graph" in c3:
             cg = c3["graph"]
             gg = gbs(c3["alg_bytes"], cg["call_ms"])

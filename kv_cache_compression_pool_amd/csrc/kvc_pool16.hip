@@ -60,6 +60,11 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Streaming 128-bit store (non-temporal: the line is not kept in the caches).
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  __builtin_nontemporal_store((u32x4_t){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 // The same load through a buffer resource: the base address sits in scalar
 // registers and each lane adds a 32-bit byte offset, which spares the 64-bit
 // address arithmetic of the prefill's 16 row loads per lane (measured: 73.7%
@@ -537,6 +542,10 @@ struct RingLayers {
 //    ring rows, so waves that only stash never read it and no barrier sits in
 //    the chain; multi-layer launches stage ape in LDS once per workgroup,
 //    because those registers would cost occupancy there.
+//  * Multi-layer launches (kParkTokens with kMaxN <= 8) store the stashes and
+//    read the ring rows with non-temporal accesses: 64 layers of 256 x 4
+//    19.8-19.9 -> 18.3-18.4 us, bit-identical.  Single calls keep cached
+//    accesses (non-temporal ones made 256 x 4 4.21 -> 4.38 us per call).
 //  * kParkTokens (multi-layer launches, and windows of more than 8 tokens):
 //    the token rows are parked in LDS after loading (the wave's four rows
 //    share the loads) instead of staying in registers through the completion
@@ -559,6 +568,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   }
   static_assert(kMaxN <= 32, "completion mask is 32 bits");
   constexpr int kReqPerBlock = kBlock / 64;
+  constexpr bool kStreamRing = kParkTokens && kMaxN <= 8;   // multi-layer launches
   const int c = threadIdx.x & 15;
   const int q = (threadIdx.x >> 4) & 3;
   // The request index is made wave-uniform for the 4- and 8-token instances:
@@ -676,8 +686,15 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
         if (mask & (1u << t)) {
           uint16_t* ring_k = ring + (int64_t)blk[t] * (2 * kPool * 128);
           const int slot = pos[t] & (kPool - 1);
-          reinterpret_cast<uint4*>(ring_k + slot * 128)[c] = tok_key(t);
-          reinterpret_cast<uint4*>(ring_k + kPool * 128 + slot * 128)[c] = tok_score(t);
+          uint4* dk = reinterpret_cast<uint4*>(ring_k + slot * 128) + c;
+          uint4* ds = reinterpret_cast<uint4*>(ring_k + kPool * 128 + slot * 128) + c;
+          if constexpr (kStreamRing) {
+            store_stream(dk, tok_key(t));
+            store_stream(ds, tok_score(t));
+          } else {
+            *dk = tok_key(t);
+            *ds = tok_score(t);
+          }
         }
       }
     };
@@ -715,8 +732,10 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int slot = 4 * q + i;
-        S[i] = reinterpret_cast<const uint4*>(ring_s + slot * 128)[c];
-        K[i] = reinterpret_cast<const uint4*>(ring_k + slot * 128)[c];
+        const uint4* rs = reinterpret_cast<const uint4*>(ring_s + slot * 128) + c;
+        const uint4* rk = reinterpret_cast<const uint4*>(ring_k + slot * 128) + c;
+        S[i] = kStreamRing ? load_stream(rs) : *rs;
+        K[i] = kStreamRing ? load_stream(rk) : *rk;
         if constexpr (!kParkTokens) {
           const float4* ap = reinterpret_cast<const float4*>(ape) + slot * 32 + 2 * c;
           A[i][0] = ap[0];

@@ -129,19 +129,28 @@ class PreparedCall:
 
     def __init__(self, name, args, stream):
         self.name = name
-        self._fn = getattr(lib(), name)
-        # converted to ctypes values once (the call then only passes them)
-        self._args = tuple(None if a is None else t(a)
-                           for t, a in zip(self._fn.argtypes, args))
+        fn = getattr(lib(), name)
+        # converted to ctypes values once (NULL stays None) ...
+        self._args = tuple(None if a is None else t(a) for t, a in zip(fn.argtypes, args))
+        # ... and passed through a pointer to the same function that has no
+        # argtypes, so ctypes takes them as they are instead of converting
+        # each one again on every call (about 0.3 us of a ~1 us ctypes call).
+        # Every value it gets is a ctypes instance or None, so each keeps its
+        # declared C type.
+        self._fn = ctypes.cast(fn, ctypes.CFUNCTYPE(fn.restype))
+        self._fn.argtypes = None
         # a stream given at preparation is kept; None means torch's current
         # stream at each call
-        self._stream = None if stream is None else _stream(stream)
+        self._stream = None if stream is None else ctypes.c_void_p(_stream(stream))
         self._keep = None
 
     def __call__(self, stream=None):
-        s = self._stream if stream is None else _stream(stream)
-        if s is None:
-            s = _current_stream()
+        if stream is not None:
+            s = ctypes.c_void_p(_stream(stream))
+        elif self._stream is not None:
+            s = self._stream
+        else:
+            s = ctypes.c_void_p(_current_stream())
         rc = self._fn(*self._args, s)
         if rc != KVC_OK:
             _check(rc)

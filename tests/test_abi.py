@@ -307,3 +307,27 @@ def test_prepare_accepts_device_entry_points_only():
     with pytest.raises(TypeError):
         kvc.prepare(kvc.kvc_plan_pool_prefill, np.array([32], np.int64))
     assert callable(kvc.PreparedCall.__call__)
+
+
+def test_prepared_call_passes_64_bit_values_and_null():
+    """A PreparedCall hands its pre-converted values to the C function as
+    their declared C types (no GPU work: each call stops at host validation).
+    A 64-bit size whose low 32 bits are zero, a pointer above 4 GiB and a
+    NULL each reach the library intact, or the error named would differ."""
+    fn = "kvc_c128_online_decode_layers"
+    hi = 1 << 32                                    # 16-byte aligned, above 4 GiB
+    ptrs = dict(state=hi, kv=hi + 0x1000, out=hi + 0x2000, ape=hi + 0x3000,
+                idx=hi + 0x4000, sl=hi + 0x5000)
+
+    def call(state, num_slots, batch, num_layers, out):
+        # state, state_ls, num_slots, in, in_ls, out, out_ls, ape, ape_ls, indices, seq_lens,
+        # batch, num_layers (the stream is the call's own, here the null stream)
+        return kvc.PreparedCall(fn, (state, 0, num_slots, ptrs["kv"], 0, out, 0, ptrs["ape"], 0,
+                                     ptrs["idx"], ptrs["sl"], batch, num_layers), 0)
+
+    with pytest.raises(kvc.KvcError, match="negative size"):
+        call(ptrs["state"], 8, -(1 << 40), 1, ptrs["out"])()   # low 32 bits are 0
+    with pytest.raises(kvc.KvcError, match="NULL pointer"):
+        call(None, 8, 1, 1, ptrs["out"])()
+    with pytest.raises(kvc.KvcError, match="num_layers exceeds 65535"):
+        call(ptrs["state"], 8, 1, 70000, ptrs["out"])()       # out truncated would be NULL
