@@ -100,14 +100,19 @@ def timed(fn, steps, warmup, torch, stream, host_us_per_call=60.0):
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    # host cost: the median over 9 batches of up to 20 launches, each batch
+    # timed from the host alone (the device runs the launches asynchronously;
+    # 20 launches do not fill the queue, so the host never waits for the
+    # device here)
     n_host = min(steps, 20)
-    t0 = time.perf_counter()
-    for i in range(n_host):
-        fn(warmup + i)
-    # launches only: the device runs them asynchronously (20 launches do not
-    # fill the queue, so the host never waits for the device here)
-    host = (time.perf_counter() - t0) / n_host
-    torch.cuda.synchronize()
+    batches = []
+    for k in range(9):
+        t0 = time.perf_counter()
+        for i in range(n_host):
+            fn(warmup + k * n_host + i)
+        batches.append((time.perf_counter() - t0) / n_host)
+        torch.cuda.synchronize()
+    host = sorted(batches)[len(batches) // 2]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     _hold_queue(torch, stream, ms=steps * host_us_per_call / 1e3 + 2.0)
@@ -248,9 +253,14 @@ def bench_c128_decode(args, torch, kvc, synth, stream):
         kvc.kvc_c128_online_decode(states[r], ins[r], outs[r], ape, idx, sl_t)
 
     _, _, host_unprepared = timed(step_unprepared, 20, 2, torch, stream)
+    # the binding's own share: the same prepared call with an empty batch,
+    # which returns after the argument checks without launching anything
+    empty = kvc.prepare(kvc.kvc_c128_online_decode, states[0], ins[0][:0], outs[0][:0], ape,
+                        idx[:0], sl_t[:0], stream=stream)
+    _, _, host_binding = timed(lambda i: empty(), 20, 2, torch, stream)
     res = dict(batch=B, emitted=int((c == 127).sum()), replicas=R, total_ms=total_ms,
                steps=steps, ev_ms=ev_ms, host_s=host, host_unprepared_s=host_unprepared,
-               alg_bytes=alg)
+               host_binding_s=host_binding, alg_bytes=alg)
 
     # Sustained single calls: 64 calls captured in one HIP graph, each graph
     # covering 64 of the state / input replicas, graphs replayed in turn.  The
@@ -928,7 +938,8 @@ def main():
             "hbm_gbs": round(g4, 1), "hbm_frac": round(g4 / PEAK_HBM_GBS, 4),
             "state_replicas": c4["replicas"],
             "host_launch_us": round(c4["host_s"] * 1e6, 2),
-            "host_launch_us_unprepared": round(c4["host_unprepared_s"] * 1e6, 2)}
+            "host_launch_us_unprepared": round(c4["host_unprepared_s"] * 1e6, 2),
+            "host_binding_us": round(c4["host_binding_s"] * 1e6, 2)}
         if "graph" in c4:
             cg = c4["graph"]
             gg = gbs(c4["alg_bytes"], cg["call_ms"])

@@ -87,14 +87,29 @@ __device__ __forceinline__ void store_stream4(float4* p, float4 v) {
   __builtin_nontemporal_store((f32x4_t){v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(p));
 }
 
-// One request per 32 lanes; blockIdx.y selects the layer (state, input,
-// output and ape advance by their layer strides; indices and lengths are
-// shared by all layers).
+// (group, layer) of a workgroup in a multi-layer launch whose layer count is
+// a multiple of 8, laid out XCD-major.  Workgroups go to the eight XCDs round
+// robin in dispatch order (blockIdx.x fastest), so workgroup number n runs on
+// XCD n % 8; it is given layer (n % 8) + 8 * ((n / 8) / G) and group
+// (n / 8) % G (G = gridDim.x), a one-to-one map under which each XCD runs
+// every group of its own layers and each layer's ape table is fetched into
+// one XCD's L2 instead of all eight.
+__device__ __forceinline__ void xcd_major_group_layer(uint32_t& group, uint32_t& layer) {
+  const uint32_t G = gridDim.x, n = blockIdx.x + blockIdx.y * G;
+  const uint32_t j = n >> 3;
+  layer = (n & 7u) + 8u * (j / G);
+  group = j % G;
+}
+
+// One request per 32 lanes; the workgroup handles requests group * kReq ..
+// group * kReq + kReq - 1 of one layer (state, input, output and ape advance
+// by their layer strides; indices and lengths are shared by all layers).
 template <bool kQuant, int kReq>
-__global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
+__device__ __forceinline__ void c128_decode_group(
     float* __restrict__ state, int64_t state_ls, int64_t num_slots, const float* __restrict__ in,
-    int64_t in_ls, EmitSink o, const float* __restrict__ ape, int64_t ape_ls,
-    const int32_t* __restrict__ indices, const int32_t* __restrict__ seq_lens, int64_t batch) {
+    int64_t in_ls, const EmitSink& o, const float* __restrict__ ape, int64_t ape_ls,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ seq_lens, int64_t batch,
+    uint32_t group, int64_t layer) {
   static_assert(kReq == 1 || kReq % 2 == 0, "a wave holds two whole requests");
   // Single calls: take every kernel argument into SGPRs at entry.  Left to
   // itself the compiler loads arguments next to their first use, behind the
@@ -108,8 +123,7 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
     asm volatile("" ::"s"(state), "s"(state_ls), "s"(num_slots), "s"(in), "s"(in_ls), "s"(ape),
                  "s"(ape_ls), "s"(indices), "s"(seq_lens), "s"(batch), "s"(o.out), "s"(o.codes),
                  "s"(o.scales));
-  const int64_t layer = blockIdx.y;
-  const int64_t b = (int64_t)blockIdx.x * kReq + (threadIdx.x >> 5);
+  const int64_t b = (int64_t)group * kReq + (threadIdx.x >> 5);
   const int q = threadIdx.x & 31;                       // channels 4q..4q+3
   // Two round trips.  Each issues its loads together (the empty asm
   // statements take all their values at once; without them the compiler had
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
     // vector loads instead of four (64 layers 44.32-44.40 -> 44.11-44.22 us).
     // The asm statement comes after the slot loads, which keeps them scalar.
     const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int64_t b0 = (int64_t)blockIdx.x * kReq + 2 * v;
+    const int64_t b0 = (int64_t)group * kReq + 2 * v;
     const int64_t c0 = b0 < batch ? b0 : batch - 1, c1 = b0 + 1 < batch ? b0 + 1 : batch - 1;
     int32_t i0 = indices[c0], l0 = seq_lens[c0], i1 = indices[c1], l1 = seq_lens[c1];
     asm volatile("" ::"s"(state), "s"(state_ls), "s"(num_slots), "s"(in), "s"(in_ls), "s"(ape),
@@ -203,6 +217,39 @@ __global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
     store_stream4(st + 32 + q, make_float4(S[0], S[1], S[2], S[3]));
     store_stream4(st + 64 + q, make_float4(K[0], K[1], K[2], K[3]));
   }
+}
+
+// Multi-layer launches (and single calls whose sizes exceed 32 bits): grid
+// (request groups, layers).  With a multiple of 8 layers the workgroups run
+// XCD-major (64 layers: 42.8 -> 40.0 us, bit-identical); otherwise workgroup
+// (x, y) is group x of layer y.
+template <bool kQuant, int kReq>
+__global__ __launch_bounds__(32 * kReq) void c128_decode_kernel(
+    float* __restrict__ state, int64_t state_ls, int64_t num_slots, const float* __restrict__ in,
+    int64_t in_ls, EmitSink o, const float* __restrict__ ape, int64_t ape_ls,
+    const int32_t* __restrict__ indices, const int32_t* __restrict__ seq_lens, int64_t batch) {
+  uint32_t group = blockIdx.x, layer = blockIdx.y;
+  if (kReq > 2 && (gridDim.y & 7u) == 0) xcd_major_group_layer(group, layer);
+  c128_decode_group<kQuant, kReq>(state, state_ls, num_slots, in, in_ls, o, ape, ape_ls, indices,
+                                  seq_lens, batch, group, layer);
+}
+
+// Single calls with a compact argument block (72 bytes instead of the 136 of
+// the general kernel; out0 is the fp32 output or, quantised, the codes).  The
+// runtime's host-side cost of a launch grows with the kernel's argument
+// block, by about 1 us between 96 and 120 bytes, and this call is short
+// enough on the device (about 3 us) for that to matter.
+template <bool kQuant>
+__global__ __launch_bounds__(32 * kDecodeReqSingle) void c128_decode_one_kernel(
+    float* __restrict__ state, const float* __restrict__ in, void* __restrict__ out0,
+    float* __restrict__ scales, const float* __restrict__ ape, const int32_t* __restrict__ indices,
+    const int32_t* __restrict__ seq_lens, uint32_t num_slots, uint32_t batch,
+    uint32_t round_scale) {
+  const EmitSink o{kQuant ? nullptr : static_cast<float*>(out0),
+                   kQuant ? static_cast<uint8_t*>(out0) : nullptr, scales, 0, 0, 0,
+                   round_scale != 0};
+  c128_decode_group<kQuant, kDecodeReqSingle>(state, 0, num_slots, in, 0, o, ape, 0, indices,
+                                              seq_lens, batch, blockIdx.x, 0);
 }
 
 // ------------------------------------------------------------------ prefill
@@ -461,6 +508,16 @@ hipError_t launch_c128_decode(float* state, int64_t state_ls, int64_t num_slots,
   if (num_layers > 1) {
     if (codes) KVC_DECODE(true, kDecodeReqLayers);
     else KVC_DECODE(false, kDecodeReqLayers);
+  } else if (num_slots <= 0xFFFFFFFFLL && batch <= 0xFFFFFFFFLL) {
+    const dim3 grid((unsigned)((batch + kDecodeReqSingle - 1) / kDecodeReqSingle));
+    if (codes)
+      hipLaunchKernelGGL((c128_decode_one_kernel<true>), grid, dim3(32 * kDecodeReqSingle), 0,
+                         stream, state, in, static_cast<void*>(codes), scales, ape, indices,
+                         seq_lens, (uint32_t)num_slots, (uint32_t)batch, (uint32_t)round_scale);
+    else
+      hipLaunchKernelGGL((c128_decode_one_kernel<false>), grid, dim3(32 * kDecodeReqSingle), 0,
+                         stream, state, in, static_cast<void*>(out), scales, ape, indices,
+                         seq_lens, (uint32_t)num_slots, (uint32_t)batch, (uint32_t)round_scale);
   } else {
     if (codes) KVC_DECODE(true, kDecodeReqSingle);
     else KVC_DECODE(false, kDecodeReqSingle);

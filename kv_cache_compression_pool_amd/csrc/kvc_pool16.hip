@@ -550,22 +550,16 @@ struct RingLayers {
 //    the token rows are parked in LDS after loading (the wave's four rows
 //    share the loads) instead of staying in registers through the completion
 //    path: about 30 fewer VGPRs, for an LDS round trip on the critical path.
+//  * The workgroup handles requests group * 4 .. group * 4 + 3 of one layer;
+//    the kernels below choose the group and offset the pointers to the layer.
 template <bool kRoundScale, int kMaxN, bool kParkTokens>
-__global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
+__device__ __forceinline__ void ring_decode_group(
     uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
     const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
     const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
     const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
     const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink,
-    RingLayers ls) {
-  {
-    const int64_t layer = blockIdx.y;
-    ring += layer * ls.ring;
-    key += layer * ls.key;
-    score += layer * ls.score;
-    ape += layer * ls.ape;
-    sink = sink.advanced(layer * ls.out_rows);
-  }
+    int64_t group) {
   static_assert(kMaxN <= 32, "completion mask is 32 bits");
   constexpr int kReqPerBlock = kBlock / 64;
   constexpr bool kStreamRing = kParkTokens && kMaxN <= 8;   // multi-layer launches
@@ -579,14 +573,7 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   // 48 scalar map loads measured 25-30% slower there.
   const int wave_in_block = kMaxN <= 8 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))
                                        : (int)(threadIdx.x >> 6);
-  // Multi-layer launches: workgroup x of layer y takes request group
-  // (x + y) mod gridDim.x; one layer: the identity.  Workgroups go to the
-  // eight XCDs round robin in launch order, and the token maps are shared by
-  // all layers, so without the rotation the XCD that holds a group's
-  // completing requests would get them again in every layer, and the
-  // busiest XCD would set the launch time (64 layers of 256 x 4: 24.9 us
-  // without, 20.4 us with, bit-identical).
-  const int64_t r = (((int64_t)blockIdx.x + blockIdx.y) % gridDim.x) * kReqPerBlock + wave_in_block;
+  const int64_t r = group * kReqPerBlock + wave_in_block;
   const int64_t rr = r < num_requests ? r : 0;   // waves past the batch read request 0, stop below
 
   __shared__ uint4 s_tok[kParkTokens ? kReqPerBlock : 1][kParkTokens ? kMaxN : 1][2][16];
@@ -781,6 +768,50 @@ __global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
   }
 }
 
+// Multi-layer launches (blockIdx.y = layer), and single calls whose sizes do
+// not fit the compact form below.  Workgroup x of layer y takes request group
+// (x + y) mod gridDim.x.  Workgroups go to the eight XCDs round robin in
+// launch order, and the token maps are shared by all layers, so without the
+// rotation the XCD that holds a group's completing requests would get them
+// again in every layer, and the busiest XCD would set the launch time (64
+// layers of 256 x 4: 24.9 us without, 20.4 us with, bit-identical).
+template <bool kRoundScale, int kMaxN, bool kParkTokens>
+__global__ __launch_bounds__(kBlock) void pool16_ring_wave_kernel(
+    uint16_t* ring, int64_t num_blocks, const int32_t* __restrict__ tail_slot,
+    const uint16_t* __restrict__ key, int64_t key_sb, int64_t key_st,
+    const uint16_t* __restrict__ score, int64_t score_sb, int64_t score_st,
+    const float* __restrict__ ape, const int32_t* __restrict__ slot_mapping,
+    const int32_t* __restrict__ positions, int64_t num_requests, int next_n, OutSink sink,
+    RingLayers ls) {
+  const int64_t layer = blockIdx.y;
+  ring_decode_group<kRoundScale, kMaxN, kParkTokens>(
+      ring + layer * ls.ring, num_blocks, tail_slot, key + layer * ls.key, key_sb, key_st,
+      score + layer * ls.score, score_sb, score_st, ape + layer * ls.ape, slot_mapping, positions,
+      num_requests, next_n, sink.advanced(layer * ls.out_rows),
+      ((int64_t)blockIdx.x + blockIdx.y) % gridDim.x);
+}
+
+// Single calls with a compact argument block: 112 bytes (32-bit sizes and
+// strides; the paged flag in bit 31 of next_n_paged) instead of 448 (the
+// general kernel's 192 plus the runtime's hidden arguments, which its use of
+// gridDim brings in).  The runtime's host-side cost of a launch grows with
+// the argument block, by about 1 us above 112 bytes and 1.5 us at 448, and a
+// single call takes about 4 us on the device.
+template <bool kRoundScale, int kMaxN, bool kParkTokens>
+__global__ __launch_bounds__(kBlock) void pool16_ring_one_kernel(
+    uint16_t* ring, const int32_t* __restrict__ tail_slot, const uint16_t* __restrict__ key,
+    const uint16_t* __restrict__ score, const float* __restrict__ ape,
+    const int32_t* __restrict__ slot_mapping, const int32_t* __restrict__ positions,
+    uint8_t* codes, float* scales, float* dbg, uint32_t num_blocks, uint32_t num_requests,
+    uint32_t next_n_paged, uint32_t rows, uint32_t key_sb, uint32_t key_st, uint32_t score_sb,
+    uint32_t score_st) {
+  const OutSink sink{codes, scales, (int64_t)rows, (next_n_paged >> 31) != 0u, dbg};
+  ring_decode_group<kRoundScale, kMaxN, kParkTokens>(
+      ring, num_blocks, tail_slot, key, key_sb, key_st, score, score_sb, score_st, ape,
+      slot_mapping, positions, num_requests, (int)(next_n_paged & 0x7FFFFFFFu), sink,
+      blockIdx.x);
+}
+
 // Tail-ring seeding.  Each lane decides for one token whether it is among its
 // request's last 16 (no token 16 positions later maps to the same ring
 // block); the wave then copies its few seeded tokens together, two per step,
@@ -911,32 +942,51 @@ hipError_t launch_pool16_ring(uint16_t* ring, int64_t num_blocks, const int32_t*
   const RingLayers ls{ring_ls, key_ls, score_ls, ape_ls, out_rows};
   constexpr int kWaveReq = kBlock / 64;
   dim3 grid((unsigned)((num_requests + kWaveReq - 1) / kWaveReq), (unsigned)num_layers);
-#define KVC_RING(KERNEL)                                                                      \
-  hipLaunchKernelGGL(KERNEL, grid, block, 0, stream, ring, num_blocks, tail_slot, key, key_sb, \
-                     key_st, score, score_sb, score_st, ape, slot_mapping, positions,           \
-                     num_requests, next_n, sink, ls)
+  constexpr int64_t kU32 = 0xFFFFFFFFLL;
+  const bool one = num_layers == 1 && num_blocks <= kU32 && num_requests <= kU32 &&
+                   out_rows <= kU32 && key_sb <= kU32 && key_st <= kU32 && score_sb <= kU32 &&
+                   score_st <= kU32;
+  const uint32_t next_n_paged = (uint32_t)next_n | (paged ? 0x80000000u : 0u);
+  // The kernel instance (round_scale, window, parking) and its argument form
+  // (the parked 4- and 8-token instances serve multi-layer launches only).
+#define KVC_RING(RS, N, PARK)                                                                  \
+  do {                                                                                         \
+    if constexpr (!PARK || N > 8) {                                                            \
+      if (one) {                                                                               \
+        hipLaunchKernelGGL((pool16_ring_one_kernel<RS, N, PARK>), grid, block, 0, stream, ring,  \
+                           tail_slot, key, score, ape, slot_mapping, positions, out_fp8,         \
+                           out_scale, dbg, (uint32_t)num_blocks, (uint32_t)num_requests,         \
+                           next_n_paged, (uint32_t)out_rows, (uint32_t)key_sb,                   \
+                           (uint32_t)key_st, (uint32_t)score_sb, (uint32_t)score_st);            \
+        break;                                                                                 \
+      }                                                                                        \
+    }                                                                                          \
+    hipLaunchKernelGGL((pool16_ring_wave_kernel<RS, N, PARK>), grid, block, 0, stream, ring,     \
+                       num_blocks, tail_slot, key, key_sb, key_st, score, score_sb, score_st,    \
+                       ape, slot_mapping, positions, num_requests, next_n, sink, ls);           \
+  } while (0)
   const bool park = num_layers > 1;
   if (next_n <= 4) {
     if (round_scale) {
-      if (park) KVC_RING((pool16_ring_wave_kernel<true, 4, true>));
-      else KVC_RING((pool16_ring_wave_kernel<true, 4, false>));
+      if (park) KVC_RING(true, 4, true);
+      else KVC_RING(true, 4, false);
     } else {
-      if (park) KVC_RING((pool16_ring_wave_kernel<false, 4, true>));
-      else KVC_RING((pool16_ring_wave_kernel<false, 4, false>));
+      if (park) KVC_RING(false, 4, true);
+      else KVC_RING(false, 4, false);
     }
   } else if (next_n <= 8) {
     if (round_scale) {
-      if (park) KVC_RING((pool16_ring_wave_kernel<true, 8, true>));
-      else KVC_RING((pool16_ring_wave_kernel<true, 8, false>));
+      if (park) KVC_RING(true, 8, true);
+      else KVC_RING(true, 8, false);
     } else {
-      if (park) KVC_RING((pool16_ring_wave_kernel<false, 8, true>));
-      else KVC_RING((pool16_ring_wave_kernel<false, 8, false>));
+      if (park) KVC_RING(false, 8, true);
+      else KVC_RING(false, 8, false);
     }
   } else {
     // 16 tokens' rows do not fit in registers: parked in LDS, and longer
     // verify batches run in windows of 16 tokens
-    if (round_scale) KVC_RING((pool16_ring_wave_kernel<true, 16, true>));
-    else KVC_RING((pool16_ring_wave_kernel<false, 16, true>));
+    if (round_scale) KVC_RING(true, 16, true);
+    else KVC_RING(false, 16, true);
   }
 #undef KVC_RING
   return hipGetLastError();

@@ -929,11 +929,14 @@ def _layer_case(seq_lens, indices, seed, num_slots=2048):
     return st, d["kv_score_in"], d["ape"]
 
 
-def test_c128_decode_layers_equal_separate_calls():
+@pytest.mark.parametrize("num_layers", [5, 16])
+def test_c128_decode_layers_equal_separate_calls(num_layers):
+    """5 layers: workgroup (x, y) is group x of layer y; 16 layers (a multiple
+    of 8): the XCD-major layout, here with 38 request groups per layer."""
     base = c128_decode_case(seed=3, batch=300, emit_frac=0.2)
     idx, sl = base["indices"], base["seq_lens"]
     layers = [(base["state"], base["kv_score_in"], base["ape"])]
-    layers += [_layer_case(sl, idx, seed=40 + l) for l in range(4)]
+    layers += [_layer_case(sl, idx, seed=40 + l) for l in range(num_layers - 1)]
     L = len(layers)
     note(f"c128 decode {L} layers x 300")
     st = np.stack([x[0] for x in layers])
