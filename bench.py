@@ -41,9 +41,6 @@ C128_PREFILL_TRAFFIC = os.path.join(ROOT, "profiles", "c128_prefill_32seq_single
 C128_DECODE_TRAFFIC = os.path.join(ROOT, "profiles", "c128_decode_64layers_traffic.json")
 RING_TRAFFIC = os.path.join(ROOT, "profiles", "ring_decode_64layers_traffic.json")
 KERNEL_SOURCES = ("kvc_pool16.hip", "kvc_device.hpp")
-# The pool-16 prefill launch runs one pool per wave up to this many pools and
-# two pools per wave (a second kernel) above it.
-PREFILL_WAVE_PER_POOL_MAX = 24576
 METRIC = ("compressed vectors/s + achieved HBM GB/s (% of peak), "
           "pool-16 prefill & c128 decode")
 
@@ -915,8 +912,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic() if args.prefill_seqs == 64 else None,
-                     "kernel": ("pool16_prefill_kernel" if p["n"] <= PREFILL_WAVE_PER_POOL_MAX
-                                else "pool16_prefill_pair_kernel"),
+                     "kernel": "pool16_prefill_kernel",
                      "bytes_per_launch": p["alg_bytes"],
                      "bytes_per_vector": p["bytes_per_vec"],
                      "launch_us": round(p["ev_ms"] * 1e3, 3),

@@ -19,14 +19,9 @@
 //     register, bits 1-2 across rows, bits 3-6 across the 16 lanes of a row
 //     (DPP); the absmax is a wave reduction; each lane stores 2 codes, so the
 //     128-byte code vector leaves as one coalesced store.
-//   * Batches of more than 24,576 pools run two pools per wave instead
-//     (pool16_prefill_pair_kernel): 32 lanes per pool, a 16-lane row per 8
-//     slots, 8 x 8 values per lane, the rows exchanging max and sums by
-//     ds_swizzle.  One pool per wave halves the arithmetic a wave runs after
-//     its last row arrives (a shorter drain at the end of a launch) and needs
-//     73 instead of 120 VGPRs; two pools per wave keep more bytes in flight
-//     per SIMD (64 KB at four waves against 48 KB at six), which wins on
-//     large batches.
+//   * One pool per wave at every batch size: a form with two pools per wave
+//     (32 lanes per pool, 120 VGPRs) measured within 2% of it, either way,
+//     from 31k to 257k pools, and slower below.
 //   * Slot rows are streamed with non-temporal loads, through buffer
 //     resources with 32-bit offsets when keys and scores each span less than
 //     4 GiB (64-bit global addresses otherwise); ape ([16,128] fp32) is
@@ -44,12 +39,7 @@ namespace {
 constexpr int kPool = 16;
 constexpr int kBlock = 256;                    // 4 waves per workgroup
 constexpr int kPoolsPerBlock = kBlock / 64;    // prefill, one pool per wave
-constexpr int kHalf = 8;                       // prefill, two pools per wave: slots per 16-lane row
-constexpr int kPairPoolsPerBlock = kBlock / 32;
 constexpr int kMinWavesPerEU = 4;              // caps VGPRs at 128
-// Ragged prefill batches of at most this many pools run one pool per wave;
-// larger ones two pools per wave (see launch_pool16_prefill).
-constexpr int64_t kWavePerPoolMaxPools = 24576;
 constexpr int64_t kPagedBytes = 132;           // page of one token: 128 codes + fp32 scale
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -104,55 +94,6 @@ __device__ __forceinline__ void store_ape(float4* s_ape, const ApeRegs& r) {
   s_ape[threadIdx.x] = r.a;
   s_ape[threadIdx.x + kBlock] = r.b;
   __syncthreads();
-}
-
-// Softmax-weighted mean of one pool, 32-lane layout.  S[i], K[i]: gate scores
-// and keys of slot 8h + i, channels 8c..8c+7 (bf16 x 8).  Both rows return
-// the same x[0..7] for channels 8c..8c+7.
-__device__ __forceinline__ void pool_mean(const uint4 (&S)[kHalf], const uint4 (&K)[kHalf],
-                                          const float4* __restrict__ s_ape, int c, int h,
-                                          float (&x)[8]) {
-  const float4* ap = s_ape + (kHalf * h) * 32 + 2 * c;
-  float u[kHalf][8], m[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m[j] = -__builtin_huge_valf();
-#pragma unroll
-  for (int i = 0; i < kHalf; ++i) {
-    float s[8];
-    widen8(S[i], s);
-    const float4 a0 = ap[i * 32], a1 = ap[i * 32 + 1];
-    const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u[i][j] = s[j] + a[j];
-      m[j] = fmaxf(m[j], u[i][j]);
-    }
-  }
-  float ml[8], den[8], acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    m[j] = fmaxf(m[j], swap_rows16(m[j]));        // max over all 16 slots
-    ml[j] = m[j] * kLog2e;
-    den[j] = 0.0f;
-    acc[j] = 0.0f;
-  }
-#pragma unroll
-  for (int i = 0; i < kHalf; ++i) {
-    float k[8];
-    widen8(K[i], k);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = exp2_hw(__builtin_fmaf(u[i][j], kLog2e, -ml[j]));
-      den[j] += p;
-      acc[j] = __builtin_fmaf(k[j], p, acc[j]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float d = den[j] + swap_rows16(den[j]);
-    const float a = acc[j] + swap_rows16(acc[j]);
-    x[j] = a * __builtin_amdgcn_rcpf(d);
-  }
 }
 
 // Softmax-weighted mean of one pool, whole-wave layout (one pool per wave).
@@ -287,17 +228,6 @@ __device__ __forceinline__ void pool_mean_wave_lds(const uint4 (&S)[4], const ui
                         x);
 }
 
-// bf16 round -> rotate -> bf16 round -> scale -> e4m3 for the pool's two
-// rows.  Row h handles channels 8c + 4h + t; returns their 4 codes packed
-// little-endian and the pool's scale.
-__device__ __forceinline__ uint32_t pool_epilogue(const float (&x)[8], int c, int h,
-                                                  bool round_scale, float& scale_out) {
-  float v[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) v[t] = h ? x[4 + t] : x[t];
-  return rotate_quantise32(v, c, h, round_scale, scale_out);
-}
-
 // Where a compressed vector goes.  Packed: codes row `row` of a [n,128]
 // array and scales[row].  Paged (page size 1): page `row` of a [pages, 132]
 // byte cache holding the 128 codes followed by the fp32 scale.
@@ -307,19 +237,6 @@ struct OutSink {
   int64_t rows;        // rows / pages available
   bool paged;
   float* dbg;          // ring decode: fp32 [rows, 128] pre-rounding means, or null
-  // 32-lane layout: lane 16h + c of a pool stores the codes of channels
-  // 8c + 4h .. 8c + 4h + 3; its lane 0 also stores the scale.
-  __device__ __forceinline__ void store(int64_t row, int c, int h, uint32_t code4,
-                                        float scale) const {
-    if (paged) {
-      uint8_t* page = codes + row * kPagedBytes;
-      reinterpret_cast<uint32_t*>(page)[2 * c + h] = code4;
-      if (c == 0 && h == 0) *reinterpret_cast<float*>(page + 128) = scale;
-    } else {
-      reinterpret_cast<uint32_t*>(codes + row * 128)[2 * c + h] = code4;
-      if (c == 0 && h == 0) scales[row] = scale;
-    }
-  }
   // The same sink advanced by `rows` rows (the next layer's outputs).
   __device__ __forceinline__ OutSink advanced(int64_t rows_by) const {
     OutSink o = *this;
@@ -340,83 +257,6 @@ struct OutSink {
     }
   }
 };
-
-// Two pools per wave (32-lane layout), for large batches: a pool's two
-// 16-lane rows take slots 8h..8h+7, lane c channels 8c..8c+7.  Twice the
-// bytes in flight per wave of the one-pool-per-wave kernel, at 120 VGPRs.
-// kBuf as for pool16_prefill_kernel.
-template <bool kRoundScale, bool kDbg, bool kBuf>
-__global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_pair_kernel(
-    const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
-    int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
-    const int32_t* __restrict__ src_rows, int64_t n_pools, OutSink sink,
-    const int64_t* __restrict__ loc, const uint8_t* __restrict__ write_mask,
-    float* __restrict__ dbg, uint32_t key_bytes, uint32_t score_bytes) {
-  __shared__ float4 s_ape[kPool * 32];
-  const int c = threadIdx.x & 15;
-  const int h = (threadIdx.x >> 4) & 1;
-  const int64_t pool = (int64_t)blockIdx.x * kPairPoolsPerBlock + (threadIdx.x >> 5);
-  int64_t r0 = -1, dst = pool;
-  bool ok = pool < n_pools;
-  // The wave's two plan entries (pools 2v and 2v+1 of the workgroup) are read
-  // at a wave-uniform address, so they come through scalar loads, which
-  // return before the vector path would: the row loads wait on them (measured
-  // 74.5-75.0% instead of 72.7-73.4% of HBM peak on the ragged prefill).
-  int32_t e0 = 0, e1 = 0;
-  if (src_rows) {
-    const int v = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int64_t p0 = (int64_t)blockIdx.x * kPairPoolsPerBlock + 2 * v;
-    if (p0 < n_pools) e0 = src_rows[p0];
-    if (p0 + 1 < n_pools) e1 = src_rows[p0 + 1];
-  }
-  if (ok) {
-    r0 = src_rows ? (int64_t)((threadIdx.x & 32) ? e1 : e0) : pool * kPool;
-    if (loc) dst = loc[pool];
-    if (write_mask && !write_mask[pool]) ok = false;
-  }
-  // Both rows of a pool take the same decision, so DPP / swizzle partners
-  // are always active.
-  ok = ok && r0 >= 0 && r0 + kPool <= num_rows && dst >= 0 && dst < sink.rows;
-
-  // ape is requested first; the row loads are unconditional (a skipped pool
-  // reads rows 0..15, which exist: the launcher only runs with num_rows >=
-  // 16), so no branch forces the compiler to wait on them early.
-  const ApeRegs ape_regs = load_ape(ape);
-  uint4 S[kHalf], K[kHalf];
-  {
-    const int64_t row = (ok ? r0 : 0) + kHalf * h;
-    if constexpr (kBuf) {
-      const BufRsrc rs = make_rsrc(scores, score_bytes), rk = make_rsrc(keys, key_bytes);
-      const uint32_t so = (uint32_t)(row * score_stride * 2) + 16u * c;
-      const uint32_t ko = (uint32_t)(row * key_stride * 2) + 16u * c;
-      const uint32_t ss = (uint32_t)(score_stride * 2), ks = (uint32_t)(key_stride * 2);
-#pragma unroll
-      for (int i = 0; i < kHalf; ++i) S[i] = load_stream(rs, so + i * ss);
-#pragma unroll
-      for (int i = 0; i < kHalf; ++i) K[i] = load_stream(rk, ko + i * ks);
-    } else {
-      const uint4* sp = reinterpret_cast<const uint4*>(scores + row * score_stride) + c;
-      const uint4* kp = reinterpret_cast<const uint4*>(keys + row * key_stride) + c;
-      const int64_t ss = score_stride >> 3, ks = key_stride >> 3;
-#pragma unroll
-      for (int i = 0; i < kHalf; ++i) S[i] = load_stream(sp + i * ss);
-#pragma unroll
-      for (int i = 0; i < kHalf; ++i) K[i] = load_stream(kp + i * ks);
-    }
-  }
-  store_ape(s_ape, ape_regs);
-  if (!ok) return;
-
-  float x[8];
-  pool_mean(S, K, s_ape, c, h, x);
-  if constexpr (kDbg) {
-    reinterpret_cast<float4*>(dbg + pool * 128 + 8 * c)[h] =
-        h ? make_float4(x[4], x[5], x[6], x[7]) : make_float4(x[0], x[1], x[2], x[3]);
-  }
-  float scale;
-  const uint32_t codes = pool_epilogue(x, c, h, kRoundScale, scale);
-  sink.store(dst, c, h, codes, scale);
-}
 
 // One pool per wave.
 // kBuf: keys and scores each span less than 4 GiB (key_bytes / score_bytes
@@ -873,17 +713,9 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
                                  const int64_t* loc, const uint8_t* write_mask, bool round_scale,
                                  float* dbg, hipStream_t stream) {
   if (num_rows < kPool || n_pools <= 0) return hipSuccess;   // no pool can be complete
-  // One pool per wave halves the arithmetic a wave runs after its rows
-  // arrive, which shortens the launch's drain; two pools per wave keep more
-  // bytes in flight per SIMD (64 KB at four waves against 48 KB at six),
-  // which wins once the drain is a small share.  Measured on the ragged
-  // workload: one per wave 2-4% faster at 7k-23k pools, two per wave 1-3%
-  // faster at 31k-62k pools.
-  const bool pair = n_pools > kWavePerPoolMaxPools;
   // n_pools >= 1 here, so the kernels' clamped plan index is valid
   const int plan_mode = !src_rows ? 0 : (!loc && !write_mask) ? 1 : loc ? 2 : 0;
-  const int64_t per_block = pair ? kPairPoolsPerBlock : kPoolsPerBlock;
-  const dim3 grid((unsigned)((n_pools + per_block - 1) / per_block));
+  const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
   const OutSink sink{out_fp8, out_scale, out_rows, paged, nullptr};
   // Bytes from each base to the end of its last row: buffer loads when both
@@ -894,11 +726,7 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
   const uint32_t kb = buf ? (uint32_t)key_bytes : 0u, sb = buf ? (uint32_t)score_bytes : 0u;
 #define KVC_LAUNCH(RS, DBG, BUF)                                                              \
   do {                                                                                        \
-    if (pair)                                                                                 \
-      hipLaunchKernelGGL((pool16_prefill_pair_kernel<RS, DBG, BUF>), grid, block, 0, stream,  \
-                         keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
-                         n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
-    else if (plan_mode == 1)                                                                  \
+    if (plan_mode == 1)                                                                       \
       hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, 1>), grid, block, 0, stream,    \
                          keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
                          n_pools, sink, loc, write_mask, dbg, kb, sb);                        \

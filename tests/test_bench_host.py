@@ -33,12 +33,3 @@ def test_traffic_is_reported_only_for_the_measured_sources(tmp_path):
     assert bench.measured_traffic(str(tmp_path / "missing.json")) is None
 
 
-def test_prefill_size_rule_matches_the_launcher():
-    """bench.py names the prefill kernel by the launcher's pool-count rule."""
-    import re
-    src = os.path.join(ROOT, "kv_cache_compression_pool_amd", "csrc", "kvc_pool16.hip")
-    with open(src) as f:
-        m = re.search(r"kWavePerPoolMaxPools\s*=\s*(\d+)", f.read())
-    assert m and int(m.group(1)) == bench.PREFILL_WAVE_PER_POOL_MAX
-    from tests import test_gpu_parity
-    assert test_gpu_parity.PAIR_KERNEL_MIN_POOLS == bench.PREFILL_WAVE_PER_POOL_MAX + 1
