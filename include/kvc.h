@@ -173,6 +173,7 @@ int64_t kvc_c128_fused_capacity(int64_t num_tokens, int64_t max_batch);
  *   round_scale     nonzero: scale rounded up to a power of two.
  *   dbg_pooled      device fp32 [n_pools, 128] or NULL: receives the fp32
  *                   weighted mean before any rounding (for parity checks).
+ * num_rows, n_pools and the row strides are at most 2^31-1.
  * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE (strides, alignment, sizes),
  *         KVC_ERR_UNSUPPORTED (pool_size != 16), KVC_ERR_HIP. */
 int kvc_compress_prefill(const uint16_t* keys, int64_t key_row_stride,
@@ -192,7 +193,8 @@ int kvc_compress_prefill(const uint16_t* keys, int64_t key_row_stride,
  * [0, num_pages), are skipped (no rows read, nothing written).
  *   keys, scores, ape, pool_src_row, n_pools, round_scale: as
  *                 kvc_compress_prefill
- *   kv_cache      device uint8 [num_pages, 132], 4-byte aligned
+ *   kv_cache      device uint8 [num_pages, 132], 4-byte aligned; num_pages
+ *                 at most 2^31-1
  *   loc           device int64 [n_pools]
  *   write_mask    device uint8 (bool) [n_pools] or NULL (write all)
  * Errors: KVC_ERR_NULL, KVC_ERR_SHAPE, KVC_ERR_UNSUPPORTED (pool_size != 16

@@ -255,8 +255,9 @@ int check_prefill_inputs(const char* fn, const uint16_t* keys, int64_t key_row_s
     return fail(KVC_ERR_SHAPE, "%s: row strides must be >= 128 and a multiple of 8", fn);
   if (!aligned(keys, 16) || !aligned(scores, 16) || !aligned(ape, 16))
     return fail(KVC_ERR_SHAPE, "%s: misaligned pointer", fn);
-  if (n_pools > kMaxI32 || num_rows > kMaxI32)
-    return fail(KVC_ERR_SHAPE, "%s: sizes exceed 2^31-1", fn);
+  if (n_pools > kMaxI32 || num_rows > kMaxI32 || key_row_stride > kMaxI32 ||
+      score_row_stride > kMaxI32)
+    return fail(KVC_ERR_SHAPE, "%s: sizes or strides exceed 2^31-1", fn);
   if (!pool_src_row && n_pools * kPool > num_rows)
     return fail(KVC_ERR_SHAPE, "%s: %lld pools need %lld rows, have %lld", fn, (long long)n_pools,
                 (long long)(n_pools * kPool), (long long)num_rows);
@@ -315,6 +316,7 @@ int kvc_compress_prefill_paged(const uint16_t* keys, int64_t key_row_stride,
   if (page_size != 1)
     return fail(KVC_ERR_UNSUPPORTED, "%s: page_size %d (only 1: the larger pages' token order is not specified)", fn, page_size);
   if (n_pools < 0 || num_rows < 0 || num_pages < 0) return fail(KVC_ERR_SHAPE, "%s: negative size", fn);
+  if (num_pages > kMaxI32) return fail(KVC_ERR_SHAPE, "%s: num_pages exceeds 2^31-1", fn);
   if (n_pools == 0) return ok();
   int rc = check_prefill_inputs(fn, keys, key_row_stride, scores, score_row_stride, num_rows, ape,
                                 pool_size, pool_src_row, n_pools);

@@ -267,12 +267,17 @@ struct OutSink {
 // then load their plan entry (and loc) without branches before the row loads.
 // 0 = anything else.
 template <bool kRoundScale, bool kDbg, bool kBuf, int kPlan>
+// Arguments: 9 pointers and 8 32-bit values (104 bytes; the host checks that
+// sizes and strides fit): the runtime's host-side launch cost grows by about
+// 1 us once a kernel's argument block exceeds 112 bytes.
 __global__ __launch_bounds__(kBlock, kMinWavesPerEU) void pool16_prefill_kernel(
-    const uint16_t* __restrict__ keys, int64_t key_stride, const uint16_t* __restrict__ scores,
-    int64_t score_stride, int64_t num_rows, const float* __restrict__ ape,
-    const int32_t* __restrict__ src_rows, int64_t n_pools, OutSink sink,
-    const int64_t* __restrict__ loc, const uint8_t* __restrict__ write_mask,
-    float* __restrict__ dbg, uint32_t key_bytes, uint32_t score_bytes) {
+    const uint16_t* __restrict__ keys, const uint16_t* __restrict__ scores,
+    const float* __restrict__ ape, const int32_t* __restrict__ src_rows, uint8_t* out_codes,
+    float* out_scales, const int64_t* __restrict__ loc, const uint8_t* __restrict__ write_mask,
+    float* __restrict__ dbg, uint32_t key_stride, uint32_t score_stride, uint32_t num_rows,
+    uint32_t n_pools, uint32_t out_rows, uint32_t paged, uint32_t key_bytes,
+    uint32_t score_bytes) {
+  const OutSink sink{out_codes, out_scales, (int64_t)out_rows, paged != 0u, nullptr};
   __shared__ float4 s_ape[kPool * 32];
   const int c = threadIdx.x & 15;
   const int q = (threadIdx.x >> 4) & 3;
@@ -717,27 +722,32 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
   const int plan_mode = !src_rows ? 0 : (!loc && !write_mask) ? 1 : loc ? 2 : 0;
   const dim3 grid((unsigned)((n_pools + kPoolsPerBlock - 1) / kPoolsPerBlock));
   const dim3 block(kBlock);
-  const OutSink sink{out_fp8, out_scale, out_rows, paged, nullptr};
+  // The kernel takes sizes and strides as 32-bit values.
+  constexpr int64_t kU32 = 0xFFFFFFFFLL;
+  if (key_stride > kU32 || score_stride > kU32 || num_rows > kU32 || n_pools > kU32 ||
+      out_rows > kU32)
+    return hipErrorInvalidValue;
   // Bytes from each base to the end of its last row: buffer loads when both
   // fit in 32-bit offsets.
   const int64_t key_bytes = (num_rows - 1) * key_stride * 2 + 256;
   const int64_t score_bytes = (num_rows - 1) * score_stride * 2 + 256;
   const bool buf = key_bytes < (1LL << 32) && score_bytes < (1LL << 32);
   const uint32_t kb = buf ? (uint32_t)key_bytes : 0u, sb = buf ? (uint32_t)score_bytes : 0u;
+#define KVC_ARGS                                                                               \
+  keys, scores, ape, src_rows, out_fp8, out_scale, loc, write_mask, dbg, (uint32_t)key_stride,   \
+      (uint32_t)score_stride, (uint32_t)num_rows, (uint32_t)n_pools, (uint32_t)out_rows,         \
+      (uint32_t)(paged ? 1 : 0), kb, sb
 #define KVC_LAUNCH(RS, DBG, BUF)                                                              \
   do {                                                                                        \
     if (plan_mode == 1)                                                                       \
       hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, 1>), grid, block, 0, stream,    \
-                         keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
-                         n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
+                         KVC_ARGS);                                                           \
     else if (plan_mode == 2)                                                                  \
       hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, 2>), grid, block, 0, stream,    \
-                         keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
-                         n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
+                         KVC_ARGS);                                                           \
     else                                                                                      \
       hipLaunchKernelGGL((pool16_prefill_kernel<RS, DBG, BUF, 0>), grid, block, 0, stream,    \
-                         keys, key_stride, scores, score_stride, num_rows, ape, src_rows,     \
-                         n_pools, sink, loc, write_mask, dbg, kb, sb);                        \
+                         KVC_ARGS);                                                           \
   } while (0)
   if (buf) {
     if (round_scale) {
@@ -753,6 +763,7 @@ hipError_t launch_pool16_prefill(const uint16_t* keys, int64_t key_stride, const
     }
   }
 #undef KVC_LAUNCH
+#undef KVC_ARGS
   return hipGetLastError();
 }
 

@@ -180,6 +180,13 @@ def test_device_entry_points_validate_before_launch():
                                   1, None, None) == kvc.KVC_ERR_SHAPE
     assert L.kvc_compress_prefill(p, 128, p, 128, 15, p, 16, None, 1, p, p, 1, None, None) \
         == kvc.KVC_ERR_SHAPE
+    # sizes and strides the kernels take as 32-bit values
+    assert L.kvc_compress_prefill(p, 1 << 31, p, 128, 16, p, 16, None, 1, p, p, 1, None, None) \
+        == kvc.KVC_ERR_SHAPE
+    assert b"exceed 2^31-1" in L.kvc_last_error()
+    assert L.kvc_compress_prefill_paged(p, 128, p, 128, 16, p, 16, None, 1, p, 1 << 31, 1, p,
+                                        None, 1, None) == kvc.KVC_ERR_SHAPE
+    assert b"num_pages" in L.kvc_last_error()
     # empty work is a no-op, even with NULL buffers
     assert L.kvc_compress_prefill(None, 0, None, 0, 0, None, 16, None, 0, None, None, 1, None,
                                   None) == kvc.KVC_OK
