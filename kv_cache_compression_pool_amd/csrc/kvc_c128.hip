@@ -277,10 +277,14 @@ __device__ __forceinline__ void merge_partial(float& M, float& D, float& A, floa
   M = mx;
 }
 
-// LDS partials of one plan: (max, sum, weighted sum) per wave and channel.
+// LDS partials of one plan: (max, sum, weighted sum) per wave and channel
+// (rows padded to 136 floats: the merge below reads four rows at once, which
+// then fall on different banks), and the finished vector for the quantised
+// epilogue.
 template <int kWaves>
 struct PlanLds {
-  float m[kWaves][128], d[kWaves][128], a[kWaves][128];
+  float m[kWaves][136], d[kWaves][136], a[kWaves][136];
+  float k[128];
 };
 
 // One plan (16-byte entry pv) processed by the whole workgroup.  Returns
@@ -309,6 +313,15 @@ __device__ __forceinline__ void prefill_plan(
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5;                 // even / odd chunk positions
   const int q = lane & 31;                 // channels 4q..4q+3
+  // After the partials meet in LDS, wave w finishes channels kChPerWave * w ..
+  // kChPerWave * w + kChPerWave - 1: lane group g (kChPerWave lanes) merges
+  // the partials of waves 2g and 2g + 1 for channel ch, then the groups merge
+  // across lanes, and group 0 finishes the channel.
+  constexpr int kChPerWave = 128 / kWaves;
+  static_assert(kWaves >= 2 && kWaves <= 64 && kChPerWave * kWaves == 128,
+                "two partials per lane group");
+  const int ch = kChPerWave * w + lane % kChPerWave;
+  const int g = lane / kChPerWave;
   const float4* in4 = reinterpret_cast<const float4*>(in);
   const float4* ape4 = reinterpret_cast<const float4*>(ape);
 
@@ -333,14 +346,13 @@ __device__ __forceinline__ void prefill_plan(
   if (off != 0u) load_idx = load_indices[batch_id];
   int32_t store_idx = -1;
   if constexpr (kWrite) store_idx = indices[batch_id];
-  const bool lead = (w == 0 && h == 0);    // the 32 lanes that finish the plan
   const bool load_ok = load_idx >= 0 && (int64_t)load_idx < num_slots;
-  float4 m1 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = m1, k1 = m1;
-  if (lead && off != 0u && load_ok) {
-    const float4* st = reinterpret_cast<const float4*>(state + (int64_t)load_idx * 384);
-    m1 = st[q];
-    s1 = st[32 + q];
-    k1 = st[64 + q];
+  float m1 = 0.f, s1 = 0.f, k1 = 0.f;      // stored state of channel ch (group 0)
+  if (g == 0 && off != 0u && load_ok) {
+    const float* st = state + (int64_t)load_idx * 384;
+    m1 = st[ch];
+    s1 = st[128 + ch];
+    k1 = st[256 + ch];
   }
   float4 u[kTokPerLane];
 #pragma unroll
@@ -389,52 +401,55 @@ __device__ __forceinline__ void prefill_plan(
     }
   }
   __syncthreads();
-  if (!lead) return;
   // A segment that needs the stored state but has no valid slot for it, or a
-  // write plan without a valid destination, is malformed: skip it.
+  // write plan without a valid destination, is malformed: skip it (the test
+  // is uniform over the workgroup).
   if ((off != 0u && !load_ok) || (kWrite && (store_idx < 0 || (int64_t)store_idx >= num_slots)))
     return;
 
-  float M[4], D[4], A[4];
+  // Every wave finishes kChPerWave channels, all its lanes working: a serial
+  // merge of the kWaves partials by 32 lanes (4 channels each) had measured
+  // 1.5-1.8 us of a 44 us single-launch prefill.
+  float M = lds.m[2 * g][ch], D = lds.d[2 * g][ch], A = lds.a[2 * g][ch];
+  merge_partial(M, D, A, lds.m[2 * g + 1][ch], lds.d[2 * g + 1][ch], lds.a[2 * g + 1][ch]);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    M[k] = lds.m[0][4 * q + k]; D[k] = lds.d[0][4 * q + k]; A[k] = lds.a[0][4 * q + k];
+  for (int dist = kChPerWave; dist < 64; dist *= 2) {
+    const float m2 = __shfl_xor(M, dist);
+    const float d2 = __shfl_xor(D, dist);
+    const float a2 = __shfl_xor(A, dist);
+    merge_partial(M, D, A, m2, d2, a2);
   }
-#pragma unroll
-  for (int ww = 1; ww < kWaves; ++ww)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      merge_partial(M[k], D[k], A[k], lds.m[ww][4 * q + k], lds.d[ww][4 * q + k],
-                    lds.a[ww][4 * q + k]);
-
-  float K[4];
+  float K;
   if (off != 0u) {
     // Merge with the stored state of the open chunk: (m1, s1, k1) with k1 a
     // normalised mean, i.e. an unnormalised sum k1 * s1.
-    const float mm1[4] = {m1.x, m1.y, m1.z, m1.w};
-    const float ss1[4] = {s1.x, s1.y, s1.z, s1.w};
-    const float kk1[4] = {k1.x, k1.y, k1.z, k1.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float mx = fmaxf(mm1[k], M[k]);
-      const float f1 = ss1[k] * exp2_hw((mm1[k] - mx) * kLog2e);
-      const float f2 = exp2_hw((M[k] - mx) * kLog2e);
-      const float sum = f1 + D[k] * f2;
-      K[k] = (kk1[k] * f1 + A[k] * f2) / sum;
-      D[k] = sum;
-      M[k] = mx;
-    }
+    const float mx = fmaxf(m1, M);
+    const float f1 = s1 * exp2_hw((m1 - mx) * kLog2e);
+    const float f2 = exp2_hw((M - mx) * kLog2e);
+    const float sum = f1 + D * f2;
+    K = (k1 * f1 + A * f2) / sum;
+    D = sum;
+    M = mx;
   } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) K[k] = A[k] / D[k];
+    K = A / D;
   }
   if constexpr (kWrite) {
-    float4* st = reinterpret_cast<float4*>(state + (int64_t)store_idx * 384);
-    st[q] = make_float4(M[0], M[1], M[2], M[3]);
-    st[32 + q] = make_float4(D[0], D[1], D[2], D[3]);
-    st[64 + q] = make_float4(K[0], K[1], K[2], K[3]);
+    if (g == 0) {
+      float* st = state + (int64_t)store_idx * 384;
+      st[ch] = M;
+      st[128 + ch] = D;
+      st[256 + ch] = K;
+    }
+  } else if constexpr (kQuant) {
+    // The rotation needs the whole vector in one half-wave.
+    if (g == 0) lds.k[ch] = K;
+    __syncthreads();
+    if (w == 0 && h == 0) {
+      const float Kq[4] = {lds.k[4 * q], lds.k[4 * q + 1], lds.k[4 * q + 2], lds.k[4 * q + 3]};
+      emit32<true>(o, 0, (int64_t)ragged_id, q, Kq);
+    }
   } else {
-    emit32<kQuant>(o, 0, (int64_t)ragged_id, q, K);
+    if (g == 0) o.out[(int64_t)ragged_id * 128 + ch] = K;
   }
 }
 
