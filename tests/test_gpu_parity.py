@@ -695,6 +695,35 @@ def test_c128_prefill_fused_quant():
         assert np.array_equal(gst, g2.cpu().numpy(), equal_nan=True)
 
 
+def test_c128_prefill_segments_at_every_wave_boundary():
+    """Segments that cover one token, one wave's 16 positions, a span across
+    two waves, a full chunk, or close a chunk with one or two tokens: after the
+    partials meet, each wave finishes its own 16 channels from lane groups
+    whose partials may all be empty.  Both launch forms against the oracle,
+    and the quantised forms against each other."""
+    offs = np.array([0, 127, 16, 15, 62, 0, 127, 100, 126, 48, 112], np.int64)
+    ext = np.array([1, 1, 16, 17, 3, 128, 129, 200, 2, 80, 16], np.int64)
+    prior = np.array([0, 1, 2, 0, 3, 1, 0, 2, 5, 1, 0], np.int64) * 128 + offs
+    d = c128_prefill_case(seed=11, seq_lens=prior + ext, extend_lens=ext)
+    compare_c128_prefill(d, "c128 prefill wave-boundary segments")
+    compare_c128_prefill_fused(d, "c128 fused prefill wave-boundary segments")
+    compare_c128_prefill_fused(d, "c128 fused prefill wave-boundary segments padded", pad=True)
+    N = int(ext.sum())
+    gst, (gc, gs), _ = run_c128_prefill_fused_gpu(d, d["state"], quant=True)
+    cp, wp = kvc.kvc_c128_plan_prefill(d["seq_lens"], d["extend_lens"], N)
+    g2 = dev(d["state"])
+    c2 = torch.full((N, 128), 0x33, dtype=torch.uint8, device="cuda")
+    s2 = torch.full((N,), 5.0, device="cuda")
+    kvc.kvc_c128_online_prefill_quant(g2, dev(d["kv_score_in"]), c2, s2, dev(d["ape"]),
+                                      dev(d["indices"]), kvc.plans_to_device(cp), cp.size,
+                                      kvc.plans_to_device(wp), wp.size, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(gc, c2.cpu().numpy())
+    assert np.array_equal(gs, s2.cpu().numpy())
+    assert np.array_equal(gst, g2.cpu().numpy(), equal_nan=True)
+    assert (gc != 0x33).any(axis=1).sum() == int((d["seq_lens"] // 128 - prior // 128).sum())
+
+
 def test_c128_prefill_fused_distinct_load_indices():
     """Open-chunk states read from other slots than the ones written back (the
     single launch's precondition holds: no request reads a written slot)."""
