@@ -189,13 +189,17 @@ def launch_floor(torch, kvc, stream, workgroups, threads, steps=100, graph_calls
     back (behind the busy-wait, as every timed leg) and as one node of a
     `graph_calls`-node HIP graph; and the host time of one prepared launch of
     it (the runtime's own launch cost plus one ctypes call).  Returns (us per
-    launch, us per graph node, host us per prepared launch)."""
+    launch, us per graph node, host us per prepared launch by argument-block
+    size in bytes)."""
     def step(i):
         kvc.kvc.kvc_diag_empty_launch(workgroups, threads)
 
     _, ev, _ = timed(step, steps, 5, torch, stream)
-    call = kvc.prepare(kvc.kvc.kvc_diag_empty_launch, workgroups, threads, stream=stream)
-    _, _, host = timed(lambda i: call(), steps, 5, torch, stream)
+    host = {}
+    for arg_bytes in (0, 112, 136, 448):
+        call = kvc.prepare(kvc.kvc.kvc_diag_empty_launch, workgroups, threads, arg_bytes,
+                           stream=stream)
+        host[arg_bytes] = timed(lambda i: call(), steps, 5, torch, stream)[2]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for _ in range(graph_calls):
@@ -204,7 +208,7 @@ def launch_floor(torch, kvc, stream, workgroups, threads, steps=100, graph_calls
     _, evg, _ = timed(lambda i: g.replay(), max(steps // 10, 8), 2, torch, stream,
                       host_us_per_call=100.0)
     del g
-    return ev * 1e3, evg / graph_calls * 1e3, host * 1e6
+    return ev * 1e3, evg / graph_calls * 1e3, {k: round(v * 1e6, 2) for k, v in host.items()}
 
 
 # ------------------------------------------------------------------ pool-128 decode
@@ -947,7 +951,8 @@ def main():
         fl, flg, flh = launch_floor(torch, kvc, stream, (c4["batch"] + 1) // 2, 64)
         line["c128_decode"]["launch_floor_us"] = {
             "grid": f"{(c4['batch'] + 1) // 2} x 64 threads", "single": round(fl, 3),
-            "graph_64_calls_per_call": round(flg, 3), "host_prepared": round(flh, 2),
+            "graph_64_calls_per_call": round(flg, 3), "host_prepared": flh[0],
+            "host_prepared_by_arg_bytes": flh,
             "us_at_60pct_of_peak": round(c4["alg_bytes"] / (0.6 * PEAK_HBM_GBS * 1e3), 3)}
         line["c128_decode"]["target_basis"] = (
             "The 60%-of-HBM-peak goal applies to multi_layer: the same 1024 requests decoding one "
@@ -995,7 +1000,7 @@ def main():
         fl, flg, flh = launch_floor(torch, kvc, stream, (c3["requests"] + 3) // 4, 256)
         line["ring_decode"]["launch_floor_us"] = {
             "grid": f"{(c3['requests'] + 3) // 4} x 256 threads", "single": round(fl, 3),
-            "graph_64_calls_per_call": round(flg, 3), "host_prepared": round(flh, 2)}
+            "graph_64_calls_per_call": round(flg, 3), "host_prepared": flh[0]}
         if "graph" in c3:
             cg = c3["graph"]
             gg = gbs(c3["alg_bytes"], cg["call_ms"])

@@ -448,9 +448,12 @@ int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t
 
 /* Launches a kernel that does nothing, with `workgroups` workgroups of
  * `threads` threads (1..1024), for measuring the launch and dispatch floor
- * that a kernel of that grid pays.  workgroups == 0 is a no-op.
- * Errors: KVC_ERR_SHAPE, KVC_ERR_HIP. */
-int kvc_diag_empty_launch(int64_t workgroups, int threads, void* stream);
+ * that a kernel of that grid pays.  arg_bytes (0, 64, 112, 136 or 448) sets
+ * the size of the kernel's (unused) argument block, for measuring how the
+ * runtime's host-side cost of a launch depends on it.  workgroups == 0 is a
+ * no-op.
+ * Errors: KVC_ERR_SHAPE, KVC_ERR_UNSUPPORTED (arg_bytes), KVC_ERR_HIP. */
+int kvc_diag_empty_launch(int64_t workgroups, int threads, int arg_bytes, void* stream);
 
 #ifdef __cplusplus
 }

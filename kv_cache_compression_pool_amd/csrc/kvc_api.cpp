@@ -668,13 +668,15 @@ int kvc_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, int64_t
                     "kvc_diag_stream_read launch");
 }
 
-int kvc_diag_empty_launch(int64_t workgroups, int threads, void* stream) {
+int kvc_diag_empty_launch(int64_t workgroups, int threads, int arg_bytes, void* stream) {
   const char* fn = "kvc_diag_empty_launch";
   if (workgroups < 0 || workgroups > 0x7fffffffLL)
     return fail(KVC_ERR_SHAPE, "%s: workgroups out of range", fn);
   if (threads < 1 || threads > 1024) return fail(KVC_ERR_SHAPE, "%s: threads must be 1..1024", fn);
+  if (arg_bytes != 0 && arg_bytes != 64 && arg_bytes != 112 && arg_bytes != 136 && arg_bytes != 448)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: arg_bytes %d (0, 64, 112, 136 or 448)", fn, arg_bytes);
   if (workgroups == 0) return ok();
-  return hip_status(kvc::launch_diag_empty(workgroups, threads, (hipStream_t)stream),
+  return hip_status(kvc::launch_diag_empty(workgroups, threads, arg_bytes, (hipStream_t)stream),
                     "kvc_diag_empty_launch launch");
 }
 

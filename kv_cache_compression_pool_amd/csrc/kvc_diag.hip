@@ -66,8 +66,18 @@ __global__ __launch_bounds__(256) void diag_stream_read_kernel(const u32x4_t* __
 }
 
 // A kernel that does nothing: its launch-to-launch time with a given grid is
-// the dispatch floor that any kernel of that grid pays.
+// the dispatch floor that any kernel of that grid pays.  The forms with an
+// argument block of N 8-byte words show what the runtime's host-side launch
+// costs for a kernel whose arguments take that many bytes.
 __global__ __launch_bounds__(1024) void diag_empty_kernel() {}
+template <int N>
+struct ArgBlock {
+  uint64_t w[N];
+};
+template <int N>
+__global__ __launch_bounds__(1024) void diag_empty_args_kernel(ArgBlock<N> a) {
+  (void)a;
+}
 
 }  // namespace
 
@@ -104,8 +114,15 @@ hipError_t launch_diag_stream_read(const void* src, int64_t bytes, uint32_t* sin
   return hipGetLastError();
 }
 
-hipError_t launch_diag_empty(int64_t workgroups, int threads, hipStream_t stream) {
-  hipLaunchKernelGGL(diag_empty_kernel, dim3((unsigned)workgroups), dim3(threads), 0, stream);
+hipError_t launch_diag_empty(int64_t workgroups, int threads, int arg_bytes, hipStream_t stream) {
+  const dim3 grid((unsigned)workgroups), block(threads);
+  switch (arg_bytes) {
+    case 0: hipLaunchKernelGGL(diag_empty_kernel, grid, block, 0, stream); break;
+    case 64: hipLaunchKernelGGL(diag_empty_args_kernel<8>, grid, block, 0, stream, ArgBlock<8>{}); break;
+    case 112: hipLaunchKernelGGL(diag_empty_args_kernel<14>, grid, block, 0, stream, ArgBlock<14>{}); break;
+    case 136: hipLaunchKernelGGL(diag_empty_args_kernel<17>, grid, block, 0, stream, ArgBlock<17>{}); break;
+    default: hipLaunchKernelGGL(diag_empty_args_kernel<56>, grid, block, 0, stream, ArgBlock<56>{}); break;
+  }
   return hipGetLastError();
 }
 

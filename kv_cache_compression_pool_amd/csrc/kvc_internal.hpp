@@ -72,6 +72,7 @@ hipError_t launch_diag_convert(const float* in, uint16_t* bf16_out, uint8_t* fp8
 // words (one per wave).
 hipError_t launch_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink,
                                    int loads_per_lane, bool fold, hipStream_t stream);
-hipError_t launch_diag_empty(int64_t workgroups, int threads, hipStream_t stream);
+// arg_bytes: 0, 64, 112, 136 or 448 (the size of the empty kernel's argument block).
+hipError_t launch_diag_empty(int64_t workgroups, int threads, int arg_bytes, hipStream_t stream);
 
 }  // namespace kvc

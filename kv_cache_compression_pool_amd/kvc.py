@@ -95,7 +95,7 @@ def lib() -> ctypes.CDLL:
                                                     _p, _i64, _p, _u32, _p]
         L.kvc_diag_convert.argtypes = [_p, _p, _p, _i64, _p]
         L.kvc_diag_stream_read.argtypes = [_p, _i64, _p, _i64, _i32, _i32, _p]
-        L.kvc_diag_empty_launch.argtypes = [_i64, _i32, _p]
+        L.kvc_diag_empty_launch.argtypes = [_i64, _i32, _i32, _p]
         for name in EXPORTS[2:]:
             getattr(L, name).restype = _i32
         L.kvc_c128_fused_capacity.restype = _i64
@@ -665,9 +665,11 @@ def kvc_diag_stream_read(src, sink, loads_per_lane: int = 4, fold: bool = False,
                                             int(loads_per_lane), int(bool(fold))), stream)
 
 
-def kvc_diag_empty_launch(workgroups: int, threads: int, stream=None):
-    """Launch an empty kernel of the given grid (launch-floor measurements)."""
-    return _invoke("kvc_diag_empty_launch", (int(workgroups), int(threads)), stream)
+def kvc_diag_empty_launch(workgroups: int, threads: int, arg_bytes: int = 0, stream=None):
+    """Launch an empty kernel of the given grid (launch-floor measurements);
+    arg_bytes (0, 64, 112, 136 or 448) sizes its unused argument block."""
+    return _invoke("kvc_diag_empty_launch", (int(workgroups), int(threads), int(arg_bytes)),
+                   stream)
 
 
 def plans_to_device(plan: np.ndarray, device="cuda"):

@@ -12,5 +12,5 @@ hipError_t launch_c128_prefill(float*, int64_t, const float*, float*, uint8_t*, 
 hipError_t launch_c128_prefill_fused(float*, int64_t, const float*, float*, uint8_t*, float*, bool, int64_t, const float*, const int32_t*, const int32_t*, int64_t, const kvc_online_item*, uint32_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_diag_convert(const float*, uint16_t*, uint8_t*, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_diag_stream_read(const void*, int64_t, uint32_t*, int, bool, hipStream_t) { return hipSuccess; }
-hipError_t launch_diag_empty(int64_t, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_diag_empty(int64_t, int, int, hipStream_t) { return hipSuccess; }
 }

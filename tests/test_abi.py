@@ -257,10 +257,11 @@ def test_device_entry_points_validate_before_launch():
     assert b"sink needs 12 words" in L.kvc_last_error()
     assert sr(ctypes.c_void_p(0x1008), 4096, p, 8, 8, 1, None) == kvc.KVC_ERR_SHAPE
     assert kvc.stream_read_sink_words(3 * 4096 * 8 + 16, 8) == 16
-    assert L.kvc_diag_empty_launch(4, 0, None) == kvc.KVC_ERR_SHAPE
-    assert L.kvc_diag_empty_launch(4, 1025, None) == kvc.KVC_ERR_SHAPE
-    assert L.kvc_diag_empty_launch(-1, 64, None) == kvc.KVC_ERR_SHAPE
-    assert L.kvc_diag_empty_launch(0, 64, None) == kvc.KVC_OK
+    assert L.kvc_diag_empty_launch(4, 0, 0, None) == kvc.KVC_ERR_SHAPE
+    assert L.kvc_diag_empty_launch(4, 1025, 0, None) == kvc.KVC_ERR_SHAPE
+    assert L.kvc_diag_empty_launch(-1, 64, 0, None) == kvc.KVC_ERR_SHAPE
+    assert L.kvc_diag_empty_launch(4, 64, 100, None) == kvc.KVC_ERR_UNSUPPORTED
+    assert L.kvc_diag_empty_launch(0, 64, 0, None) == kvc.KVC_OK
 
 
 def test_last_error_is_per_thread():

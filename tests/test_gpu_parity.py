@@ -1050,7 +1050,8 @@ def test_diag_stream_read_reads_every_word(loads):
 
 
 def test_diag_empty_launch_runs():
-    kvc.kvc.kvc_diag_empty_launch(512, 64)
+    for arg_bytes in (0, 64, 112, 136, 448):
+        kvc.kvc.kvc_diag_empty_launch(512, 64, arg_bytes)
     kvc.kvc.kvc_diag_empty_launch(0, 64)
     torch.cuda.synchronize()
 
